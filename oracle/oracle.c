@@ -1,0 +1,252 @@
+/*
+ * oracle.c -- plain fp64 CPU oracle for the selected-token log-probability.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The product library
+ * (the HIP path) never links, calls or includes anything from this directory,
+ * and this file includes nothing from the product either: the two share no
+ * code, no headers, no constants.
+ *
+ * What it computes (the method's definition, written out):
+ *   For hidden states h[T][H] and LM-head weight w[V][H], both given as
+ *   bfloat16 bit patterns, and target ids y[T]:
+ *     z[t][v]  = sum_k h[t][k] * w[v][k]                (logits)
+ *     lse[t]   = log sum_v exp(z[t][v])                 (log-sum-exp over the
+ *                                                        whole vocabulary)
+ *     logp[t]  = z[t][y[t]] - lse[t]                    (log-softmax read at
+ *                                                        the target token)
+ *   Source: RL-Kernel blog (princepride.github.io, "RL-Kernel ... LogP"),
+ *   section 四 ("five reduction classes"): the Linear-LogP class reduces over
+ *   the vocabulary, the selected token's log-probability depends on the LSE of
+ *   all vocabulary scores, and the LSE is evaluated in its stabilised form
+ *   m + log sum exp(x_i - m) with m = max_i x_i.  Section 一 names the
+ *   quantity: the log-probability of the selected (sampled) token.
+ *
+ * How (plainly, in fp64):
+ *   - bf16 -> fp64 is exact (bits << 16 reinterpreted as fp32, then widened).
+ *   - Each logit is one dot product accumulated in fp64 in increasing k, one
+ *     multiply and one add per k.  A product of two bf16 values carries at most
+ *     16 significant bits, so it is exact in fp64; only the additions round.
+ *     For speed, eight independent dot products (eight vocabulary rows) are
+ *     advanced together, each still in increasing k; this interleaving of
+ *     independent sums changes no result bit relative to the one-at-a-time
+ *     loop (the tests check that too).
+ *   - m = max over the row, s = sum_v exp(z - m) sequentially in v,
+ *     lse = m + log(s).
+ *   - OpenMP over rows; every row is computed by one thread in a fixed order,
+ *     so results do not depend on the thread count.
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *   - Non-finite logits: a NaN or +Inf logit anywhere in a row makes that
+ *     row's lse and logp NaN.  -Inf logits carry probability zero and add
+ *     nothing to the sum; a row whose logits are all -Inf has lse = -Inf and
+ *     logp = NaN.
+ *   - A target outside [0, V) gives logp = NaN; lse is still produced.
+ *   - No temperature, no soft-capping: the LSE covers exactly the V rows of w
+ *     that are passed.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_VERSION 1
+
+int oracle_version(void) { return ORACLE_VERSION; }
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* bfloat16 bit pattern -> fp64, exactly. */
+static double bf16_to_f64(uint16_t bits) {
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* One row of logits: z[v] = sum_k h[k] * w[v][k] for v in [0, V), each sum in
+ * increasing k.  h is already fp64 (exact copy of the bf16 row). */
+static void row_logits(const double *h, const uint16_t *w, int64_t ldw,
+                       int64_t H, int64_t V, double *z) {
+    int64_t v = 0;
+    for (; v + 8 <= V; v += 8) {
+        const uint16_t *w0 = w + (v + 0) * ldw, *w1 = w + (v + 1) * ldw;
+        const uint16_t *w2 = w + (v + 2) * ldw, *w3 = w + (v + 3) * ldw;
+        const uint16_t *w4 = w + (v + 4) * ldw, *w5 = w + (v + 5) * ldw;
+        const uint16_t *w6 = w + (v + 6) * ldw, *w7 = w + (v + 7) * ldw;
+        double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+        double a4 = 0.0, a5 = 0.0, a6 = 0.0, a7 = 0.0;
+        for (int64_t k = 0; k < H; ++k) {
+            const double hk = h[k];
+            a0 = a0 + hk * bf16_to_f64(w0[k]);
+            a1 = a1 + hk * bf16_to_f64(w1[k]);
+            a2 = a2 + hk * bf16_to_f64(w2[k]);
+            a3 = a3 + hk * bf16_to_f64(w3[k]);
+            a4 = a4 + hk * bf16_to_f64(w4[k]);
+            a5 = a5 + hk * bf16_to_f64(w5[k]);
+            a6 = a6 + hk * bf16_to_f64(w6[k]);
+            a7 = a7 + hk * bf16_to_f64(w7[k]);
+        }
+        z[v + 0] = a0; z[v + 1] = a1; z[v + 2] = a2; z[v + 3] = a3;
+        z[v + 4] = a4; z[v + 5] = a5; z[v + 6] = a6; z[v + 7] = a7;
+    }
+    for (; v < V; ++v) {
+        const uint16_t *wv = w + v * ldw;
+        double a = 0.0;
+        for (int64_t k = 0; k < H; ++k) a = a + h[k] * bf16_to_f64(wv[k]);
+        z[v] = a;
+    }
+}
+
+/* The reference one-at-a-time dot product, kept only so the tests can check
+ * that the interleaved loop above reproduces it bit for bit. */
+static double dot_naive(const double *h, const uint16_t *wv, int64_t H) {
+    double a = 0.0;
+    for (int64_t k = 0; k < H; ++k) a = a + h[k] * bf16_to_f64(wv[k]);
+    return a;
+}
+
+/* lse and logp of one row of logits (policy for non-finite values above). */
+static void row_lse_logp(const double *z, int64_t V, int64_t y,
+                         double *lse_out, double *logp_out) {
+    double m = -INFINITY;
+    int bad = 0;
+    for (int64_t v = 0; v < V; ++v) {
+        const double x = z[v];
+        if (isnan(x) || x == INFINITY) bad = 1;
+        else if (x > m) m = x;
+    }
+    if (bad) { *lse_out = NAN; *logp_out = NAN; return; }
+    if (m == -INFINITY) { *lse_out = -INFINITY; *logp_out = NAN; return; }
+    double s = 0.0;
+    for (int64_t v = 0; v < V; ++v) s = s + exp(z[v] - m);
+    const double lse = m + log(s);
+    *lse_out = lse;
+    *logp_out = (y >= 0 && y < V) ? z[y] - lse : NAN;
+}
+
+static void hidden_row(const uint16_t *hidden, int64_t ldh, int64_t t,
+                       int64_t H, double *h) {
+    const uint16_t *src = hidden + t * ldh;
+    for (int64_t k = 0; k < H; ++k) h[k] = bf16_to_f64(src[k]);
+}
+
+static void set_threads(int nthreads) {
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+}
+
+/* Logits z[t][v] (row-major [T][V]).  Returns 0, or -1 on allocation failure. */
+int oracle_logits(const uint16_t *hidden, int64_t ldh, const uint16_t *weight,
+                  int64_t ldw, int64_t T, int64_t H, int64_t V, double *z,
+                  int nthreads) {
+    int fail = 0;
+    set_threads(nthreads);
+#pragma omp parallel
+    {
+        double *h = (double *)malloc((size_t)(H > 0 ? H : 1) * sizeof(double));
+        if (!h) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t t = 0; t < T; ++t) {
+                hidden_row(hidden, ldh, t, H, h);
+                row_logits(h, weight, ldw, H, V, z + t * V);
+            }
+        }
+        free(h);
+    }
+    return fail ? -1 : 0;
+}
+
+/* Same logits, one dot product at a time (test of the interleaving only). */
+int oracle_logits_naive(const uint16_t *hidden, int64_t ldh,
+                        const uint16_t *weight, int64_t ldw, int64_t T,
+                        int64_t H, int64_t V, double *z) {
+    double *h = (double *)malloc((size_t)(H > 0 ? H : 1) * sizeof(double));
+    if (!h) return -1;
+    for (int64_t t = 0; t < T; ++t) {
+        hidden_row(hidden, ldh, t, H, h);
+        for (int64_t v = 0; v < V; ++v)
+            z[t * V + v] = dot_naive(h, weight + v * ldw, H);
+    }
+    free(h);
+    return 0;
+}
+
+/* lse / logp from logits given directly (row-major [T][V]). */
+void oracle_lse_from_logits(const double *z, const int32_t *targets, int64_t T,
+                            int64_t V, double *logp, double *lse) {
+    for (int64_t t = 0; t < T; ++t)
+        row_lse_logp(z + t * V, V, (int64_t)targets[t], &lse[t], &logp[t]);
+}
+
+/* The whole path: logits, vocabulary LSE, gather.  Returns 0 or -1. */
+int oracle_selected_logp(const uint16_t *hidden, int64_t ldh,
+                         const uint16_t *weight, int64_t ldw,
+                         const int32_t *targets, int64_t T, int64_t H,
+                         int64_t V, double *logp, double *lse, int nthreads) {
+    int fail = 0;
+    set_threads(nthreads);
+#pragma omp parallel
+    {
+        double *h = (double *)malloc((size_t)(H > 0 ? H : 1) * sizeof(double));
+        double *z = (double *)malloc((size_t)(V > 0 ? V : 1) * sizeof(double));
+        if (!h || !z) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t t = 0; t < T; ++t) {
+                hidden_row(hidden, ldh, t, H, h);
+                row_logits(h, weight, ldw, H, V, z);
+                row_lse_logp(z, V, (int64_t)targets[t], &lse[t], &logp[t]);
+            }
+        }
+        free(h);
+        free(z);
+    }
+    return fail ? -1 : 0;
+}
+
+/* Full-row log-softmax out[t][v] = z[t][v] - lse[t] (test use: sum-to-one
+ * checks and drawing targets from the model's distribution). */
+int oracle_log_softmax(const uint16_t *hidden, int64_t ldh,
+                       const uint16_t *weight, int64_t ldw, int64_t T,
+                       int64_t H, int64_t V, double *out, int nthreads) {
+    int fail = 0;
+    set_threads(nthreads);
+#pragma omp parallel
+    {
+        double *h = (double *)malloc((size_t)(H > 0 ? H : 1) * sizeof(double));
+        if (!h) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t t = 0; t < T; ++t) {
+                double *z = out + t * V;
+                double lse, logp;
+                hidden_row(hidden, ldh, t, H, h);
+                row_logits(h, weight, ldw, H, V, z);
+                row_lse_logp(z, V, 0, &lse, &logp);
+                for (int64_t v = 0; v < V; ++v) z[v] = z[v] - lse;
+            }
+        }
+        free(h);
+    }
+    return fail ? -1 : 0;
+}
