@@ -1,0 +1,163 @@
+/*
+ * rlk.h -- C ABI of the batch-invariant selected-token log-probability library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes.  For hidden states h[T][H], an LM-head weight w[V][H]
+ * (both bfloat16) and target ids y[T] (int32):
+ *     z[t][v]  = sum_k h[t][k] * w[v][k]          logits, fp32 accumulation
+ *     lse[t]   = log sum_v exp(z[t][v])           vocabulary log-sum-exp
+ *     logp[t]  = z[t][y[t]] - lse[t]              selected-token log-prob
+ * Sources: the RL-Kernel blog (princepride.github.io, "RL-Kernel ... LogP"):
+ * section 一 names the quantity (the selected token's log-probability that
+ * rollout and training must agree on); section 四 puts it in the Linear-LogP
+ * reduction class, whose LSE runs over the whole vocabulary, computed as
+ * m + log sum exp(x - m) from per-block maxima and exponent sums merged in a
+ * fixed order; section 二 ties GEMM drift to how the K dimension is split;
+ * sections 六/七 require a GEMM with one workgroup per output tile and the full
+ * K in a fixed order (no split-K) and a vocabulary reduction merged in a fixed
+ * vocabulary-tile order.  The vLLM blog summary (papercache.org, "Finish RL
+ * Training Faster ...", the consistency criteria) requires that a request's
+ * result not depend on the batch it shares (batch independence), nor on
+ * prefill vs decode (phase consistency).
+ *
+ * Numerical contract (fixed for RLK_ABI_VERSION):
+ *   - Inputs are bfloat16 bit patterns; products are exact in fp32, sums are
+ *     fp32, accumulated over k = 0 .. H-1 in chunks of 16 in increasing order,
+ *     one workgroup per (256 token x 256 vocabulary) tile, no split-K.
+ *   - Logits are never rounded to bf16 and never written to memory.
+ *   - Per (row, 128-wide vocabulary tile): tile max m_j and
+ *     s_j = sum exp(z - m_j) with a reduction tree that depends only on the
+ *     tile geometry; tiles are merged per row with a fold whose shape depends
+ *     only on ceil(V / 128): lse = M + log(sum_j s_j exp(m_j - M)),
+ *     M = max_j m_j.
+ *   - A row's logp and lse are bitwise identical whatever the other rows of
+ *     the call are, whatever the row's position, the batch size T, the stream,
+ *     and across repeated calls.  (Bitwise equality across GPUs of other
+ *     models or other library versions is not promised.)
+ *   - Target outside [0, V): logp = NaN (lse still written).
+ *   - A NaN or +Inf logit in a row: lse = logp = NaN for that row only.
+ *     -Inf logits carry probability zero.  All logits -Inf: lse = -Inf,
+ *     logp = NaN.  fp32 overflow of a logit, and subnormal bf16 inputs
+ *     (which the matrix cores may flush), are outside the contract.
+ *   - The LSE covers exactly the V rows of w passed in; pass the real
+ *     vocabulary size to leave out padding rows.  No temperature, no masking:
+ *     callers drop inactive rows themselves.
+ *
+ * Memory and execution.
+ *   - Every pointer argument of the compute calls is a device pointer on the
+ *     current HIP device.  The caller owns every buffer; the library allocates
+ *     nothing and keeps no pointer after returning.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream) and never synchronise.  Results are valid once the caller has
+ *     synchronised with that stream.  Device faults surface at that sync.
+ *   - Outputs must not alias inputs or the workspace.
+ *   - Validation runs before any HIP call: on an error status nothing was
+ *     launched and nothing was written.
+ */
+#ifndef RLK_H
+#define RLK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RLK_ABI_VERSION 1
+
+/* Status codes returned by every entry point that can fail. */
+#define RLK_OK                      0
+#define RLK_ERR_NULL_POINTER        1  /* a required pointer is NULL */
+#define RLK_ERR_INVALID_SHAPE       2  /* T < 0, H <= 0, V <= 0, ld < H, n < 0 */
+#define RLK_ERR_UNSUPPORTED         3  /* H % 64 != 0, or a size above the
+                                          limits below */
+#define RLK_ERR_MISALIGNED          4  /* pointer or row stride alignment */
+#define RLK_ERR_WORKSPACE_TOO_SMALL 5
+#define RLK_ERR_HIP                 6  /* a launch failed; rlk_last_hip_error()
+                                          has the hipError_t */
+
+/* Size limits: T <= 2^31 - 1 rows, V <= 2^31 - 1, H <= 65536, row strides
+ * ld_hidden, ld_weight <= 2^21 elements, and ceil(T/256) * ceil(V/256) below
+ * 2^31 workgroup tiles.  Beyond them: RLK_ERR_UNSUPPORTED. */
+
+/* Version of this ABI and of the numerical contract above. */
+int rlk_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *rlk_status_string(int status);
+
+/* The hipError_t (as int) behind the calling thread's most recent
+ * RLK_ERR_HIP; hipSuccess (0) if there was none. */
+int rlk_last_hip_error(void);
+
+/* Width of one vocabulary statistics tile (128 rows of w): the unit whose
+ * max and sum of exponentials are merged.  Part of the numerical contract. */
+int rlk_vocab_tile(void);
+
+/* Bytes of device workspace rlk_selected_logp needs for T rows and a
+ * vocabulary of V (H does not matter).  Returns 0 when T <= 0 or V <= 0.
+ * The contents are opaque to callers. */
+size_t rlk_selected_logp_workspace_bytes(int64_t T, int64_t V);
+/* Layout detail: 2 * ceil(V/128) * T floats of tile statistics, then T floats
+ * of target logits, each region rounded up to 256 bytes. */
+
+/* Selected-token log-probabilities: the hot path.
+ *   hidden    bf16 [T][ld_hidden] row-major, only the first H columns read;
+ *             16-byte aligned, ld_hidden >= H and a multiple of 8.
+ *   weight    bf16 [V][ld_weight] row-major (the LM head, one row per
+ *             vocabulary entry), same alignment rules.
+ *   targets   int32 [T], 4-byte aligned.
+ *   logp, lse fp32 [T] outputs, 4-byte aligned; every one of the T entries
+ *             is overwritten.
+ *   T         rows (T == 0: returns RLK_OK, launches nothing).
+ *   H         hidden size, a multiple of 64.
+ *   V         vocabulary size (rows of weight taken into the LSE).
+ *   workspace device scratch of at least
+ *             rlk_selected_logp_workspace_bytes(T, V) bytes, 16-byte
+ *             aligned; its contents on entry do not matter.
+ *   stream    hipStream_t or NULL.
+ * Two kernels run on `stream`: the logit GEMM with the per-tile statistics
+ * and target capture fused into its epilogue, then the fixed-order
+ * vocabulary merge that writes lse and logp. */
+int rlk_selected_logp(const void *hidden, int64_t ld_hidden,
+                      const void *weight, int64_t ld_weight,
+                      const int32_t *targets, float *logp, float *lse,
+                      int64_t T, int64_t H, int64_t V,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* The logits stage alone, for stage-by-stage comparison (the RL-Kernel blog,
+ * section 五: compare intermediate results to find the first divergence).
+ * Runs the very same GEMM main loop as rlk_selected_logp and stores the fp32
+ * accumulators: logits[t * V + v], row-major [T][V], 4-byte aligned.
+ * Argument rules as above; no workspace.  Test and debugging use: it writes
+ * 4*T*V bytes. */
+int rlk_logits(const void *hidden, int64_t ld_hidden, const void *weight,
+               int64_t ld_weight, float *logits, int64_t T, int64_t H,
+               int64_t V, void *stream);
+
+/* Consistency statistics of two fp32 arrays a (the side under test, e.g.
+ * training) and b (the reference, e.g. rollout), as the pages measure them:
+ * the mismatch count and maximum absolute logp difference (RL-Kernel blog,
+ * sections 六/七), and mean / spread of the absolute difference plus the k3
+ * estimator r - 1 - log r with r = exp(a - b) (vLLM blog summary, "diff = 0"
+ * definition).  One workgroup, fixed reduction order, so the statistics are
+ * themselves deterministic.
+ *   a, b   fp32 [n] device arrays, 4-byte aligned.  n >= 0, n < 2^31.
+ *   stats  fp64 [8] device array, 8-byte aligned, overwritten with:
+ *          [0] n
+ *          [1] mismatch count: entries whose 32-bit patterns differ
+ *          [2] max |a - b| in fp64 (0 where bits are equal, +inf where
+ *              exactly one side is NaN)
+ *          [3] sum |a - b|      [4] sum |a - b|^2
+ *          [5] sum of k3 over entries where both sides are finite
+ *          [6] number of such entries        [7] 0 (reserved)
+ * No workspace; asynchronous on `stream`. */
+int rlk_compare(const float *a, const float *b, int64_t n, double *stats,
+                void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RLK_H */

@@ -1,0 +1,225 @@
+"""Python binding of the batch-invariant selected-token log-probability library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``librlk.so`` (built from ``csrc/`` for gfx950).  Function names
+match the C entry points declared in ``include/rlk.h``.  There is no fallback:
+if the library is missing, every call raises.
+
+Tensors are PyTorch device tensors (PyTorch provides device memory and
+streams).  bfloat16 operands may be given as ``torch.bfloat16`` or as 16-bit
+integer tensors holding the bit patterns.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "librlk.so")
+
+RLK_OK = 0
+RLK_ERR_NULL_POINTER = 1
+RLK_ERR_INVALID_SHAPE = 2
+RLK_ERR_UNSUPPORTED = 3
+RLK_ERR_MISALIGNED = 4
+RLK_ERR_WORKSPACE_TOO_SMALL = 5
+RLK_ERR_HIP = 6
+
+EXPORTED = (
+    "rlk_abi_version", "rlk_status_string", "rlk_last_hip_error",
+    "rlk_vocab_tile", "rlk_selected_logp_workspace_bytes",
+    "rlk_selected_logp", "rlk_logits", "rlk_compare",
+)
+
+_lib = None
+
+
+class RLKError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = f"{where}: status {status}: {rlk_status_string(status)}"
+        if status == RLK_ERR_HIP:
+            msg += f" (hipError {rlk_last_hip_error()})"
+        super().__init__(msg)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded ``librlk.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m invariant_selected_token_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, sz, vp, c_int = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int
+    L.rlk_abi_version.restype = c_int
+    L.rlk_status_string.argtypes = [c_int]
+    L.rlk_status_string.restype = ctypes.c_char_p
+    L.rlk_last_hip_error.restype = c_int
+    L.rlk_vocab_tile.restype = c_int
+    L.rlk_selected_logp_workspace_bytes.argtypes = [i64, i64]
+    L.rlk_selected_logp_workspace_bytes.restype = sz
+    L.rlk_selected_logp.argtypes = [vp, i64, vp, i64, vp, vp, vp, i64, i64, i64,
+                                    vp, sz, vp]
+    L.rlk_selected_logp.restype = c_int
+    L.rlk_logits.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, vp]
+    L.rlk_logits.restype = c_int
+    L.rlk_compare.argtypes = [vp, vp, i64, vp, vp]
+    L.rlk_compare.restype = c_int
+    _lib = L
+    return L
+
+
+def rlk_abi_version() -> int:
+    return int(lib().rlk_abi_version())
+
+
+def rlk_status_string(status: int) -> str:
+    return lib().rlk_status_string(int(status)).decode()
+
+
+def rlk_last_hip_error() -> int:
+    return int(lib().rlk_last_hip_error())
+
+
+def rlk_vocab_tile() -> int:
+    return int(lib().rlk_vocab_tile())
+
+
+def rlk_selected_logp_workspace_bytes(T: int, V: int) -> int:
+    return int(lib().rlk_selected_logp_workspace_bytes(int(T), int(V)))
+
+
+# ---------------------------------------------------------------- tensors --
+
+def _torch():
+    import torch
+    return torch
+
+
+def _check_device(name, t, device=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (cuda) tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _bf16_operand(name, t, device=None):
+    torch = _torch()
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must be bfloat16 (or 16-bit bit patterns)")
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+    _check_device(name, t, device)
+    return t.data_ptr(), t.stride(0)
+
+
+def _stream_ptr(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _call(where, status):
+    if status != RLK_OK:
+        raise RLKError(status, where)
+
+
+def rlk_selected_logp(hidden, weight, targets, logp=None, lse=None,
+                      workspace=None, V=None, stream=None):
+    """logp[T], lse[T] (fp32) for hidden [T, H], weight [>=V, H], targets [T].
+
+    ``V`` defaults to ``weight.shape[0]``; pass the real vocabulary size when
+    ``weight`` carries padding rows.  Outputs and the workspace are allocated
+    on ``hidden.device`` when not given.  Runs on ``stream`` (default: the
+    current torch stream) without synchronising.
+    """
+    torch = _torch()
+    dev = hidden.device
+    hp, ldh = _bf16_operand("hidden", hidden, dev)
+    wp, ldw = _bf16_operand("weight", weight, dev)
+    T, H = hidden.shape
+    if weight.shape[1] != H:
+        raise ValueError("hidden and weight disagree on H")
+    V = int(weight.shape[0] if V is None else V)
+    if V > weight.shape[0]:
+        raise ValueError("V exceeds the rows of weight")
+    if targets.dtype != torch.int32 or targets.shape != (T,) or not targets.is_contiguous():
+        raise ValueError("targets must be a contiguous int32 [T] tensor")
+    _check_device("targets", targets, dev)
+    if logp is None:
+        logp = torch.empty(T, dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(T, dtype=torch.float32, device=dev)
+    for name, t in (("logp", logp), ("lse", lse)):
+        if t.dtype != torch.float32 or t.shape != (T,) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 [T] tensor")
+        _check_device(name, t, dev)
+    need = rlk_selected_logp_workspace_bytes(T, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check_device("workspace", workspace, dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _call("rlk_selected_logp", lib().rlk_selected_logp(
+        hp, ldh, wp, ldw, targets.data_ptr(), logp.data_ptr(), lse.data_ptr(),
+        T, H, V, workspace.data_ptr(), ws_bytes, _stream_ptr(stream, dev)))
+    return logp, lse
+
+
+def rlk_logits(hidden, weight, logits=None, V=None, stream=None):
+    """fp32 logits [T, V] from the same GEMM main loop (stage comparison)."""
+    torch = _torch()
+    dev = hidden.device
+    hp, ldh = _bf16_operand("hidden", hidden, dev)
+    wp, ldw = _bf16_operand("weight", weight, dev)
+    T, H = hidden.shape
+    V = int(weight.shape[0] if V is None else V)
+    if logits is None:
+        logits = torch.empty((T, V), dtype=torch.float32, device=dev)
+    if logits.dtype != torch.float32 or logits.shape != (T, V) or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous float32 [T, V] tensor")
+    _check_device("logits", logits, dev)
+    _call("rlk_logits", lib().rlk_logits(hp, ldh, wp, ldw, logits.data_ptr(),
+                                         T, H, V, _stream_ptr(stream, dev)))
+    return logits
+
+
+def rlk_compare(a, b, stats=None, stream=None):
+    """fp64 [8] statistics of a vs b (see rlk.h), computed on the device."""
+    torch = _torch()
+    dev = a.device
+    if a.dtype != torch.float32 or b.dtype != torch.float32 or a.shape != b.shape:
+        raise ValueError("a and b must be float32 tensors of one shape")
+    _check_device("a", a, dev)
+    _check_device("b", b, dev)
+    a = a.contiguous()
+    b = b.contiguous()
+    if stats is None:
+        stats = torch.empty(8, dtype=torch.float64, device=dev)
+    _check_device("stats", stats, dev)
+    _call("rlk_compare", lib().rlk_compare(a.data_ptr(), b.data_ptr(), a.numel(),
+                                           stats.data_ptr(), _stream_ptr(stream, dev)))
+    return stats
+
+
+def consistency_report(stats) -> dict:
+    """Host-side view of rlk_compare's statistics (synchronises)."""
+    s = [float(x) for x in stats.cpu().tolist()]
+    n = s[0]
+    mean = s[3] / n if n else 0.0
+    var = max(s[4] / n - mean * mean, 0.0) if n else 0.0
+    return {
+        "n": int(n),
+        "mismatch_count": int(s[1]),
+        "max_abs_diff": s[2],
+        "mean_abs_diff": mean,
+        "std_abs_diff": var ** 0.5,
+        "k3_mean": s[5] / s[6] if s[6] else 0.0,
+    }
+
+
+selected_logp = rlk_selected_logp

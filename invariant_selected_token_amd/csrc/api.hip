@@ -1,0 +1,173 @@
+// api.hip -- the C ABI declared in include/rlk.h: argument validation,
+// workspace carve-up and the kernel launches.  Validation happens before any
+// HIP call, so an invalid call launches nothing and writes nothing.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+#include "rlk.h"
+
+namespace {
+
+using rlk::ceil_div;
+
+constexpr int64_t MAX_ROWS = 2147483647;   // T and V fit in a signed int
+constexpr int64_t MAX_H = 65536;
+constexpr int64_t MAX_LD = int64_t(1) << 21;  // 256-row tile bytes < 2^31
+constexpr size_t WS_ALIGN = 256;
+
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+bool aligned(const void *p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+size_t round_up(size_t x) { return (x + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN; }
+
+size_t stats_bytes(int64_t T, int64_t V) {
+  return round_up((size_t)ceil_div(V, rlk::STAT_V) * (size_t)T * sizeof(float));
+}
+
+// Shape and support checks shared by the GEMM entry points.
+int check_shapes(int64_t T, int64_t H, int64_t V, int64_t ldh, int64_t ldw) {
+  if (T < 0 || H <= 0 || V <= 0 || ldh < H || ldw < H)
+    return RLK_ERR_INVALID_SHAPE;
+  if (H % rlk::TILE_K != 0 || H > MAX_H || T > MAX_ROWS || V > MAX_ROWS ||
+      ldh > MAX_LD || ldw > MAX_LD)
+    return RLK_ERR_UNSUPPORTED;
+  const int64_t tiles = (int64_t)ceil_div(T, rlk::TILE_T) * ceil_div(V, rlk::TILE_V);
+  if (tiles > MAX_ROWS) return RLK_ERR_UNSUPPORTED;
+  return RLK_OK;
+}
+
+int check_operands(const void *hidden, int64_t ldh, const void *weight,
+                   int64_t ldw) {
+  if (!hidden || !weight) return RLK_ERR_NULL_POINTER;
+  if (!aligned(hidden, 16) || !aligned(weight, 16) || ldh % 8 != 0 ||
+      ldw % 8 != 0)
+    return RLK_ERR_MISALIGNED;
+  return RLK_OK;
+}
+
+rlk::GemmArgs gemm_args(const void *hidden, int64_t ldh, const void *weight,
+                        int64_t ldw, int64_t T, int64_t H, int64_t V) {
+  rlk::GemmArgs g{};
+  g.hidden = static_cast<const uint16_t *>(hidden);
+  g.weight = static_cast<const uint16_t *>(weight);
+  g.ldh = ldh;
+  g.ldw = ldw;
+  g.T = (int)T;
+  g.H = (int)H;
+  g.V = (int)V;
+  g.nMT = ceil_div(T, rlk::TILE_T);
+  g.nVT = ceil_div(V, rlk::TILE_V);
+  g.nST = ceil_div(V, rlk::STAT_V);
+  return g;
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return RLK_OK;
+  g_last_hip_error = e;
+  return RLK_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rlk_abi_version(void) { return RLK_ABI_VERSION; }
+
+int rlk_vocab_tile(void) { return rlk::STAT_V; }
+
+int rlk_last_hip_error(void) { return (int)g_last_hip_error; }
+
+const char *rlk_status_string(int status) {
+  switch (status) {
+    case RLK_OK: return "ok";
+    case RLK_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case RLK_ERR_INVALID_SHAPE:
+      return "invalid shape (T < 0, H <= 0, V <= 0, n < 0 or ld < H)";
+    case RLK_ERR_UNSUPPORTED:
+      return "unsupported size (H must be a multiple of 64 and <= 65536; "
+             "T, V < 2^31; ld <= 2^21)";
+    case RLK_ERR_MISALIGNED:
+      return "misaligned pointer or row stride (16-byte operands, ld % 8 == 0, "
+             "4-byte vectors)";
+    case RLK_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case RLK_ERR_HIP: return "HIP launch error (see rlk_last_hip_error)";
+    default: return "unknown status";
+  }
+}
+
+size_t rlk_selected_logp_workspace_bytes(int64_t T, int64_t V) {
+  if (T <= 0 || V <= 0 || T > MAX_ROWS || V > MAX_ROWS) return 0;
+  return 2 * stats_bytes(T, V) + round_up((size_t)T * sizeof(float));
+}
+
+int rlk_selected_logp(const void *hidden, int64_t ld_hidden,
+                      const void *weight, int64_t ld_weight,
+                      const int32_t *targets, float *logp, float *lse,
+                      int64_t T, int64_t H, int64_t V, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  int st = check_shapes(T, H, V, ld_hidden, ld_weight);
+  if (st != RLK_OK) return st;
+  if (T == 0) return RLK_OK;
+  st = check_operands(hidden, ld_hidden, weight, ld_weight);
+  if (st != RLK_OK) return st;
+  if (!targets || !logp || !lse || !workspace) return RLK_ERR_NULL_POINTER;
+  if (!aligned(targets, 4) || !aligned(logp, 4) || !aligned(lse, 4) ||
+      !aligned(workspace, 16))
+    return RLK_ERR_MISALIGNED;
+  if (workspace_bytes < rlk_selected_logp_workspace_bytes(T, V))
+    return RLK_ERR_WORKSPACE_TOO_SMALL;
+
+  char *ws = static_cast<char *>(workspace);
+  rlk::GemmArgs g = gemm_args(hidden, ld_hidden, weight, ld_weight, T, H, V);
+  g.targets = targets;
+  g.part_m = reinterpret_cast<float *>(ws);
+  g.part_s = reinterpret_cast<float *>(ws + stats_bytes(T, V));
+  g.xt = reinterpret_cast<float *>(ws + 2 * stats_bytes(T, V));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = hip_status(rlk::launch_gemm_stats(g, s));
+  if (st != RLK_OK) return st;
+
+  rlk::MergeArgs mg{};
+  mg.part_m = g.part_m;
+  mg.part_s = g.part_s;
+  mg.xt = g.xt;
+  mg.targets = targets;
+  mg.logp = logp;
+  mg.lse = lse;
+  mg.T = g.T;
+  mg.V = g.V;
+  mg.nST = g.nST;
+  return hip_status(rlk::launch_merge(mg, s));
+}
+
+int rlk_logits(const void *hidden, int64_t ld_hidden, const void *weight,
+               int64_t ld_weight, float *logits, int64_t T, int64_t H,
+               int64_t V, void *stream) {
+  int st = check_shapes(T, H, V, ld_hidden, ld_weight);
+  if (st != RLK_OK) return st;
+  if (T == 0) return RLK_OK;
+  st = check_operands(hidden, ld_hidden, weight, ld_weight);
+  if (st != RLK_OK) return st;
+  if (!logits) return RLK_ERR_NULL_POINTER;
+  if (!aligned(logits, 4)) return RLK_ERR_MISALIGNED;
+  rlk::GemmArgs g = gemm_args(hidden, ld_hidden, weight, ld_weight, T, H, V);
+  g.logits = logits;
+  return hip_status(rlk::launch_gemm_logits(g, static_cast<hipStream_t>(stream)));
+}
+
+int rlk_compare(const float *a, const float *b, int64_t n, double *stats,
+                void *stream) {
+  if (n < 0) return RLK_ERR_INVALID_SHAPE;
+  if (n > MAX_ROWS) return RLK_ERR_UNSUPPORTED;
+  if (!stats || (n > 0 && (!a || !b))) return RLK_ERR_NULL_POINTER;
+  if (!aligned(stats, 8) || !aligned(a, 4) || !aligned(b, 4))
+    return RLK_ERR_MISALIGNED;
+  return hip_status(rlk::launch_compare(a, b, (int)n, stats,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

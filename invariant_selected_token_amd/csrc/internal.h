@@ -1,0 +1,64 @@
+// internal.h -- launch interface between the C ABI layer (api.hip) and the
+// kernels (kernels.hip).  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rlk {
+
+// Workgroup tile of the logit GEMM: TILE_V vocabulary rows x TILE_T token
+// rows, the full hidden dimension per workgroup.  Each wave covers 128 x 128
+// of it; STAT_V = 128 is the width of the vocabulary tiles whose (max, sum of
+// exponentials) statistics are merged, so it is part of the numerical
+// contract.
+constexpr int TILE_V = 256;
+constexpr int STAT_V = 128;
+constexpr int TILE_T = 256;
+constexpr int TILE_K = 64;
+constexpr int GEMM_THREADS = 256;
+// The vocabulary merge: waves per workgroup, each folding one contiguous
+// group of vocabulary tiles; 64 rows per workgroup (one per lane).
+constexpr int MERGE_GROUPS = 8;
+constexpr int MERGE_ROWS = 64;
+constexpr int COMPARE_THREADS = 256;
+
+struct GemmArgs {
+  const uint16_t *hidden;
+  const uint16_t *weight;
+  const int32_t *targets;
+  float *part_m;   // [nST][T] per-statistics-tile maxima
+  float *part_s;   // [nST][T] per-statistics-tile sums of exp(z - m)
+  float *xt;       // [T] target logits
+  float *logits;   // [T][V] (logits stage only)
+  int64_t ldh;
+  int64_t ldw;
+  int T;
+  int H;
+  int V;
+  int nMT;   // token tiles, ceil(T / TILE_T)
+  int nVT;   // workgroup vocabulary tiles, ceil(V / TILE_V)
+  int nST;   // statistics tiles, ceil(V / STAT_V)
+};
+
+struct MergeArgs {
+  const float *part_m;
+  const float *part_s;
+  const float *xt;
+  const int32_t *targets;
+  float *logp;
+  float *lse;
+  int T;
+  int V;
+  int nST;
+};
+
+inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+hipError_t launch_gemm_stats(const GemmArgs &a, hipStream_t s);
+hipError_t launch_gemm_logits(const GemmArgs &a, hipStream_t s);
+hipError_t launch_merge(const MergeArgs &a, hipStream_t s);
+hipError_t launch_compare(const float *a, const float *b, int n,
+                          double *stats, hipStream_t s);
+
+}  // namespace rlk

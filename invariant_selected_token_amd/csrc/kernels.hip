@@ -1,0 +1,412 @@
+// kernels.hip -- gfx950 kernels of the batch-invariant selected-token
+// log-probability path.
+//
+//   gemm_kernel<true>   logits z = W . h^T on bf16 MFMA with fp32 accumulation
+//                       (RL-Kernel blog, section 二: the K split of a GEMM is a
+//                       source of drift; sections 六/七: one workgroup per
+//                       output tile, full K in a fixed order, no split-K),
+//                       with the per-(row, vocabulary tile) max and sum of
+//                       exponentials and the target-logit capture fused into
+//                       its epilogue (section 四: per-block m_j, s_j of the
+//                       LSE; section 七: local statistics per vocabulary
+//                       tile, here 128 wide).  Logits never leave registers.
+//   gemm_kernel<false>  the same main loop, storing the fp32 logits (the
+//                       stage-by-stage comparison of section 五).
+//   merge_kernel        per row, folds the tile statistics in a fixed order
+//                       that depends only on the number of vocabulary tiles,
+//                       then lse = M + log(s) and logp = z_y - lse.
+//   compare_kernel      mismatch count / max |diff| / k3 of two fp32 arrays
+//                       (sections 六/七; the vLLM blog summary's diff = 0).
+//
+// Why rows are batch invariant: every output z[t][v] is produced by the same
+// chain of MFMA instructions over k in increasing order whatever tile or tile
+// position row t lands in; rows beyond T and vocabulary rows beyond V are read
+// as zeros by the buffer unit's range check and never mix into other rows; the
+// epilogue's reduction tree for a row depends only on the tile geometry; the
+// merge's fold depends only on ceil(V / STAT_V).  No split-K, no atomics, no
+// shape-dependent kernel choice.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace rlk {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int STAGE_BYTES = TILE_V * TILE_K * 2;  // one operand, one stage
+constexpr int GROUP_M = 8;   // token tiles that walk the vocabulary together
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+// Buffer resource word 3 for gfx9-family raw buffers (32-bit data format).
+constexpr int RSRC_WORD3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base,
+                                                            uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
+                                           (int)bytes, RSRC_WORD3);
+}
+
+// Logical tile (token tile m, vocabulary tile n) of workgroup b.  The hardware
+// deals workgroups to the 8 XCDs round-robin (b % 8); the first remap hands
+// each XCD a contiguous run of logical tiles so that tiles sharing operands
+// share one L2.  Within the logical order, GROUP_M token tiles advance through
+// the vocabulary together, so a weight tile is read by all of them while it
+// is hot.  Only the schedule changes; every tile's arithmetic is the same.
+__device__ __forceinline__ void tile_of_block(int b, int nMT, int nVT, int &m,
+                                              int &n) {
+  const int total = nMT * nVT;
+  const int per_xcd = total >> 3;
+  int L = b;
+  if (b < (per_xcd << 3)) L = (b & 7) * per_xcd + (b >> 3);
+  const int in_group = GROUP_M * nVT;
+  const int g = L / in_group;
+  const int first_m = g * GROUP_M;
+  const int gsm = min(nMT - first_m, GROUP_M);
+  const int r = L - g * in_group;
+  m = first_m + r % gsm;
+  n = r / gsm;
+}
+
+// LDS layout of one operand stage: 256 rows x 64 bf16 (128 bytes per row);
+// the 16-byte chunk c of row r sits at chunk position c ^ (r & 7).
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  return row * 128 + ((chunk ^ (row & 7)) << 4);
+}
+
+// One workgroup tile.  MASK is true only for the workgroup column that holds
+// the end of the vocabulary (V not a multiple of TILE_V, or a statistics tile
+// that is cut by V); it is chosen by a tile-uniform branch in the kernel and
+// depends on V alone, never on T or on where a row sits.
+template <bool STATS, bool MASK>
+__device__ __forceinline__ void gemm_tile(const GemmArgs &a, char *smem, int m,
+                                          int n) {
+  const int v0 = n * TILE_V;
+  const int t0 = m * TILE_T;
+  const int vrows = min(TILE_V, a.V - v0);
+  const int trows = min(TILE_T, a.T - t0);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wv = wave & 1;   // vocabulary half of the tile
+  const int wt = wave >> 1;  // token half of the tile
+  const int fr = lane & 31;  // MFMA row / column within a 32-block
+  const int fk = lane >> 5;  // which 8-wide K slice of a 16-wide MFMA step
+
+  // Global -> LDS staging: thread loads rows lrow + 32 i (i = 0..7), chunk lkc.
+  const int lrow = tid >> 3;
+  const int lkc = tid & 7;
+  const __amdgpu_buffer_rsrc_t rw =
+      make_rsrc(a.weight + (size_t)v0 * a.ldw, (uint32_t)(vrows * a.ldw * 2));
+  const __amdgpu_buffer_rsrc_t rh =
+      make_rsrc(a.hidden + (size_t)t0 * a.ldh, (uint32_t)(trows * a.ldh * 2));
+  const uint32_t offw = (uint32_t)(lrow * a.ldw * 2 + lkc * 16);
+  const uint32_t offh = (uint32_t)(lrow * a.ldh * 2 + lkc * 16);
+  const uint32_t stw = (uint32_t)(32 * a.ldw * 2);
+  const uint32_t sth = (uint32_t)(32 * a.ldh * 2);
+  const int st_base = lds_off(lrow, lkc);  // (lrow + 32 i) & 7 == lrow & 7
+
+  u32x4 gw[8], gh[8];
+  auto gload = [&](int kb) {
+    const uint32_t kofs = (uint32_t)kb * (TILE_K * 2);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      gw[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, offw + i * stw + kofs, 0, 0);
+      gh[i] = __builtin_amdgcn_raw_buffer_load_b128(rh, offh + i * sth + kofs, 0, 0);
+    }
+  };
+  auto lstore = [&](int stage) {
+    char *sw = smem + stage * (2 * STAGE_BYTES);
+    char *sh = sw + STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      *(u32x4 *)(sw + st_base + i * 32 * 128) = gw[i];
+      *(u32x4 *)(sh + st_base + i * 32 * 128) = gh[i];
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int nk = a.H / TILE_K;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+
+  // Fragment read offsets (bytes) within a stage, for K step ks = 0.
+  const int arow = wv * 128 + fr;
+  const int brow = wt * 128 + fr;
+
+  for (int kb = 0; kb < nk; ++kb) {
+    const int stage = kb & 1;
+    if (kb + 1 < nk) gload(kb + 1);
+    const char *sw = smem + stage * (2 * STAGE_BYTES);
+    const char *sh = sw + STAGE_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < TILE_K / 16; ++ks) {
+      bf16x8 fa[4], fb[4];
+      const int chunk = 2 * ks + fk;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        fa[i] = *(const bf16x8 *)(sw + lds_off(arow + 32 * i, chunk));
+        fb[i] = *(const bf16x8 *)(sh + lds_off(brow + 32 * i, chunk));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j],
+                                                             acc[i][j], 0, 0, 0);
+    }
+    if (kb + 1 < nk) lstore(stage ^ 1);
+    __syncthreads();
+  }
+
+  // acc[i][j][r] holds z[t][v] for
+  //   v = v0 + wv*128 + 32 i + 8 (r >> 2) + 4 fk + (r & 3)
+  //   t = t0 + wt*128 + 32 j + fr
+  const int vbase = v0 + wv * 128;
+  if (!STATS) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = t0 + wt * 128 + 32 * j + fr;
+      if (t >= a.T) continue;
+      float *row = a.logits + (size_t)t * a.V;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int v = vbase + 32 * i + 8 * (r >> 2) + 4 * fk + (r & 3);
+          if (v < a.V) row[v] = acc[i][j][r];
+        }
+    }
+    return;
+  }
+
+  // Statistics tiles are 128 vocabulary rows wide: wave (wv, wt) owns tile
+  // js = 2 n + wv for its 128 token rows, so no data crosses waves.  A wave
+  // whose tile starts at or past V (only in the last workgroup column when
+  // V mod 256 <= 128) has nothing to write.
+  const int js = 2 * n + wv;
+  if (js >= a.nST) return;
+
+  // Columns past the vocabulary end count as -inf: they add nothing to the
+  // max and exactly 0 to the sum.  On valid columns the masked and unmasked
+  // instantiations compute the same thing.
+  const int lim = a.V - vbase - 4 * fk;  // columns at offset < lim are valid
+  float mt[4], st[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // 1) tile max: this lane's 64 values in (i, r) order, then the partner
+    //    lane (fk flipped) holding the other 64 values of the tile.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool out = MASK && (32 * i + 8 * (r >> 2) + (r & 3) >= lim);
+        mx = fmaxf(mx, out ? -INFINITY : acc[i][j][r]);
+      }
+    const float mo = __shfl_xor(mx, 32);
+    const float m2 = fk == 0 ? fmaxf(mx, mo) : fmaxf(mo, mx);
+    // 2) sum of exp(z - m), same tree; m is taken as 0 when the whole tile is
+    //    -inf so that such a tile adds exactly 0.  z == m gives exp(0) = 1
+    //    exactly, so the sum is >= 1 when the max is finite.
+    const float ms = (m2 == -INFINITY) ? 0.0f : m2;
+    float sx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool out = MASK && (32 * i + 8 * (r >> 2) + (r & 3) >= lim);
+        const float z = out ? -INFINITY : acc[i][j][r];
+        sx = sx + __builtin_amdgcn_exp2f((z - ms) * LOG2E);
+      }
+    const float so = __shfl_xor(sx, 32);
+    mt[j] = m2;
+    st[j] = fk == 0 ? sx + so : so + sx;
+  }
+
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = t0 + wt * 128 + 32 * j + fr;
+    // 3) tile-major [nST][T] statistics (coalesced over rows).
+    if (t < a.T) {
+      const size_t o = (size_t)js * a.T + t;
+      if (fk == 0) a.part_m[o] = mt[j];
+      else a.part_s[o] = st[j];
+    }
+    // 4) target capture: the one lane holding z[t][y[t]] writes xt[t], the
+    //    value picked by a fixed select tree over the lane's 64 values.
+    const int y = (t < a.T) ? a.targets[t] : -1;
+    const int rel = y - vbase;
+    const bool hit = rel >= 0 && rel < STAT_V && ((rel >> 2) & 1) == fk;
+    if (__any(hit)) {
+      // block i = rel >> 5, register r = ((w >> 3) << 2) | (w & 3), w = rel & 31
+      const int bi = (rel >> 5) & 3;
+      const int w = rel & 31;
+      const int ri = ((w >> 3) << 2) | (w & 3);
+      float sel[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float lo = (bi & 1) ? acc[1][j][r] : acc[0][j][r];
+        const float hi = (bi & 1) ? acc[3][j][r] : acc[2][j][r];
+        sel[r] = (bi & 2) ? hi : lo;
+      }
+#pragma unroll
+      for (int lvl = 0; lvl < 4; ++lvl) {
+        const bool bit = (ri >> lvl) & 1;
+#pragma unroll
+        for (int q = 0; q < (8 >> lvl); ++q)
+          sel[q] = bit ? sel[2 * q + 1] : sel[2 * q];
+      }
+      if (hit) a.xt[t] = sel[0];
+    }
+  }
+}
+
+template <bool STATS>
+__global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[4 * STAGE_BYTES];
+  int m, n;
+  tile_of_block(blockIdx.x, a.nMT, a.nVT, m, n);
+  if (STATS && (n + 1) * TILE_V > a.V)
+    gemm_tile<STATS, true>(a, smem, m, n);
+  else
+    gemm_tile<STATS, false>(a, smem, m, n);
+}
+
+// Per row t: M = max_j m_j (exact in any order), then
+// s = sum_j s_j exp(m_j - M) as MERGE_GROUPS sequential folds over contiguous
+// groups of ceil(nST / MERGE_GROUPS) statistics tiles, then the group sums
+// folded in order 0 .. MERGE_GROUPS-1.  The shape depends only on nST.
+__global__ __launch_bounds__(MERGE_GROUPS * MERGE_ROWS) void merge_kernel(
+    const MergeArgs a) {
+  __shared__ float red[MERGE_GROUPS][MERGE_ROWS];
+  const int lane = threadIdx.x & (MERGE_ROWS - 1);
+  const int g = threadIdx.x / MERGE_ROWS;
+  const int t = blockIdx.x * MERGE_ROWS + lane;
+  const bool valid = t < a.T;
+  const int gs = (a.nST + MERGE_GROUPS - 1) / MERGE_GROUPS;
+  const int j0 = min(a.nST, g * gs);
+  const int j1 = min(a.nST, j0 + gs);
+
+  float mg = -INFINITY;
+  if (valid)
+    for (int j = j0; j < j1; ++j) mg = fmaxf(mg, a.part_m[(size_t)j * a.T + t]);
+  red[g][lane] = mg;
+  __syncthreads();
+  float M = red[0][lane];
+#pragma unroll
+  for (int q = 1; q < MERGE_GROUPS; ++q) M = fmaxf(M, red[q][lane]);
+  __syncthreads();
+  const float Ms = (M == -INFINITY) ? 0.0f : M;
+
+  float sg = 0.0f;
+  if (valid)
+    for (int j = j0; j < j1; ++j) {
+      const size_t o = (size_t)j * a.T + t;
+      sg = sg + a.part_s[o] * __builtin_amdgcn_exp2f((a.part_m[o] - Ms) * LOG2E);
+    }
+  red[g][lane] = sg;
+  __syncthreads();
+  if (g == 0 && valid) {
+    float s = red[0][lane];
+#pragma unroll
+    for (int q = 1; q < MERGE_GROUPS; ++q) s = s + red[q][lane];
+    const float lse = M + __builtin_amdgcn_logf(s) * LN2;
+    const int y = a.targets[t];
+    a.lse[t] = lse;
+    a.logp[t] = (y >= 0 && y < a.V) ? a.xt[t] - lse : __builtin_nanf("");
+  }
+}
+
+__global__ __launch_bounds__(COMPARE_THREADS) void compare_kernel(
+    const float *__restrict__ x, const float *__restrict__ y, int n,
+    double *__restrict__ stats) {
+  __shared__ double sd[4][COMPARE_THREADS];
+  __shared__ long long sc[2][COMPARE_THREADS];
+  const int tid = threadIdx.x;
+  long long mism = 0, kcnt = 0;
+  double mx = 0.0, sa = 0.0, sq = 0.0, k3 = 0.0;
+  for (int i = tid; i < n; i += COMPARE_THREADS) {
+    const float a = x[i], b = y[i];
+    if (__float_as_uint(a) != __float_as_uint(b)) {
+      ++mism;
+      double d = fabs((double)a - (double)b);
+      if (isnan(d)) d = INFINITY;
+      mx = fmax(mx, d);
+      sa = sa + d;
+      sq = sq + d * d;
+    }
+    if (isfinite(a) && isfinite(b)) {
+      const double lr = (double)a - (double)b;
+      k3 = k3 + ((exp(lr) - 1.0) - lr);
+      ++kcnt;
+    }
+  }
+  sc[0][tid] = mism;
+  sc[1][tid] = kcnt;
+  sd[0][tid] = mx;
+  sd[1][tid] = sa;
+  sd[2][tid] = sq;
+  sd[3][tid] = k3;
+  __syncthreads();
+  for (int s = COMPARE_THREADS / 2; s > 0; s >>= 1) {
+    if (tid < s) {
+      sc[0][tid] += sc[0][tid + s];
+      sc[1][tid] += sc[1][tid + s];
+      sd[0][tid] = fmax(sd[0][tid], sd[0][tid + s]);
+      sd[1][tid] = sd[1][tid] + sd[1][tid + s];
+      sd[2][tid] = sd[2][tid] + sd[2][tid + s];
+      sd[3][tid] = sd[3][tid] + sd[3][tid + s];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    stats[0] = (double)n;
+    stats[1] = (double)sc[0][0];
+    stats[2] = sd[0][0];
+    stats[3] = sd[1][0];
+    stats[4] = sd[2][0];
+    stats[5] = sd[3][0];
+    stats[6] = (double)sc[1][0];
+    stats[7] = 0.0;
+  }
+}
+
+hipError_t launch_gemm_stats(const GemmArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(gemm_kernel<true>, dim3(a.nMT * a.nVT), dim3(GEMM_THREADS),
+                     0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_logits(const GemmArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(gemm_kernel<false>, dim3(a.nMT * a.nVT),
+                     dim3(GEMM_THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(merge_kernel, dim3(ceil_div(a.T, MERGE_ROWS)),
+                     dim3(MERGE_GROUPS * MERGE_ROWS), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_compare(const float *a, const float *b, int n, double *stats,
+                          hipStream_t s) {
+  hipLaunchKernelGGL(compare_kernel, dim3(1), dim3(COMPARE_THREADS), 0, s, a, b,
+                     n, stats);
+  return hipGetLastError();
+}
+
+}  // namespace rlk

@@ -198,7 +198,7 @@ def compare_stats(a, b) -> dict:
     d = np.where(same, 0.0, d)
     d = np.where(np.isnan(d), np.inf, d)
     fin = np.isfinite(a64) & np.isfinite(b64)
-    lr = (a64 - b64)[fin]
+    lr = a64[fin] - b64[fin]
     k3 = np.exp(lr) - 1.0 - lr
     out = {
         "n": int(n),

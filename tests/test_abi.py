@@ -1,0 +1,156 @@
+"""CPU tests of the C-ABI library: exports, constants and every error path.
+
+No test here launches a kernel: each call either returns before its first
+HIP call (validation) or touches no device at all.  Pointer values used on
+the error paths are never dereferenced by the library.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import invariant_selected_token_amd as rlk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rlk.h")
+
+FAKE = 0x10000          # a 64 KiB-aligned non-null address, never dereferenced
+WS_FAKE = 1 << 40
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rlk_\w+)\s*\(", text)))
+
+
+def test_header_declares_what_the_binding_knows():
+    assert _declared_functions() == sorted(rlk.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = rlk.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_constants():
+    assert rlk.rlk_abi_version() == 1
+    assert rlk.rlk_vocab_tile() == 128
+    msgs = {rlk.rlk_status_string(s) for s in range(7)}
+    assert len(msgs) == 7 and all(msgs)
+    assert rlk.rlk_status_string(99) == "unknown status"
+
+
+def test_workspace_size():
+    ws = rlk.rlk_selected_logp_workspace_bytes
+    assert ws(0, 151936) == 0 and ws(-1, 10) == 0 and ws(5, 0) == 0
+
+    def expect(T, V):
+        r = lambda x: (x + 255) // 256 * 256
+        return 2 * r(((V + 127) // 128) * T * 4) + r(T * 4)
+
+    for T, V in [(1, 1), (1, 151936), (64, 4096), (4096, 151936), (16384, 151936),
+                 (257, 129)]:
+        assert ws(T, V) == expect(T, V)
+    prev = 0
+    for T in range(1, 600, 37):
+        assert ws(T, 151936) >= prev
+        prev = ws(T, 151936)
+
+
+def _call(hidden=FAKE, ldh=256, weight=FAKE, ldw=256, targets=FAKE, logp=FAKE,
+          lse=FAKE, T=4, H=256, V=1000, ws=WS_FAKE, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = max(rlk.rlk_selected_logp_workspace_bytes(T, V), 0)
+    return rlk.lib().rlk_selected_logp(hidden, ldh, weight, ldw, targets, logp, lse,
+                                       T, H, V, ws, ws_bytes, stream)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), rlk.RLK_ERR_INVALID_SHAPE),
+    (dict(H=0), rlk.RLK_ERR_INVALID_SHAPE),
+    (dict(H=-64), rlk.RLK_ERR_INVALID_SHAPE),
+    (dict(V=0), rlk.RLK_ERR_INVALID_SHAPE),
+    (dict(ldh=128), rlk.RLK_ERR_INVALID_SHAPE),
+    (dict(ldw=192), rlk.RLK_ERR_INVALID_SHAPE),
+    (dict(H=200, ldh=256, ldw=256), rlk.RLK_ERR_UNSUPPORTED),
+    (dict(H=65536 + 64, ldh=65536 + 64, ldw=65536 + 64), rlk.RLK_ERR_UNSUPPORTED),
+    (dict(ldh=(1 << 21) + 8), rlk.RLK_ERR_UNSUPPORTED),
+    (dict(T=1 << 31), rlk.RLK_ERR_UNSUPPORTED),
+    (dict(V=1 << 31), rlk.RLK_ERR_UNSUPPORTED),
+    (dict(hidden=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(weight=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(targets=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(logp=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(lse=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(ws=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(hidden=FAKE + 8), rlk.RLK_ERR_MISALIGNED),
+    (dict(weight=FAKE + 2), rlk.RLK_ERR_MISALIGNED),
+    (dict(ldh=260), rlk.RLK_ERR_MISALIGNED),
+    (dict(ldw=257), rlk.RLK_ERR_MISALIGNED),
+    (dict(targets=FAKE + 2), rlk.RLK_ERR_MISALIGNED),
+    (dict(logp=FAKE + 1), rlk.RLK_ERR_MISALIGNED),
+    (dict(lse=FAKE + 3), rlk.RLK_ERR_MISALIGNED),
+    (dict(ws=WS_FAKE + 4), rlk.RLK_ERR_MISALIGNED),
+    (dict(ws_bytes=100), rlk.RLK_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_selected_logp_error_paths(kw, status):
+    assert _call(**kw) == status
+    assert rlk.rlk_last_hip_error() == 0
+
+
+def test_selected_logp_empty_batch_is_a_no_op():
+    assert _call(T=0, hidden=None, weight=None, targets=None, logp=None, lse=None,
+                 ws=None, ws_bytes=0) == rlk.RLK_OK
+
+
+def test_workspace_one_byte_short():
+    need = rlk.rlk_selected_logp_workspace_bytes(4, 1000)
+    assert _call(ws_bytes=need - 1) == rlk.RLK_ERR_WORKSPACE_TOO_SMALL
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-5), rlk.RLK_ERR_INVALID_SHAPE),
+    (dict(H=96, ldh=96, ldw=96), rlk.RLK_ERR_UNSUPPORTED),
+    (dict(logits=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(hidden=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(logits=FAKE + 2), rlk.RLK_ERR_MISALIGNED),
+    (dict(T=0, logits=None, hidden=None, weight=None), rlk.RLK_OK),
+])
+def test_logits_error_paths(kw, status):
+    a = dict(hidden=FAKE, ldh=256, weight=FAKE, ldw=256, logits=FAKE, T=4, H=256,
+             V=100, stream=None)
+    a.update(kw)
+    assert rlk.lib().rlk_logits(a["hidden"], a["ldh"], a["weight"], a["ldw"],
+                                a["logits"], a["T"], a["H"], a["V"], a["stream"]) == status
+
+
+@pytest.mark.parametrize("a,b,n,stats,status", [
+    (FAKE, FAKE, -1, FAKE, rlk.RLK_ERR_INVALID_SHAPE),
+    (FAKE, FAKE, 1 << 31, FAKE, rlk.RLK_ERR_UNSUPPORTED),
+    (FAKE, FAKE, 10, None, rlk.RLK_ERR_NULL_POINTER),
+    (None, FAKE, 10, FAKE, rlk.RLK_ERR_NULL_POINTER),
+    (FAKE, FAKE, 10, FAKE + 4, rlk.RLK_ERR_MISALIGNED),
+    (FAKE + 1, FAKE, 10, FAKE, rlk.RLK_ERR_MISALIGNED),
+])
+def test_compare_error_paths(a, b, n, stats, status):
+    assert rlk.lib().rlk_compare(a, b, n, stats, None) == status
+
+
+def test_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    h = torch.zeros((2, 64), dtype=torch.bfloat16)
+    w = torch.zeros((8, 64), dtype=torch.bfloat16)
+    y = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        rlk.rlk_selected_logp(h, w, y)
+    with pytest.raises(ValueError):
+        rlk.rlk_logits(h, w)
+
+
+def test_status_error_type_carries_the_message():
+    e = rlk.RLKError(rlk.RLK_ERR_MISALIGNED, "where")
+    assert "misaligned" in str(e) and e.status == rlk.RLK_ERR_MISALIGNED

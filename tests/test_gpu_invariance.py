@@ -1,0 +1,159 @@
+"""Bitwise self-consistency of the HIP path (the pages' 0-mismatch criterion).
+
+A row's fp32 logp and lse must be bit-for-bit the same whatever batch it is
+in, wherever it sits, packed or per sequence, prefill or decode, and across
+repeated calls (RL-Kernel blog, sections 五-七: bitwise, not a tolerance; the
+vLLM blog summary's batch independence and phase consistency).  Bits are
+compared on the device by rlk_compare and on the host by integer views.
+"""
+
+import numpy as np
+import pytest
+
+import invariant_selected_token_amd as rlk
+from invariant_selected_token_amd import synth
+
+from conftest import to_dev_bf16, to_dev_i32
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+def _bits(x):
+    return x.contiguous().view(torch.int32)
+
+
+def _assert_bits_equal(a, b, what):
+    st = rlk.consistency_report(rlk.rlk_compare(a.contiguous(), b.contiguous()))
+    print(f"{what}: mismatch_count={st['mismatch_count']} "
+          f"max_abs_diff={st['max_abs_diff']:.3e} over {st['n']}", flush=True)
+    assert st["mismatch_count"] == 0 and st["max_abs_diff"] == 0.0, what
+    assert torch.equal(_bits(a), _bits(b)), what
+
+
+def test_tiny_batch_one_vs_batch(tiny):
+    lp, lse = rlk.rlk_selected_logp(tiny.hidden, tiny.weight, tiny.targets)
+    lp1 = torch.empty_like(lp)
+    lse1 = torch.empty_like(lse)
+    for t in range(tiny.case.T):
+        a, b = rlk.rlk_selected_logp(tiny.hidden[t:t + 1], tiny.weight, tiny.targets[t:t + 1])
+        lp1[t:t + 1] = a
+        lse1[t:t + 1] = b
+    _assert_bits_equal(lp1, lp, "tiny batch-1 vs batch-64 logp")
+    _assert_bits_equal(lse1, lse, "tiny batch-1 vs batch-64 lse")
+
+
+def test_tiny_repeats_and_permutations(tiny):
+    lp, lse = rlk.rlk_selected_logp(tiny.hidden, tiny.weight, tiny.targets)
+    for _ in range(100):
+        a, b = rlk.rlk_selected_logp(tiny.hidden, tiny.weight, tiny.targets)
+        _assert_bits_equal(a, lp, "tiny repeat logp")
+        _assert_bits_equal(b, lse, "tiny repeat lse")
+    rng = np.random.Generator(np.random.PCG64(17))
+    for _ in range(8):
+        p = torch.from_numpy(rng.permutation(tiny.case.T)).to(lp.device)
+        a, b = rlk.rlk_selected_logp(tiny.hidden[p].contiguous(), tiny.weight,
+                                     tiny.targets[p].contiguous())
+        _assert_bits_equal(a, lp[p], "tiny permuted logp")
+        _assert_bits_equal(b, lse[p], "tiny permuted lse")
+
+
+def test_every_tile_position_same_bits(prefill):
+    """One vector copied into all 512 rows (every position of two token
+    tiles): all rows must carry identical bits."""
+    h = prefill.hidden[1234:1235].expand(512, -1).contiguous()
+    y = prefill.targets[1234:1235].expand(512).contiguous()
+    lp, lse = rlk.rlk_selected_logp(h, prefill.weight, y)
+    _assert_bits_equal(lp, lp[0:1].expand(512).contiguous(), "all positions logp")
+    _assert_bits_equal(lse, lse[0:1].expand(512).contiguous(), "all positions lse")
+
+
+def test_prefill_packed_vs_per_sequence(prefill):
+    lp, lse = rlk.rlk_selected_logp(prefill.hidden, prefill.weight, prefill.targets)
+    parts_lp, parts_lse = [], []
+    for s in range(8):
+        sl = slice(512 * s, 512 * (s + 1))
+        a, b = rlk.rlk_selected_logp(prefill.hidden[sl], prefill.weight, prefill.targets[sl])
+        parts_lp.append(a)
+        parts_lse.append(b)
+    _assert_bits_equal(torch.cat(parts_lp), lp, "packed vs per-sequence logp")
+    _assert_bits_equal(torch.cat(parts_lse), lse, "packed vs per-sequence lse")
+
+
+def test_prefill_repeats(prefill):
+    lp, lse = rlk.rlk_selected_logp(prefill.hidden, prefill.weight, prefill.targets)
+    stats = torch.zeros((100, 8), dtype=torch.float64, device=lp.device)
+    a = torch.empty_like(lp)
+    b = torch.empty_like(lse)
+    for i in range(100):
+        rlk.rlk_selected_logp(prefill.hidden, prefill.weight, prefill.targets, logp=a, lse=b)
+        rlk.rlk_compare(a, lp, stats=stats[i])
+    s = stats.cpu().numpy()
+    print(f"100 repeats: total mismatch {s[:, 1].sum()} max diff {s[:, 2].max()}", flush=True)
+    assert s[:, 1].sum() == 0 and s[:, 2].max() == 0.0
+    _assert_bits_equal(b, lse, "repeat lse")
+
+
+def test_prefill_permuted_rows(prefill):
+    lp, lse = rlk.rlk_selected_logp(prefill.hidden, prefill.weight, prefill.targets)
+    rng = np.random.Generator(np.random.PCG64(23))
+    p = torch.from_numpy(rng.permutation(prefill.case.T)).to(lp.device)
+    a, b = rlk.rlk_selected_logp(prefill.hidden[p].contiguous(), prefill.weight,
+                                 prefill.targets[p].contiguous())
+    _assert_bits_equal(a, lp[p], "permuted logp")
+    _assert_bits_equal(b, lse[p], "permuted lse")
+
+
+def test_decode_sweep_matches_batch_one_and_prefill(prefill):
+    """Decode batches of {1,2,3,7,16,64,255,256} rows from a pool of 256
+    prefill vectors, at random positions: each row's bits equal its batch-1
+    bits and its bits inside the 4096-row prefill call."""
+    plan = synth.decode_plan(prefill_T=prefill.case.T)
+    dev = prefill.hidden.device
+    pool = torch.from_numpy(plan["pool"]).to(dev)
+    lp_pre, lse_pre = rlk.rlk_selected_logp(prefill.hidden, prefill.weight, prefill.targets)
+    ph = prefill.hidden[pool].contiguous()
+    py = prefill.targets[pool].contiguous()
+    lp1 = torch.empty(256, dtype=torch.float32, device=dev)
+    lse1 = torch.empty_like(lp1)
+    for i in range(256):
+        a, b = rlk.rlk_selected_logp(ph[i:i + 1], prefill.weight, py[i:i + 1])
+        lp1[i:i + 1] = a
+        lse1[i:i + 1] = b
+    _assert_bits_equal(lp1, lp_pre[pool], "batch-1 vs prefill logp")
+    _assert_bits_equal(lse1, lse_pre[pool], "batch-1 vs prefill lse")
+    for B, slots in plan["batches"].items():
+        s = torch.from_numpy(slots).to(dev)
+        a, b = rlk.rlk_selected_logp(ph[s].contiguous(), prefill.weight, py[s].contiguous())
+        _assert_bits_equal(a, lp1[s], f"decode B={B} logp")
+        _assert_bits_equal(b, lse1[s], f"decode B={B} lse")
+
+
+def test_other_rows_do_not_matter(tiny, dev):
+    """Replacing every other row's contents and targets leaves a row's bits."""
+    lp, lse = rlk.rlk_selected_logp(tiny.hidden, tiny.weight, tiny.targets)
+    c = synth.normal_case("noise", 555, tiny.case.T, tiny.case.H, tiny.case.V)
+    h2 = to_dev_bf16(c.hidden, dev)
+    y2 = to_dev_i32(c.targets, dev)
+    keep = [0, 13, 40]
+    h2[keep] = tiny.hidden[keep]
+    y2[keep] = tiny.targets[keep]
+    a, b = rlk.rlk_selected_logp(h2, tiny.weight, y2)
+    _assert_bits_equal(a[keep], lp[keep], "content independence logp")
+    _assert_bits_equal(b[keep], lse[keep], "content independence lse")
+
+
+def test_negative_control_order_change_is_visible(prefill):
+    """Reversing the K order (same mathematics, other fp32 rounding) must be
+    seen by the harness as last-bit drift: mismatches > 0, tiny differences.
+    This shows the bitwise checks above can see the drift the pages warn
+    about (RL-Kernel blog, section 二: summation order changes the last bits)."""
+    rows = slice(0, 512)
+    lp, _ = rlk.rlk_selected_logp(prefill.hidden[rows], prefill.weight, prefill.targets[rows])
+    hr = prefill.hidden[rows].flip(1).contiguous()
+    wr = prefill.weight.flip(1).contiguous()
+    a, _ = rlk.rlk_selected_logp(hr, wr, prefill.targets[rows])
+    st = rlk.consistency_report(rlk.rlk_compare(a, lp))
+    print(f"negative control: {st}", flush=True)
+    assert st["mismatch_count"] > 0
+    assert 0.0 < st["max_abs_diff"] < 1e-3
