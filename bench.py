@@ -1,0 +1,209 @@
+#!/usr/bin/env python3
+"""Benchmark of the batch-invariant selected-token log-probability path.
+
+Workload: the Qwen3-8B LM-head shape on the training-side recompute, T = 4096
+packed rows (8 sequences x 512 tokens), H = 4096, V = 151936, bf16 hidden and
+weight (synthetic, seeded), uniform targets.  One step is one pass of the
+whole hot path on one batch, with inputs already resident in HBM:
+  1. rlk_vocab_stats  logit GEMM (bf16 MFMA, fp32 accumulation) with the fused
+                      per-(row, 128-wide vocabulary tile) max / sum of
+                      exponentials and the target-logit capture;
+  2. rlk_vocab_merge  fixed-order fold of the tile statistics -> lse, logp;
+  3. rlk_compare x2   bitwise consistency of this step's logp and lse against
+                      the first call's (mismatch count, max |diff|).
+Prints one JSON line.  Only one GPU is used; --gpus N > 1 exits.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+KERNEL_SRC = os.path.join(ROOT, "invariant_selected_token_amd", "csrc", "kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_stats_prefill_T4096_traffic.md")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the GEMM kernel from the committed rocprofv3
+    counter summary, or None when the kernel source changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not b or m.group(1) != kernel_source_digest():
+        return None
+    return float(b.group(1))
+
+
+def cpu_baseline(case, seconds: float) -> dict:
+    """The fp64 oracle, as it stands, on a bounded sample of the same rows."""
+    import numpy as np
+
+    from oracle import oracle as orc
+
+    cores = orc.max_threads()
+    probe = max(2, min(cores, 16))
+    t0 = time.perf_counter()
+    orc.selected_logp(case.hidden[:probe], case.weight, case.targets[:probe])
+    per_row = (time.perf_counter() - t0) / probe
+    n = int(max(probe, min(case.T, round(seconds / max(per_row, 1e-9)))))
+    rng = np.random.Generator(np.random.PCG64(4321))
+    rows = np.sort(rng.choice(case.T, size=n, replace=False))
+    t0 = time.perf_counter()
+    orc.selected_logp(case.hidden[rows], case.weight, case.targets[rows])
+    wall = time.perf_counter() - t0
+    return {"value": n / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} of {case.T} rows of the same workload (seeded choice), "
+                      f"full vocabulary V={case.V}, fp64, {wall:.1f} s wall"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall-time budget of the oracle CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="run one plain device copy of this many MiB before the "
+                         "timed region (reference kernel for HBM counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this path is measured on one GPU only; the row-sharded "
+              "multi-GPU layout is described in the design notes but not run. "
+              "Use --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import invariant_selected_token_amd as rlk
+    from invariant_selected_token_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    case = synth.prefill_case()
+    T, H, V = case.T, case.H, case.V
+    log(f"bench: workload {case.name} on {torch.cuda.get_device_name(dev)}")
+
+    def to_dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    hidden, weight = to_dev(case.hidden), to_dev(case.weight)
+    targets = torch.from_numpy(case.targets).to(dev)
+    ws = rlk.workspace_for(T, V, dev)
+    logp = torch.empty(T, dtype=torch.float32, device=dev)
+    lse = torch.empty(T, dtype=torch.float32, device=dev)
+    ref_lp, ref_lse = rlk.rlk_selected_logp(hidden, weight, targets)
+    stats_lp = torch.zeros((max(args.steps, 1), 8), dtype=torch.float64, device=dev)
+    stats_lse = torch.zeros_like(stats_lp)
+
+    def step(i):
+        rlk.rlk_vocab_stats(hidden, weight, targets, ws)
+        rlk.rlk_vocab_merge(targets, ws, V, logp=logp, lse=lse)
+        rlk.rlk_compare(logp, ref_lp, stats=stats_lp[i])
+        rlk.rlk_compare(lse, ref_lse, stats=stats_lse[i])
+
+    if args.calib_copy_mb > 0:
+        n = args.calib_copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for i in range(args.warmup):
+        step(0)
+    torch.cuda.synchronize()
+    stats_lp.zero_()
+    stats_lse.zero_()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        e = ev[i]
+        e[0].record()
+        rlk.rlk_vocab_stats(hidden, weight, targets, ws)
+        e[1].record()
+        rlk.rlk_vocab_merge(targets, ws, V, logp=logp, lse=lse)
+        e[2].record()
+        rlk.rlk_compare(logp, ref_lp, stats=stats_lp[i])
+        rlk.rlk_compare(lse, ref_lse, stats=stats_lse[i])
+        e[3].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    gemm_ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(K)) / K
+    merge_ms = sum(ev[i][1].elapsed_time(ev[i][2]) for i in range(K)) / K
+    check_ms = sum(ev[i][2].elapsed_time(ev[i][3]) for i in range(K)) / K
+    s_lp = stats_lp.cpu().numpy()
+    s_lse = stats_lse.cpu().numpy()
+    mismatch = int(s_lp[:, 1].sum() + s_lse[:, 1].sum())
+    max_diff = float(max(s_lp[:, 2].max(), s_lse[:, 2].max()))
+
+    flops = 2.0 * T * H * V                      # algorithmic work per launch
+    achieved = flops / (gemm_ms * 1e-3) / 1e12   # TFLOP/s
+    nst = (V + 127) // 128
+    merge_bytes = 8.0 * nst * T + 4.0 * T * 2 + 8.0 * T   # partials + xt + targets, logp + lse
+    traffic = measured_traffic()
+    out = {
+        "metric": "selected-token logp tokens/s + % bf16 MFMA peak, Qwen3-8B LM head, 0 mismatch",
+        "value": T * K / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": wall / K * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": case.name, "T": T, "H": H, "V": V,
+                   "seq_len": 512, "n_seqs": T // 512, "seed": case.meta["seed"],
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic},
+        "stages_ms": {"gemm_stats": gemm_ms, "merge": merge_ms, "consistency_check": check_ms},
+        "merge_hbm": {"GB/s": merge_bytes / (merge_ms * 1e-3) / 1e9,
+                      "peak": PEAK_HBM_GBS, "bytes": merge_bytes},
+        "consistency": {"mismatch_count": mismatch, "max_abs_diff": max_diff,
+                        "compared": 2 * T * K},
+        "kernel_source": kernel_source_digest(),
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the fp64 oracle on the host")
+        out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0 if mismatch == 0 else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

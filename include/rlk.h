@@ -126,6 +126,27 @@ int rlk_selected_logp(const void *hidden, int64_t ld_hidden,
                       int64_t T, int64_t H, int64_t V,
                       void *workspace, size_t workspace_bytes, void *stream);
 
+/* The two stages of rlk_selected_logp, for callers that time or overlap
+ * them separately (or exchange the tile statistics between devices that
+ * hold different vocabulary shards).  Same argument rules as above; the
+ * workspace written by rlk_vocab_stats is read by rlk_vocab_merge and must be
+ * passed with the same T and V.  rlk_selected_logp is exactly these two
+ * calls in sequence on one stream.
+ *   rlk_vocab_stats  the logit GEMM with the fused per-(row, 128-wide tile)
+ *                    max / sum of exponentials and the target-logit capture
+ *                    (RL-Kernel blog, section 七: local statistics per
+ *                    vocabulary tile).  Writes only the workspace.
+ *   rlk_vocab_merge  the per-row fixed-order fold of the tile statistics and
+ *                    the gather (section 四: merging blocks of the LSE in a
+ *                    fixed order).  Reads the workspace, writes logp, lse. */
+int rlk_vocab_stats(const void *hidden, int64_t ld_hidden, const void *weight,
+                    int64_t ld_weight, const int32_t *targets, int64_t T,
+                    int64_t H, int64_t V, void *workspace,
+                    size_t workspace_bytes, void *stream);
+int rlk_vocab_merge(const int32_t *targets, float *logp, float *lse, int64_t T,
+                    int64_t V, const void *workspace, size_t workspace_bytes,
+                    void *stream);
+
 /* The logits stage alone, for stage-by-stage comparison (the RL-Kernel blog,
  * section 五: compare intermediate results to find the first divergence).
  * Runs the very same GEMM main loop as rlk_selected_logp and stores the fp32

@@ -29,7 +29,8 @@ RLK_ERR_HIP = 6
 EXPORTED = (
     "rlk_abi_version", "rlk_status_string", "rlk_last_hip_error",
     "rlk_vocab_tile", "rlk_selected_logp_workspace_bytes",
-    "rlk_selected_logp", "rlk_logits", "rlk_compare",
+    "rlk_selected_logp", "rlk_vocab_stats", "rlk_vocab_merge", "rlk_logits",
+    "rlk_compare",
 )
 
 _lib = None
@@ -65,6 +66,10 @@ def lib() -> ctypes.CDLL:
     L.rlk_selected_logp.argtypes = [vp, i64, vp, i64, vp, vp, vp, i64, i64, i64,
                                     vp, sz, vp]
     L.rlk_selected_logp.restype = c_int
+    L.rlk_vocab_stats.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, vp, sz, vp]
+    L.rlk_vocab_stats.restype = c_int
+    L.rlk_vocab_merge.argtypes = [vp, vp, vp, i64, i64, vp, sz, vp]
+    L.rlk_vocab_merge.restype = c_int
     L.rlk_logits.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, vp]
     L.rlk_logits.restype = c_int
     L.rlk_compare.argtypes = [vp, vp, i64, vp, vp]
@@ -129,15 +134,7 @@ def _call(where, status):
         raise RLKError(status, where)
 
 
-def rlk_selected_logp(hidden, weight, targets, logp=None, lse=None,
-                      workspace=None, V=None, stream=None):
-    """logp[T], lse[T] (fp32) for hidden [T, H], weight [>=V, H], targets [T].
-
-    ``V`` defaults to ``weight.shape[0]``; pass the real vocabulary size when
-    ``weight`` carries padding rows.  Outputs and the workspace are allocated
-    on ``hidden.device`` when not given.  Runs on ``stream`` (default: the
-    current torch stream) without synchronising.
-    """
+def _prepare(hidden, weight, targets, V):
     torch = _torch()
     dev = hidden.device
     hp, ldh = _bf16_operand("hidden", hidden, dev)
@@ -151,6 +148,11 @@ def rlk_selected_logp(hidden, weight, targets, logp=None, lse=None,
     if targets.dtype != torch.int32 or targets.shape != (T,) or not targets.is_contiguous():
         raise ValueError("targets must be a contiguous int32 [T] tensor")
     _check_device("targets", targets, dev)
+    return dev, hp, ldh, wp, ldw, T, H, V
+
+
+def _outputs(dev, T, logp, lse):
+    torch = _torch()
     if logp is None:
         logp = torch.empty(T, dtype=torch.float32, device=dev)
     if lse is None:
@@ -159,14 +161,66 @@ def rlk_selected_logp(hidden, weight, targets, logp=None, lse=None,
         if t.dtype != torch.float32 or t.shape != (T,) or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous float32 [T] tensor")
         _check_device(name, t, dev)
+    return logp, lse
+
+
+def workspace_for(T: int, V: int, device):
+    """A device workspace tensor large enough for T rows and vocabulary V."""
+    torch = _torch()
     need = rlk_selected_logp_workspace_bytes(T, V)
+    return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+
+
+def _workspace(dev, T, V, workspace):
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        workspace = workspace_for(T, V, dev)
     _check_device("workspace", workspace, dev)
-    ws_bytes = workspace.numel() * workspace.element_size()
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def rlk_selected_logp(hidden, weight, targets, logp=None, lse=None,
+                      workspace=None, V=None, stream=None):
+    """logp[T], lse[T] (fp32) for hidden [T, H], weight [>=V, H], targets [T].
+
+    ``V`` defaults to ``weight.shape[0]``; pass the real vocabulary size when
+    ``weight`` carries padding rows.  Outputs and the workspace are allocated
+    on ``hidden.device`` when not given.  Runs on ``stream`` (default: the
+    current torch stream) without synchronising.
+    """
+    dev, hp, ldh, wp, ldw, T, H, V = _prepare(hidden, weight, targets, V)
+    logp, lse = _outputs(dev, T, logp, lse)
+    ws, ws_bytes = _workspace(dev, T, V, workspace)
     _call("rlk_selected_logp", lib().rlk_selected_logp(
         hp, ldh, wp, ldw, targets.data_ptr(), logp.data_ptr(), lse.data_ptr(),
-        T, H, V, workspace.data_ptr(), ws_bytes, _stream_ptr(stream, dev)))
+        T, H, V, ws.data_ptr(), ws_bytes, _stream_ptr(stream, dev)))
+    return logp, lse
+
+
+def rlk_vocab_stats(hidden, weight, targets, workspace, V=None, stream=None):
+    """Stage 1: logit GEMM + per-tile statistics + target capture into
+    ``workspace`` (see :func:`workspace_for`)."""
+    dev, hp, ldh, wp, ldw, T, H, V = _prepare(hidden, weight, targets, V)
+    ws, ws_bytes = _workspace(dev, T, V, workspace)
+    _call("rlk_vocab_stats", lib().rlk_vocab_stats(
+        hp, ldh, wp, ldw, targets.data_ptr(), T, H, V, ws.data_ptr(), ws_bytes,
+        _stream_ptr(stream, dev)))
+    return ws
+
+
+def rlk_vocab_merge(targets, workspace, V, logp=None, lse=None, stream=None):
+    """Stage 2: fixed-order fold of the tile statistics -> (logp, lse)."""
+    torch = _torch()
+    dev = targets.device
+    _check_device("targets", targets, dev)
+    if targets.dtype != torch.int32 or targets.dim() != 1 or not targets.is_contiguous():
+        raise ValueError("targets must be a contiguous int32 [T] tensor")
+    T = targets.shape[0]
+    logp, lse = _outputs(dev, T, logp, lse)
+    _check_device("workspace", workspace, dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _call("rlk_vocab_merge", lib().rlk_vocab_merge(
+        targets.data_ptr(), logp.data_ptr(), lse.data_ptr(), T, int(V),
+        workspace.data_ptr(), ws_bytes, _stream_ptr(stream, dev)))
     return logp, lse
 
 

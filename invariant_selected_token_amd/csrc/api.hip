@@ -104,44 +104,72 @@ size_t rlk_selected_logp_workspace_bytes(int64_t T, int64_t V) {
   return 2 * stats_bytes(T, V) + round_up((size_t)T * sizeof(float));
 }
 
-int rlk_selected_logp(const void *hidden, int64_t ld_hidden,
-                      const void *weight, int64_t ld_weight,
-                      const int32_t *targets, float *logp, float *lse,
-                      int64_t T, int64_t H, int64_t V, void *workspace,
-                      size_t workspace_bytes, void *stream) {
+int rlk_vocab_stats(const void *hidden, int64_t ld_hidden, const void *weight,
+                    int64_t ld_weight, const int32_t *targets, int64_t T,
+                    int64_t H, int64_t V, void *workspace,
+                    size_t workspace_bytes, void *stream) {
   int st = check_shapes(T, H, V, ld_hidden, ld_weight);
   if (st != RLK_OK) return st;
   if (T == 0) return RLK_OK;
   st = check_operands(hidden, ld_hidden, weight, ld_weight);
   if (st != RLK_OK) return st;
-  if (!targets || !logp || !lse || !workspace) return RLK_ERR_NULL_POINTER;
-  if (!aligned(targets, 4) || !aligned(logp, 4) || !aligned(lse, 4) ||
-      !aligned(workspace, 16))
-    return RLK_ERR_MISALIGNED;
+  if (!targets || !workspace) return RLK_ERR_NULL_POINTER;
+  if (!aligned(targets, 4) || !aligned(workspace, 16)) return RLK_ERR_MISALIGNED;
   if (workspace_bytes < rlk_selected_logp_workspace_bytes(T, V))
     return RLK_ERR_WORKSPACE_TOO_SMALL;
-
   char *ws = static_cast<char *>(workspace);
   rlk::GemmArgs g = gemm_args(hidden, ld_hidden, weight, ld_weight, T, H, V);
   g.targets = targets;
   g.part_m = reinterpret_cast<float *>(ws);
   g.part_s = reinterpret_cast<float *>(ws + stats_bytes(T, V));
   g.xt = reinterpret_cast<float *>(ws + 2 * stats_bytes(T, V));
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  st = hip_status(rlk::launch_gemm_stats(g, s));
-  if (st != RLK_OK) return st;
+  return hip_status(rlk::launch_gemm_stats(g, static_cast<hipStream_t>(stream)));
+}
 
+int rlk_vocab_merge(const int32_t *targets, float *logp, float *lse, int64_t T,
+                    int64_t V, const void *workspace, size_t workspace_bytes,
+                    void *stream) {
+  if (T < 0 || V <= 0) return RLK_ERR_INVALID_SHAPE;
+  if (T > MAX_ROWS || V > MAX_ROWS) return RLK_ERR_UNSUPPORTED;
+  if (T == 0) return RLK_OK;
+  if (!targets || !logp || !lse || !workspace) return RLK_ERR_NULL_POINTER;
+  if (!aligned(targets, 4) || !aligned(logp, 4) || !aligned(lse, 4) ||
+      !aligned(workspace, 16))
+    return RLK_ERR_MISALIGNED;
+  if (workspace_bytes < rlk_selected_logp_workspace_bytes(T, V))
+    return RLK_ERR_WORKSPACE_TOO_SMALL;
+  const char *ws = static_cast<const char *>(workspace);
   rlk::MergeArgs mg{};
-  mg.part_m = g.part_m;
-  mg.part_s = g.part_s;
-  mg.xt = g.xt;
+  mg.part_m = reinterpret_cast<const float *>(ws);
+  mg.part_s = reinterpret_cast<const float *>(ws + stats_bytes(T, V));
+  mg.xt = reinterpret_cast<const float *>(ws + 2 * stats_bytes(T, V));
   mg.targets = targets;
   mg.logp = logp;
   mg.lse = lse;
-  mg.T = g.T;
-  mg.V = g.V;
-  mg.nST = g.nST;
-  return hip_status(rlk::launch_merge(mg, s));
+  mg.T = (int)T;
+  mg.V = (int)V;
+  mg.nST = ceil_div(V, rlk::STAT_V);
+  return hip_status(rlk::launch_merge(mg, static_cast<hipStream_t>(stream)));
+}
+
+int rlk_selected_logp(const void *hidden, int64_t ld_hidden,
+                      const void *weight, int64_t ld_weight,
+                      const int32_t *targets, float *logp, float *lse,
+                      int64_t T, int64_t H, int64_t V, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  // Validate everything both stages need before launching the first one.
+  int st = check_shapes(T, H, V, ld_hidden, ld_weight);
+  if (st != RLK_OK) return st;
+  if (T == 0) return RLK_OK;
+  st = check_operands(hidden, ld_hidden, weight, ld_weight);
+  if (st != RLK_OK) return st;
+  if (!targets || !logp || !lse || !workspace) return RLK_ERR_NULL_POINTER;
+  if (!aligned(logp, 4) || !aligned(lse, 4)) return RLK_ERR_MISALIGNED;
+  st = rlk_vocab_stats(hidden, ld_hidden, weight, ld_weight, targets, T, H, V,
+                       workspace, workspace_bytes, stream);
+  if (st != RLK_OK) return st;
+  return rlk_vocab_merge(targets, logp, lse, T, V, workspace, workspace_bytes,
+                         stream);
 }
 
 int rlk_logits(const void *hidden, int64_t ld_hidden, const void *weight,

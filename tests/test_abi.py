@@ -154,3 +154,49 @@ def test_binding_rejects_host_tensors():
 def test_status_error_type_carries_the_message():
     e = rlk.RLKError(rlk.RLK_ERR_MISALIGNED, "where")
     assert "misaligned" in str(e) and e.status == rlk.RLK_ERR_MISALIGNED
+
+
+def _stats(hidden=FAKE, ldh=256, weight=FAKE, ldw=256, targets=FAKE, T=4, H=256,
+           V=1000, ws=WS_FAKE, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = rlk.rlk_selected_logp_workspace_bytes(T, V)
+    return rlk.lib().rlk_vocab_stats(hidden, ldh, weight, ldw, targets, T, H, V, ws,
+                                     ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), rlk.RLK_ERR_INVALID_SHAPE),
+    (dict(H=100, ldh=104, ldw=104), rlk.RLK_ERR_UNSUPPORTED),
+    (dict(targets=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(ws=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(hidden=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(targets=FAKE + 1), rlk.RLK_ERR_MISALIGNED),
+    (dict(ws=WS_FAKE + 8), rlk.RLK_ERR_MISALIGNED),
+    (dict(ws_bytes=64), rlk.RLK_ERR_WORKSPACE_TOO_SMALL),
+    (dict(T=0, hidden=None, weight=None, targets=None, ws=None, ws_bytes=0), rlk.RLK_OK),
+])
+def test_vocab_stats_error_paths(kw, status):
+    assert _stats(**kw) == status
+
+
+def _merge(targets=FAKE, logp=FAKE, lse=FAKE, T=4, V=1000, ws=WS_FAKE, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = rlk.rlk_selected_logp_workspace_bytes(T, V)
+    return rlk.lib().rlk_vocab_merge(targets, logp, lse, T, V, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), rlk.RLK_ERR_INVALID_SHAPE),
+    (dict(V=0), rlk.RLK_ERR_INVALID_SHAPE),
+    (dict(V=1 << 31), rlk.RLK_ERR_UNSUPPORTED),
+    (dict(targets=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(logp=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(lse=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(ws=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(lse=FAKE + 2), rlk.RLK_ERR_MISALIGNED),
+    (dict(ws=WS_FAKE + 4), rlk.RLK_ERR_MISALIGNED),
+    (dict(ws_bytes=16), rlk.RLK_ERR_WORKSPACE_TOO_SMALL),
+    (dict(T=0, targets=None, logp=None, lse=None, ws=None, ws_bytes=0), rlk.RLK_OK),
+])
+def test_vocab_merge_error_paths(kw, status):
+    assert _merge(**kw) == status

@@ -157,3 +157,13 @@ def test_negative_control_order_change_is_visible(prefill):
     print(f"negative control: {st}", flush=True)
     assert st["mismatch_count"] > 0
     assert 0.0 < st["max_abs_diff"] < 1e-3
+
+
+def test_two_stages_equal_one_call(prefill):
+    """rlk_vocab_stats + rlk_vocab_merge reproduce rlk_selected_logp bitwise."""
+    lp, lse = rlk.rlk_selected_logp(prefill.hidden, prefill.weight, prefill.targets)
+    ws = rlk.workspace_for(prefill.case.T, prefill.case.V, lp.device)
+    rlk.rlk_vocab_stats(prefill.hidden, prefill.weight, prefill.targets, ws)
+    a, b = rlk.rlk_vocab_merge(prefill.targets, ws, prefill.case.V)
+    _assert_bits_equal(a, lp, "two-stage logp")
+    _assert_bits_equal(b, lse, "two-stage lse")
