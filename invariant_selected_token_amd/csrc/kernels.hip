@@ -1,7 +1,7 @@
 // kernels.hip -- gfx950 kernels of the batch-invariant selected-token
 // log-probability path.
 //
-//   gemm_kernel<true>   logits z = W . h^T on bf16 MFMA with fp32 accumulation
+//   gemm_kernel<true,*> logits z = W . h^T on bf16 MFMA with fp32 accumulation
 //                       (RL-Kernel blog, section 二: the K split of a GEMM is a
 //                       source of drift; sections 六/七: one workgroup per
 //                       output tile, full K in a fixed order, no split-K),
@@ -10,7 +10,7 @@
 //                       its epilogue (section 四: per-block m_j, s_j of the
 //                       LSE; section 七: local statistics per vocabulary
 //                       tile, here 128 wide).  Logits never leave registers.
-//   gemm_kernel<false>  the same main loop, storing the fp32 logits (the
+//   gemm_kernel<false,false> the same main loop, storing fp32 logits (the
 //                       stage-by-stage comparison of section 五).
 //   merge_kernel        per row, folds the tile statistics in a fixed order
 //                       that depends only on the number of vocabulary tiles,
@@ -29,6 +29,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace rlk {
@@ -43,6 +45,9 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 // Buffer resource word 3 for gfx9-family raw buffers (32-bit data format).
 constexpr int RSRC_WORD3 = 0x00020000;
+// s_waitcnt immediate for "vmcnt(0)" only (expcnt and lgkmcnt left at max).
+constexpr int VMCNT0 = 0x0F70;
+
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base,
                                                             uint32_t bytes) {
@@ -78,9 +83,8 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
 }
 
 // One workgroup tile.  MASK is true only for the workgroup column that holds
-// the end of the vocabulary (V not a multiple of TILE_V, or a statistics tile
-// that is cut by V); it is chosen by a tile-uniform branch in the kernel and
-// depends on V alone, never on T or on where a row sits.
+// the end of the vocabulary when V is not a multiple of TILE_V; it depends on
+// V alone, never on T or on where a row sits.
 template <bool STATS, bool MASK>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &a, char *smem, int m,
                                           int n) {
@@ -91,42 +95,38 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, char *smem, int m,
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wv = wave & 1;   // vocabulary half of the tile
   const int wt = wave >> 1;  // token half of the tile
   const int fr = lane & 31;  // MFMA row / column within a 32-block
   const int fk = lane >> 5;  // which 8-wide K slice of a 16-wide MFMA step
 
-  // Global -> LDS staging: thread loads rows lrow + 32 i (i = 0..7), chunk lkc.
-  const int lrow = tid >> 3;
-  const int lkc = tid & 7;
+  // Global -> LDS: direct-to-LDS buffer loads (each lane's 16 bytes land in
+  // LDS slot base + 16 * lane).  Load i of wave w fills the 1 KiB block
+  // b = 4 i + w of a stage, i.e. rows 8 b .. 8 b + 7; lane l supplies row
+  // 8 b + (l >> 3) and, because of the XOR swizzle, global chunk
+  // (l & 7) ^ (l >> 3) of that row.  The K offset of the block rides in the
+  // scalar offset; rows past T or V fall outside the resource and read 0.
   const __amdgpu_buffer_rsrc_t rw =
       make_rsrc(a.weight + (size_t)v0 * a.ldw, (uint32_t)(vrows * a.ldw * 2));
   const __amdgpu_buffer_rsrc_t rh =
       make_rsrc(a.hidden + (size_t)t0 * a.ldh, (uint32_t)(trows * a.ldh * 2));
-  const uint32_t offw = (uint32_t)(lrow * a.ldw * 2 + lkc * 16);
-  const uint32_t offh = (uint32_t)(lrow * a.ldh * 2 + lkc * 16);
-  const uint32_t stw = (uint32_t)(32 * a.ldw * 2);
-  const uint32_t sth = (uint32_t)(32 * a.ldh * 2);
-  const int st_base = lds_off(lrow, lkc);  // (lrow + 32 i) & 7 == lrow & 7
-
-  u32x4 gw[8], gh[8];
-  auto gload = [&](int kb) {
-    const uint32_t kofs = (uint32_t)kb * (TILE_K * 2);
+  const int lrow = 8 * (tid >> 6) + (lane >> 3);
+  const int lchunk = (lane & 7) ^ (lane >> 3);
+  uint32_t gofs[2][8];  // [operand][load]
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      gw[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, offw + i * stw + kofs, 0, 0);
-      gh[i] = __builtin_amdgcn_raw_buffer_load_b128(rh, offh + i * sth + kofs, 0, 0);
-    }
-  };
-  auto lstore = [&](int stage) {
-    char *sw = smem + stage * (2 * STAGE_BYTES);
-    char *sh = sw + STAGE_BYTES;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      *(u32x4 *)(sw + st_base + i * 32 * 128) = gw[i];
-      *(u32x4 *)(sh + st_base + i * 32 * 128) = gh[i];
-    }
+  for (int i = 0; i < 8; ++i) {
+    gofs[0][i] = (uint32_t)((lrow + 32 * i) * a.ldw * 2 + lchunk * 16);
+    gofs[1][i] = (uint32_t)((lrow + 32 * i) * a.ldh * 2 + lchunk * 16);
+  }
+  typedef __attribute__((address_space(3))) void lds_void;
+  // Load q (0..15) of K block kb into `stage`: operand q & 1, row group q >> 1.
+  auto gload = [&](__amdgpu_buffer_rsrc_t r_w, __amdgpu_buffer_rsrc_t r_h, int stage,
+                   int kb, int q) {
+    const int op = q & 1, i = q >> 1;
+    char *dst = smem + stage * (2 * STAGE_BYTES) + op * STAGE_BYTES + (4 * i + wave) * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? r_h : r_w, (lds_void *)dst, 16, gofs[op][i],
+                                             (uint32_t)kb * (TILE_K * 2), 0, 0);
   };
 
   f32x16 acc[4][4];
@@ -137,39 +137,95 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, char *smem, int m,
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nk = a.H / TILE_K;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  // Fragment read offsets (bytes) within a stage, for K step ks = 0.
-  const int arow = wv * 128 + fr;
-  const int brow = wt * 128 + fr;
-
-  for (int kb = 0; kb < nk; ++kb) {
-    const int stage = kb & 1;
-    if (kb + 1 < nk) gload(kb + 1);
-    const char *sw = smem + stage * (2 * STAGE_BYTES);
-    const char *sh = sw + STAGE_BYTES;
+  // Fragment reads: A (weight) rows wv*128 + 32 i + fr, B (hidden) rows
+  // wt*128 + 32 j + fr, 16-byte chunk 2 ks + fk of the 64-wide K step.  Byte
+  // addresses per (stage, ks); the block index i or j adds i * 4096.
+  uint32_t ra[2][4], rb[2][4];
 #pragma unroll
-    for (int ks = 0; ks < TILE_K / 16; ++ks) {
-      bf16x8 fa[4], fb[4];
-      const int chunk = 2 * ks + fk;
+  for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        fa[i] = *(const bf16x8 *)(sw + lds_off(arow + 32 * i, chunk));
-        fb[i] = *(const bf16x8 *)(sh + lds_off(brow + 32 * i, chunk));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j],
-                                                             acc[i][j], 0, 0, 0);
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint32_t x = (uint32_t)(((2 * ks + fk) ^ (fr & 7)) << 4);
+      ra[st][ks] = st * (2 * STAGE_BYTES) + (wv * 128 + fr) * 128 + x;
+      rb[st][ks] = st * (2 * STAGE_BYTES) + STAGE_BYTES + (wt * 128 + fr) * 128 + x;
     }
-    if (kb + 1 < nk) lstore(stage ^ 1);
-    __syncthreads();
+  bf16x8 fa[2][4], fb[2][4];
+  // Read number w (0..7) of the fragments of (stage, ks) into set `buf`, in
+  // the order the MFMAs consume them: A0, B0, B1, B2, B3, A1, A2, A3.
+  auto fread = [&](int buf, int st, int ks, int w) {
+    if (w == 0) fa[buf][0] = *(const bf16x8 *)(smem + ra[st][ks]);
+    else if (w <= 4) fb[buf][w - 1] = *(const bf16x8 *)(smem + rb[st][ks] + (w - 1) * 4096);
+    else fa[buf][w - 4] = *(const bf16x8 *)(smem + ra[st][ks] + (w - 4) * 4096);
+  };
+  auto mfma = [&](int buf, int q) {
+    const int i = q >> 2, j = q & 3;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j],
+                                                       0, 0, 0);
+  };
+
+  // The main loop.  Each accumulator advances in increasing k (16 per MFMA);
+  // the fixed instruction order below only decides what overlaps with what:
+  // every MFMA of K step ks is followed by one read of step ks + 1's
+  // fragments (first half) or one direct-to-LDS load of the next K block
+  // (second half, steps 0 and 1).  Half-way through step 3 the wave waits
+  // for its loads and the workgroup meets at the barrier (the next block has
+  // landed; this block is no longer read), then the next block's first
+  // fragments are read under the last eight MFMAs.
+  auto k_block = [&](int kb, auto stage, auto more, __amdgpu_buffer_rsrc_t r_w,
+                     __amdgpu_buffer_rsrc_t r_h) {
+    constexpr int st = decltype(stage)::value;    // == kb & 1
+    constexpr bool MORE = decltype(more)::value;  // not the last K block
+#pragma unroll
+    for (int ks = 0; ks < 3; ++ks) {
+      const int cur = ks & 1;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        mfma(cur, q);
+        if (q < 8) fread(cur ^ 1, st, ks + 1, q);
+        else if (MORE && ks < 2) gload(r_w, r_h, st ^ 1, kb + 1, 8 * ks + (q - 8));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      mfma(1, q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (MORE) {
+      __builtin_amdgcn_s_waitcnt(VMCNT0);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int q = 8; q < 16; ++q) {
+      mfma(1, q);
+      if (MORE) fread(0, st ^ 1, 0, q - 8);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // K blocks are run in pairs (stage 0, stage 1).  When H / 64 is odd, one
+  // more block is appended whose loads go through a resource of zero size:
+  // it reads zeros and adds exact zero products (it can only turn a logit
+  // of -0 into +0, the same way for every row of a given H).
+  const int nk = a.H / TILE_K;
+  const int nk2 = nk + (nk & 1);
+  const __amdgpu_buffer_rsrc_t zero = make_rsrc(a.weight, 0u);
+  const __amdgpu_buffer_rsrc_t rw_last = (nk & 1) ? zero : rw;
+  const __amdgpu_buffer_rsrc_t rh_last = (nk & 1) ? zero : rh;
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) gload(rw, rh, 0, 0, q);
+  __builtin_amdgcn_s_waitcnt(VMCNT0);
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < 8; ++w) fread(0, 0, 0, w);
+  for (int kb = 0; kb + 2 < nk2; kb += 2) {
+    k_block(kb, S0{}, std::true_type{}, rw, rh);
+    k_block(kb + 1, S1{}, std::true_type{}, rw, rh);
   }
+  k_block(nk2 - 2, S0{}, std::true_type{}, rw_last, rh_last);
+  k_block(nk2 - 1, S1{}, std::false_type{}, rw, rh);
 
   // acc[i][j][r] holds z[t][v] for
   //   v = v0 + wv*128 + 32 i + 8 (r >> 2) + 4 fk + (r & 3)
@@ -274,15 +330,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, char *smem, int m,
   }
 }
 
-template <bool STATS>
+// The masked instantiation runs as its own launch over the last workgroup
+// column only (when V is not a multiple of TILE_V), so each kernel holds one
+// copy of the tile code.  Which column a tile is in depends on V alone.
+template <bool STATS, bool MASK>
 __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[4 * STAGE_BYTES];
   int m, n;
-  tile_of_block(blockIdx.x, a.nMT, a.nVT, m, n);
-  if (STATS && (n + 1) * TILE_V > a.V)
-    gemm_tile<STATS, true>(a, smem, m, n);
-  else
-    gemm_tile<STATS, false>(a, smem, m, n);
+  if (MASK) {
+    m = blockIdx.x;
+    n = a.nVT - 1;
+  } else {
+    tile_of_block(blockIdx.x, a.nMT, a.nVTm, m, n);
+  }
+  gemm_tile<STATS, MASK>(a, smem, m, n);
 }
 
 // Per row t: M = max_j m_j (exact in any order), then
@@ -385,14 +446,25 @@ __global__ __launch_bounds__(COMPARE_THREADS) void compare_kernel(
 }
 
 hipError_t launch_gemm_stats(const GemmArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(gemm_kernel<true>, dim3(a.nMT * a.nVT), dim3(GEMM_THREADS),
-                     0, s, a);
+  GemmArgs g = a;
+  g.nVTm = a.V / TILE_V;  // columns that need no vocabulary mask
+  if (g.nVTm > 0) {
+    hipLaunchKernelGGL((gemm_kernel<true, false>), dim3(g.nMT * g.nVTm),
+                       dim3(GEMM_THREADS), 0, s, g);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (g.nVTm < g.nVT)
+    hipLaunchKernelGGL((gemm_kernel<true, true>), dim3(g.nMT), dim3(GEMM_THREADS), 0,
+                       s, g);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_logits(const GemmArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(gemm_kernel<false>, dim3(a.nMT * a.nVT),
-                     dim3(GEMM_THREADS), 0, s, a);
+  GemmArgs g = a;
+  g.nVTm = a.nVT;  // stores are guarded per element; no mask variant needed
+  hipLaunchKernelGGL((gemm_kernel<false, false>), dim3(g.nMT * g.nVTm),
+                     dim3(GEMM_THREADS), 0, s, g);
   return hipGetLastError();
 }
 
