@@ -19,8 +19,9 @@ constexpr int TILE_K = 64;
 constexpr int GEMM_THREADS = 256;
 // The vocabulary merge: waves per workgroup, each folding one contiguous
 // group of vocabulary tiles; 64 rows per workgroup (one per lane).
-constexpr int MERGE_GROUPS = 8;
+constexpr int MERGE_GROUPS = 16;
 constexpr int MERGE_ROWS = 64;
+constexpr int MERGE_UNROLL = 16;
 constexpr int COMPARE_THREADS = 256;
 
 struct GemmArgs {

@@ -45,8 +45,15 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 // Buffer resource word 3 for gfx9-family raw buffers (32-bit data format).
 constexpr int RSRC_WORD3 = 0x00020000;
-// s_waitcnt immediate for "vmcnt(0)" only (expcnt and lgkmcnt left at max).
+// s_waitcnt immediates for "vmcnt(0)" / "vmcnt(2)" only (expcnt and lgkmcnt
+// left at their maxima).
 constexpr int VMCNT0 = 0x0F70;
+// "vmcnt(2) lgkmcnt(0)"
+constexpr int VMCNT2_LGKMCNT0 = 0x0072;
+// K blocks between an L2 prefetch and the block's direct-to-LDS load.
+constexpr int PREFETCH_AHEAD = 2;
+// LDS bytes past the two stages that absorb the prefetch loads' data.
+constexpr int PREFETCH_SINK = 256;
 
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base,
@@ -77,10 +84,14 @@ __device__ __forceinline__ void tile_of_block(int b, int nMT, int nVT, int &m,
 }
 
 // LDS layout of one operand stage: 256 rows x 64 bf16 (128 bytes per row);
-// the 16-byte chunk c of row r sits at chunk position c ^ (r & 7).
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * 128 + ((chunk ^ (row & 7)) << 4);
-}
+// the 16-byte chunk c of row r sits at chunk position c ^ swz(r) with
+// swz(r) = (r & 7) ^ ((r >> 3) & 1).  A fragment read has 32 consecutive
+// lanes on 32 consecutive rows and one chunk; with this swizzle any 8
+// consecutive rows (aligned) use 8 distinct positions of a 128-byte bank
+// window, and any 16 (aligned) use 16 distinct 16-byte slots of a 256-byte
+// window, so ds_read_b128 is free of bank conflicts whether the LDS serves it
+// 8 or 16 lanes per cycle.
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 // One workgroup tile.  MASK is true only for the workgroup column that holds
 // the end of the vocabulary when V is not a multiple of TILE_V; it depends on
@@ -104,15 +115,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, char *smem, int m,
   // Global -> LDS: direct-to-LDS buffer loads (each lane's 16 bytes land in
   // LDS slot base + 16 * lane).  Load i of wave w fills the 1 KiB block
   // b = 4 i + w of a stage, i.e. rows 8 b .. 8 b + 7; lane l supplies row
-  // 8 b + (l >> 3) and, because of the XOR swizzle, global chunk
-  // (l & 7) ^ (l >> 3) of that row.  The K offset of the block rides in the
-  // scalar offset; rows past T or V fall outside the resource and read 0.
+  // 8 b + (l >> 3) and, because of the swizzle, global chunk
+  // (l & 7) ^ swz(row) = (l & 7) ^ (l >> 3) ^ (w & 1) of that row.  The K
+  // offset of the block rides in the scalar offset; rows past T or V fall
+  // outside the resource and read 0.
   const __amdgpu_buffer_rsrc_t rw =
       make_rsrc(a.weight + (size_t)v0 * a.ldw, (uint32_t)(vrows * a.ldw * 2));
   const __amdgpu_buffer_rsrc_t rh =
       make_rsrc(a.hidden + (size_t)t0 * a.ldh, (uint32_t)(trows * a.ldh * 2));
   const int lrow = 8 * (tid >> 6) + (lane >> 3);
-  const int lchunk = (lane & 7) ^ (lane >> 3);
+  const int lchunk = (lane & 7) ^ (lane >> 3) ^ ((tid >> 6) & 1);
   uint32_t gofs[2][8];  // [operand][load]
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -126,6 +138,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, char *smem, int m,
     const int op = q & 1, i = q >> 1;
     char *dst = smem + stage * (2 * STAGE_BYTES) + op * STAGE_BYTES + (4 * i + wave) * 1024;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? r_h : r_w, (lds_void *)dst, 16, gofs[op][i],
+                                             (uint32_t)kb * (TILE_K * 2), 0, 0);
+  };
+
+  // L2 prefetch of K block kb: one 4-byte load per 128-byte line, lane l
+  // touching row 32 (l >> 3) + 8 w + (l & 7) -- the 64 rows this wave's own
+  // loads of that block will cover.  The data lands in a scratch slot of LDS
+  // that nothing reads; the point is that the line is in L2 when the real
+  // load comes PREFETCH_AHEAD blocks later.  Past the end of a row or of the
+  // resource the load stays in bounds or reads nothing.
+  const uint32_t pofs_w = (uint32_t)((32 * (lane >> 3) + 8 * (tid >> 6) + (lane & 7)) * a.ldw * 2);
+  const uint32_t pofs_h = (uint32_t)((32 * (lane >> 3) + 8 * (tid >> 6) + (lane & 7)) * a.ldh * 2);
+  auto prefetch = [&](int op, int kb) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? rh : rw, (lds_void *)(smem + 4 * STAGE_BYTES),
+                                             4, op ? pofs_h : pofs_w,
                                              (uint32_t)kb * (TILE_K * 2), 0, 0);
   };
 
@@ -145,7 +171,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, char *smem, int m,
   for (int st = 0; st < 2; ++st)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const uint32_t x = (uint32_t)(((2 * ks + fk) ^ (fr & 7)) << 4);
+      const uint32_t x = (uint32_t)(((2 * ks + fk) ^ swz(fr)) << 4);  // swz(32 i + fr) == swz(fr)
       ra[st][ks] = st * (2 * STAGE_BYTES) + (wv * 128 + fr) * 128 + x;
       rb[st][ks] = st * (2 * STAGE_BYTES) + STAGE_BYTES + (wt * 128 + fr) * 128 + x;
     }
@@ -183,6 +209,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, char *smem, int m,
         mfma(cur, q);
         if (q < 8) fread(cur ^ 1, st, ks + 1, q);
         else if (MORE && ks < 2) gload(r_w, r_h, st ^ 1, kb + 1, 8 * ks + (q - 8));
+        else if (MORE && ks == 2 && q < 10) prefetch(q - 8, kb + 1 + PREFETCH_AHEAD);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -192,8 +219,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, char *smem, int m,
       __builtin_amdgcn_sched_barrier(0);
     }
     if (MORE) {
-      __builtin_amdgcn_s_waitcnt(VMCNT0);
-      __syncthreads();
+      // This wave's loads of the next block have landed (only the two
+      // prefetches issued after them may still be in flight) and its reads
+      // of this block are complete; then the workgroup barrier.  A plain
+      // s_barrier, not a fenced __syncthreads(), so that the prefetches are
+      // not waited for; the empty asm statements keep the compiler from
+      // moving memory accesses across it.
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(VMCNT2_LGKMCNT0);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
     }
 #pragma unroll
     for (int q = 8; q < 16; ++q) {
@@ -216,6 +251,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, char *smem, int m,
   using S1 = std::integral_constant<int, 1>;
 #pragma unroll
   for (int q = 0; q < 16; ++q) gload(rw, rh, 0, 0, q);
+#pragma unroll
+  for (int kp = 1; kp <= PREFETCH_AHEAD; ++kp) {
+    prefetch(0, kp);
+    prefetch(1, kp);
+  }
   __builtin_amdgcn_s_waitcnt(VMCNT0);
   __syncthreads();
 #pragma unroll
@@ -335,7 +375,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, char *smem, int m,
 // copy of the tile code.  Which column a tile is in depends on V alone.
 template <bool STATS, bool MASK>
 __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[4 * STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[4 * STAGE_BYTES + PREFETCH_SINK];
   int m, n;
   if (MASK) {
     m = blockIdx.x;
@@ -350,6 +390,9 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmArgs a) {
 // s = sum_j s_j exp(m_j - M) as MERGE_GROUPS sequential folds over contiguous
 // groups of ceil(nST / MERGE_GROUPS) statistics tiles, then the group sums
 // folded in order 0 .. MERGE_GROUPS-1.  The shape depends only on nST.
+// Loads are issued MERGE_UNROLL at a time ahead of the fold; slots past the
+// group's end contribute max(-inf) and + 0 * exp(-inf) = + 0, which changes
+// nothing (the running sum is never -0).
 __global__ __launch_bounds__(MERGE_GROUPS * MERGE_ROWS) void merge_kernel(
     const MergeArgs a) {
   __shared__ float red[MERGE_GROUPS][MERGE_ROWS];
@@ -360,10 +403,19 @@ __global__ __launch_bounds__(MERGE_GROUPS * MERGE_ROWS) void merge_kernel(
   const int gs = (a.nST + MERGE_GROUPS - 1) / MERGE_GROUPS;
   const int j0 = min(a.nST, g * gs);
   const int j1 = min(a.nST, j0 + gs);
+  const float *pm = a.part_m + (valid ? t : 0);
+  const float *ps = a.part_s + (valid ? t : 0);
+  const size_t T = (size_t)a.T;
 
   float mg = -INFINITY;
-  if (valid)
-    for (int j = j0; j < j1; ++j) mg = fmaxf(mg, a.part_m[(size_t)j * a.T + t]);
+  for (int j = j0; j < j1; j += MERGE_UNROLL) {
+    float v[MERGE_UNROLL];
+#pragma unroll
+    for (int u = 0; u < MERGE_UNROLL; ++u)
+      v[u] = (valid && j + u < j1) ? pm[(size_t)(j + u) * T] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < MERGE_UNROLL; ++u) mg = fmaxf(mg, v[u]);
+  }
   red[g][lane] = mg;
   __syncthreads();
   float M = red[0][lane];
@@ -373,18 +425,25 @@ __global__ __launch_bounds__(MERGE_GROUPS * MERGE_ROWS) void merge_kernel(
   const float Ms = (M == -INFINITY) ? 0.0f : M;
 
   float sg = 0.0f;
-  if (valid)
-    for (int j = j0; j < j1; ++j) {
-      const size_t o = (size_t)j * a.T + t;
-      sg = sg + a.part_s[o] * __builtin_amdgcn_exp2f((a.part_m[o] - Ms) * LOG2E);
+  for (int j = j0; j < j1; j += MERGE_UNROLL) {
+    float vm[MERGE_UNROLL], vs[MERGE_UNROLL];
+#pragma unroll
+    for (int u = 0; u < MERGE_UNROLL; ++u) {
+      const bool in = valid && j + u < j1;
+      vm[u] = in ? pm[(size_t)(j + u) * T] : -INFINITY;
+      vs[u] = in ? ps[(size_t)(j + u) * T] : 0.0f;
     }
+#pragma unroll
+    for (int u = 0; u < MERGE_UNROLL; ++u)
+      sg = sg + vs[u] * __builtin_amdgcn_exp2f((vm[u] - Ms) * LOG2E);
+  }
   red[g][lane] = sg;
   __syncthreads();
   if (g == 0 && valid) {
-    float s = red[0][lane];
+    float sum = red[0][lane];
 #pragma unroll
-    for (int q = 1; q < MERGE_GROUPS; ++q) s = s + red[q][lane];
-    const float lse = M + __builtin_amdgcn_logf(s) * LN2;
+    for (int q = 1; q < MERGE_GROUPS; ++q) sum = sum + red[q][lane];
+    const float lse = M + __builtin_amdgcn_logf(sum) * LN2;
     const int y = a.targets[t];
     a.lse[t] = lse;
     a.logp[t] = (y >= 0 && y < a.V) ? a.xt[t] - lse : __builtin_nanf("");
@@ -410,8 +469,11 @@ __global__ __launch_bounds__(COMPARE_THREADS) void compare_kernel(
       sq = sq + d * d;
     }
     if (isfinite(a) && isfinite(b)) {
-      const double lr = (double)a - (double)b;
-      k3 = k3 + ((exp(lr) - 1.0) - lr);
+      // equal bits give lr = 0 and k3 = exp(0) - 1 - 0 = 0 exactly
+      if (__float_as_uint(a) != __float_as_uint(b)) {
+        const double lr = (double)a - (double)b;
+        k3 = k3 + ((exp(lr) - 1.0) - lr);
+      }
       ++kcnt;
     }
   }
