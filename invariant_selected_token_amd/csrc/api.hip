@@ -65,6 +65,17 @@ rlk::GemmArgs gemm_args(const void *hidden, int64_t ldh, const void *weight,
   return g;
 }
 
+// Compute units of the current device (the persistent kernel's workgroup
+// count).  Falls back to 256 (MI355X) if the query fails.
+int compute_units() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return 256;
+  return cus;
+}
+
 int hip_status(hipError_t e) {
   if (e == hipSuccess) return RLK_OK;
   g_last_hip_error = e;
@@ -123,7 +134,7 @@ int rlk_vocab_stats(const void *hidden, int64_t ld_hidden, const void *weight,
   g.part_m = reinterpret_cast<float *>(ws);
   g.part_s = reinterpret_cast<float *>(ws + stats_bytes(T, V));
   g.xt = reinterpret_cast<float *>(ws + 2 * stats_bytes(T, V));
-  return hip_status(rlk::launch_gemm_stats(g, static_cast<hipStream_t>(stream)));
+  return hip_status(rlk::launch_gemm_stats(g, compute_units(), static_cast<hipStream_t>(stream)));
 }
 
 int rlk_vocab_merge(const int32_t *targets, float *logp, float *lse, int64_t T,

@@ -57,7 +57,9 @@ struct MergeArgs {
 
 inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-hipError_t launch_gemm_stats(const GemmArgs &a, hipStream_t s);
+// `workers`: workgroups of the persistent statistics kernel (the device's
+// compute-unit count); it changes the schedule, never the results.
+hipError_t launch_gemm_stats(const GemmArgs &a, int workers, hipStream_t s);
 hipError_t launch_gemm_logits(const GemmArgs &a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t s);
 hipError_t launch_compare(const float *a, const float *b, int n,

@@ -93,24 +93,38 @@ __device__ __forceinline__ void tile_of_block(int b, int nMT, int nVT, int &m,
 // 8 or 16 lanes per cycle.
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-// One workgroup tile.  MASK is true only for the workgroup column that holds
-// the end of the vocabulary when V is not a multiple of TILE_V; it depends on
-// V alone, never on T or on where a row sits.
-template <bool STATS, bool MASK>
-__device__ __forceinline__ void gemm_tile(const GemmArgs &a, char *smem, int m,
-                                          int n) {
-  const int v0 = n * TILE_V;
-  const int t0 = m * TILE_T;
-  const int vrows = min(TILE_V, a.V - v0);
-  const int trows = min(TILE_T, a.T - t0);
-
+// The logit GEMM with its epilogue, for a sequence of workgroup tiles of 256
+// vocabulary x 256 token rows.  4 waves; wave w covers vocabulary half
+// wv = w & 1 and token half wt = w >> 1 as 4 x 4 MFMA blocks of 32 x 32.
+//
+// PERSIST: the workgroup walks tiles L = blockIdx.x, + gridDim.x, ... and
+// issues the next tile's first K-block loads before the current tile's
+// epilogue, so that their latency hides under the epilogue.  The order of
+// tiles only changes the schedule; every tile's arithmetic is the same.
+// MASK: the workgroup column that holds the end of the vocabulary when V is
+// not a multiple of TILE_V (its own launch); it depends on V alone, never on
+// T or on where a row sits.
+template <bool STATS, bool MASK, bool PERSIST>
+__device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
   const int wv = wave & 1;   // vocabulary half of the tile
   const int wt = wave >> 1;  // token half of the tile
   const int fr = lane & 31;  // MFMA row / column within a 32-block
   const int fk = lane >> 5;  // which 8-wide K slice of a 16-wide MFMA step
+
+  const int total = MASK ? a.nMT : a.nMT * a.nVTm;
+  int L = blockIdx.x;
+  if (L >= total) return;
+  auto coords = [&](int l, int &m, int &n) {
+    if (MASK) {
+      m = l;
+      n = a.nVT - 1;
+    } else {
+      tile_of_block(l, a.nMT, a.nVTm, m, n);
+    }
+  };
 
   // Global -> LDS: direct-to-LDS buffer loads (each lane's 16 bytes land in
   // LDS slot base + 16 * lane).  Load i of wave w fills the 1 KiB block
@@ -118,11 +132,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, char *smem, int m,
   // 8 b + (l >> 3) and, because of the swizzle, global chunk
   // (l & 7) ^ swz(row) = (l & 7) ^ (l >> 3) ^ (w & 1) of that row.  The K
   // offset of the block rides in the scalar offset; rows past T or V fall
-  // outside the resource and read 0.
-  const __amdgpu_buffer_rsrc_t rw =
-      make_rsrc(a.weight + (size_t)v0 * a.ldw, (uint32_t)(vrows * a.ldw * 2));
-  const __amdgpu_buffer_rsrc_t rh =
-      make_rsrc(a.hidden + (size_t)t0 * a.ldh, (uint32_t)(trows * a.ldh * 2));
+  // outside the tile's resource and read 0.
+  auto rsrc_w = [&](int n) {
+    const int v0 = n * TILE_V;
+    return make_rsrc(a.weight + (size_t)v0 * a.ldw,
+                     (uint32_t)(min(TILE_V, a.V - v0) * a.ldw * 2));
+  };
+  auto rsrc_h = [&](int m) {
+    const int t0 = m * TILE_T;
+    return make_rsrc(a.hidden + (size_t)t0 * a.ldh,
+                     (uint32_t)(min(TILE_T, a.T - t0) * a.ldh * 2));
+  };
   const int lrow = 8 * (tid >> 6) + (lane >> 3);
   const int lchunk = (lane & 7) ^ (lane >> 3) ^ ((tid >> 6) & 1);
   uint32_t gofs[2][8];  // [operand][load]
@@ -140,28 +160,30 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, char *smem, int m,
     __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? r_h : r_w, (lds_void *)dst, 16, gofs[op][i],
                                              (uint32_t)kb * (TILE_K * 2), 0, 0);
   };
-
   // L2 prefetch of K block kb: one 4-byte load per 128-byte line, lane l
   // touching row 32 (l >> 3) + 8 w + (l & 7) -- the 64 rows this wave's own
   // loads of that block will cover.  The data lands in a scratch slot of LDS
   // that nothing reads; the point is that the line is in L2 when the real
   // load comes PREFETCH_AHEAD blocks later.  Past the end of a row or of the
   // resource the load stays in bounds or reads nothing.
-  const uint32_t pofs_w = (uint32_t)((32 * (lane >> 3) + 8 * (tid >> 6) + (lane & 7)) * a.ldw * 2);
-  const uint32_t pofs_h = (uint32_t)((32 * (lane >> 3) + 8 * (tid >> 6) + (lane & 7)) * a.ldh * 2);
-  auto prefetch = [&](int op, int kb) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? rh : rw, (lds_void *)(smem + 4 * STAGE_BYTES),
-                                             4, op ? pofs_h : pofs_w,
+  const int prow = 32 * (lane >> 3) + 8 * (tid >> 6) + (lane & 7);
+  const uint32_t pofs_w = (uint32_t)(prow * a.ldw * 2);
+  const uint32_t pofs_h = (uint32_t)(prow * a.ldh * 2);
+  auto prefetch = [&](__amdgpu_buffer_rsrc_t r, int op, int kb) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(smem + 4 * STAGE_BYTES), 4,
+                                             op ? pofs_h : pofs_w,
                                              (uint32_t)kb * (TILE_K * 2), 0, 0);
   };
-
-  f32x16 acc[4][4];
+  // A tile's first K block into stage 0, and its next blocks into L2.
+  auto issue_first = [&](__amdgpu_buffer_rsrc_t r_w, __amdgpu_buffer_rsrc_t r_h) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int q = 0; q < 16; ++q) gload(r_w, r_h, 0, 0, q);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    for (int kp = 1; kp <= PREFETCH_AHEAD; ++kp) {
+      prefetch(r_w, 0, kp);
+      prefetch(r_h, 1, kp);
+    }
+  };
 
   // Fragment reads: A (weight) rows wv*128 + 32 i + fr, B (hidden) rows
   // wt*128 + 32 j + fr, 16-byte chunk 2 ks + fk of the 64-wide K step.  Byte
@@ -171,7 +193,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, char *smem, int m,
   for (int st = 0; st < 2; ++st)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const uint32_t x = (uint32_t)(((2 * ks + fk) ^ swz(fr)) << 4);  // swz(32 i + fr) == swz(fr)
+      // swz(32 i + fr) == swz(fr)
+      const uint32_t x = (uint32_t)(((2 * ks + fk) ^ swz(fr)) << 4);
       ra[st][ks] = st * (2 * STAGE_BYTES) + (wv * 128 + fr) * 128 + x;
       rb[st][ks] = st * (2 * STAGE_BYTES) + STAGE_BYTES + (wt * 128 + fr) * 128 + x;
     }
@@ -183,22 +206,25 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, char *smem, int m,
     else if (w <= 4) fb[buf][w - 1] = *(const bf16x8 *)(smem + rb[st][ks] + (w - 1) * 4096);
     else fa[buf][w - 4] = *(const bf16x8 *)(smem + ra[st][ks] + (w - 4) * 4096);
   };
+  f32x16 acc[4][4];
   auto mfma = [&](int buf, int q) {
     const int i = q >> 2, j = q & 3;
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j],
                                                        0, 0, 0);
   };
 
-  // The main loop.  Each accumulator advances in increasing k (16 per MFMA);
-  // the fixed instruction order below only decides what overlaps with what:
-  // every MFMA of K step ks is followed by one read of step ks + 1's
-  // fragments (first half) or one direct-to-LDS load of the next K block
-  // (second half, steps 0 and 1).  Half-way through step 3 the wave waits
-  // for its loads and the workgroup meets at the barrier (the next block has
-  // landed; this block is no longer read), then the next block's first
-  // fragments are read under the last eight MFMAs.
+  // One K block of the main loop.  Each accumulator advances in increasing k
+  // (16 per MFMA); the fixed instruction order below only decides what
+  // overlaps with what: every MFMA of K step ks is followed by one read of
+  // step ks + 1's fragments (first half) or one direct-to-LDS load of the
+  // next K block (second half, steps 0 and 1; step 2: the L2 prefetches).
+  // Half-way through step 3 the wave waits for its loads and the workgroup
+  // meets at the barrier (the next block has landed; this block is no longer
+  // read), then the next block's first fragments are read under the last
+  // eight MFMAs.
   auto k_block = [&](int kb, auto stage, auto more, __amdgpu_buffer_rsrc_t r_w,
-                     __amdgpu_buffer_rsrc_t r_h) {
+                     __amdgpu_buffer_rsrc_t r_h, __amdgpu_buffer_rsrc_t p_w,
+                     __amdgpu_buffer_rsrc_t p_h) {
     constexpr int st = decltype(stage)::value;    // == kb & 1
     constexpr bool MORE = decltype(more)::value;  // not the last K block
 #pragma unroll
@@ -209,7 +235,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, char *smem, int m,
         mfma(cur, q);
         if (q < 8) fread(cur ^ 1, st, ks + 1, q);
         else if (MORE && ks < 2) gload(r_w, r_h, st ^ 1, kb + 1, 8 * ks + (q - 8));
-        else if (MORE && ks == 2 && q < 10) prefetch(q - 8, kb + 1 + PREFETCH_AHEAD);
+        else if (MORE && ks == 2 && q < 10)
+          prefetch(q == 8 ? p_w : p_h, q - 8, kb + 1 + PREFETCH_AHEAD);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -245,145 +272,161 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, char *smem, int m,
   const int nk = a.H / TILE_K;
   const int nk2 = nk + (nk & 1);
   const __amdgpu_buffer_rsrc_t zero = make_rsrc(a.weight, 0u);
-  const __amdgpu_buffer_rsrc_t rw_last = (nk & 1) ? zero : rw;
-  const __amdgpu_buffer_rsrc_t rh_last = (nk & 1) ? zero : rh;
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-#pragma unroll
-  for (int q = 0; q < 16; ++q) gload(rw, rh, 0, 0, q);
-#pragma unroll
-  for (int kp = 1; kp <= PREFETCH_AHEAD; ++kp) {
-    prefetch(0, kp);
-    prefetch(1, kp);
-  }
-  __builtin_amdgcn_s_waitcnt(VMCNT0);
-  __syncthreads();
-#pragma unroll
-  for (int w = 0; w < 8; ++w) fread(0, 0, 0, w);
-  for (int kb = 0; kb + 2 < nk2; kb += 2) {
-    k_block(kb, S0{}, std::true_type{}, rw, rh);
-    k_block(kb + 1, S1{}, std::true_type{}, rw, rh);
-  }
-  k_block(nk2 - 2, S0{}, std::true_type{}, rw_last, rh_last);
-  k_block(nk2 - 1, S1{}, std::false_type{}, rw, rh);
 
-  // acc[i][j][r] holds z[t][v] for
-  //   v = v0 + wv*128 + 32 i + 8 (r >> 2) + 4 fk + (r & 3)
-  //   t = t0 + wt*128 + 32 j + fr
-  const int vbase = v0 + wv * 128;
-  if (!STATS) {
+  int m, n;
+  coords(L, m, n);
+  __amdgpu_buffer_rsrc_t rw = rsrc_w(n), rh = rsrc_h(m);
+  issue_first(rw, rh);
+
+  for (;;) {
+    const __amdgpu_buffer_rsrc_t rw_last = (nk & 1) ? zero : rw;
+    const __amdgpu_buffer_rsrc_t rh_last = (nk & 1) ? zero : rh;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = t0 + wt * 128 + 32 * j + fr;
-      if (t >= a.T) continue;
-      float *row = a.logits + (size_t)t * a.V;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int v = vbase + 32 * i + 8 * (r >> 2) + 4 * fk + (r & 3);
-          if (v < a.V) row[v] = acc[i][j][r];
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    // The tile's first block (issued before the previous epilogue, or above).
+    __builtin_amdgcn_s_waitcnt(VMCNT0);
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < 8; ++w) fread(0, 0, 0, w);
+    for (int kb = 0; kb + 2 < nk2; kb += 2) {
+      k_block(kb, S0{}, std::true_type{}, rw, rh, rw, rh);
+      k_block(kb + 1, S1{}, std::true_type{}, rw, rh, rw, rh);
+    }
+    k_block(nk2 - 2, S0{}, std::true_type{}, rw_last, rh_last, rw, rh);
+    k_block(nk2 - 1, S1{}, std::false_type{}, rw, rh, rw, rh);
+
+    // Stage 0 was last read before the barrier of block nk2 - 2, so the
+    // next tile's first block can go there now, under this epilogue.
+    const int Ln = PERSIST ? L + (int)gridDim.x : total;
+    int mn = 0, nn = 0;
+    __amdgpu_buffer_rsrc_t rwn = rw, rhn = rh;
+    if (Ln < total) {
+      coords(Ln, mn, nn);
+      rwn = rsrc_w(nn);
+      rhn = rsrc_h(mn);
+      issue_first(rwn, rhn);
+    }
+
+    // acc[i][j][r] holds z[t][v] for
+    //   v = v0 + wv*128 + 32 i + 8 (r >> 2) + 4 fk + (r & 3)
+    //   t = t0 + wt*128 + 32 j + fr
+    const int v0 = n * TILE_V;
+    const int t0 = m * TILE_T;
+    const int vbase = v0 + wv * 128;
+    if (!STATS) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = t0 + wt * 128 + 32 * j + fr;
+        if (t >= a.T) continue;
+        float *row = a.logits + (size_t)t * a.V;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int v = vbase + 32 * i + 8 * (r >> 2) + 4 * fk + (r & 3);
+            if (v < a.V) row[v] = acc[i][j][r];
+          }
+      }
+    } else {
+      // Statistics tiles are 128 vocabulary rows wide: wave (wv, wt) owns
+      // tile js = 2 n + wv for its 128 token rows, so no data crosses waves.
+      // A wave whose tile starts at or past V (only in the last workgroup
+      // column when V mod 256 <= 128) has nothing to write.
+      const int js = 2 * n + wv;
+      if (js < a.nST) {
+        // Columns past the vocabulary end count as -inf: they add nothing to
+        // the max and exactly 0 to the sum.  On valid columns the masked and
+        // unmasked instantiations compute the same thing.
+        const int lim = a.V - vbase - 4 * fk;  // columns at offset < lim are valid
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int t = t0 + wt * 128 + 32 * j + fr;
+          // 1) tile max: this lane's 64 values in (i, r) order, then the
+          //    partner lane (fk flipped) holding the other 64 of the tile.
+          float mx = -INFINITY;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const bool out = MASK && (32 * i + 8 * (r >> 2) + (r & 3) >= lim);
+              mx = fmaxf(mx, out ? -INFINITY : acc[i][j][r]);
+            }
+          const float mo = __shfl_xor(mx, 32);
+          const float m2 = fk == 0 ? fmaxf(mx, mo) : fmaxf(mo, mx);
+          // 2) sum of exp(z - m), same tree; m is taken as 0 when the whole
+          //    tile is -inf so that such a tile adds exactly 0.  z == m gives
+          //    exp(0) = 1 exactly, so the sum is >= 1 when the max is finite.
+          const float ms = (m2 == -INFINITY) ? 0.0f : m2;
+          float sx = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const bool out = MASK && (32 * i + 8 * (r >> 2) + (r & 3) >= lim);
+              const float z = out ? -INFINITY : acc[i][j][r];
+              sx = sx + __builtin_amdgcn_exp2f((z - ms) * LOG2E);
+            }
+          const float so = __shfl_xor(sx, 32);
+          const float s2 = fk == 0 ? sx + so : so + sx;
+          // 3) tile-major [nST][T] statistics (coalesced over rows).
+          if (t < a.T) {
+            const size_t o = (size_t)js * a.T + t;
+            if (fk == 0) a.part_m[o] = m2;
+            else a.part_s[o] = s2;
+          }
+          // 4) target capture: the one lane holding z[t][y[t]] writes xt[t],
+          //    the value picked by a fixed select tree over its 64 values.
+          const int y = (t < a.T) ? a.targets[t] : -1;
+          const int rel = y - vbase;
+          const bool hit = rel >= 0 && rel < STAT_V && ((rel >> 2) & 1) == fk;
+          if (__any(hit)) {
+            // block i = rel >> 5, register r = ((w >> 3) << 2) | (w & 3),
+            // w = rel & 31
+            const int bi = (rel >> 5) & 3;
+            const int w = rel & 31;
+            const int ri = ((w >> 3) << 2) | (w & 3);
+            float sel[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float lo = (bi & 1) ? acc[1][j][r] : acc[0][j][r];
+              const float hi = (bi & 1) ? acc[3][j][r] : acc[2][j][r];
+              sel[r] = (bi & 2) ? hi : lo;
+            }
+#pragma unroll
+            for (int lvl = 0; lvl < 4; ++lvl) {
+              const bool bit = (ri >> lvl) & 1;
+#pragma unroll
+              for (int q = 0; q < (8 >> lvl); ++q)
+                sel[q] = bit ? sel[2 * q + 1] : sel[2 * q];
+            }
+            if (hit) a.xt[t] = sel[0];
+          }
         }
+      }
     }
-    return;
-  }
 
-  // Statistics tiles are 128 vocabulary rows wide: wave (wv, wt) owns tile
-  // js = 2 n + wv for its 128 token rows, so no data crosses waves.  A wave
-  // whose tile starts at or past V (only in the last workgroup column when
-  // V mod 256 <= 128) has nothing to write.
-  const int js = 2 * n + wv;
-  if (js >= a.nST) return;
-
-  // Columns past the vocabulary end count as -inf: they add nothing to the
-  // max and exactly 0 to the sum.  On valid columns the masked and unmasked
-  // instantiations compute the same thing.
-  const int lim = a.V - vbase - 4 * fk;  // columns at offset < lim are valid
-  float mt[4], st[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    // 1) tile max: this lane's 64 values in (i, r) order, then the partner
-    //    lane (fk flipped) holding the other 64 values of the tile.
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const bool out = MASK && (32 * i + 8 * (r >> 2) + (r & 3) >= lim);
-        mx = fmaxf(mx, out ? -INFINITY : acc[i][j][r]);
-      }
-    const float mo = __shfl_xor(mx, 32);
-    const float m2 = fk == 0 ? fmaxf(mx, mo) : fmaxf(mo, mx);
-    // 2) sum of exp(z - m), same tree; m is taken as 0 when the whole tile is
-    //    -inf so that such a tile adds exactly 0.  z == m gives exp(0) = 1
-    //    exactly, so the sum is >= 1 when the max is finite.
-    const float ms = (m2 == -INFINITY) ? 0.0f : m2;
-    float sx = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const bool out = MASK && (32 * i + 8 * (r >> 2) + (r & 3) >= lim);
-        const float z = out ? -INFINITY : acc[i][j][r];
-        sx = sx + __builtin_amdgcn_exp2f((z - ms) * LOG2E);
-      }
-    const float so = __shfl_xor(sx, 32);
-    mt[j] = m2;
-    st[j] = fk == 0 ? sx + so : so + sx;
-  }
-
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int t = t0 + wt * 128 + 32 * j + fr;
-    // 3) tile-major [nST][T] statistics (coalesced over rows).
-    if (t < a.T) {
-      const size_t o = (size_t)js * a.T + t;
-      if (fk == 0) a.part_m[o] = mt[j];
-      else a.part_s[o] = st[j];
-    }
-    // 4) target capture: the one lane holding z[t][y[t]] writes xt[t], the
-    //    value picked by a fixed select tree over the lane's 64 values.
-    const int y = (t < a.T) ? a.targets[t] : -1;
-    const int rel = y - vbase;
-    const bool hit = rel >= 0 && rel < STAT_V && ((rel >> 2) & 1) == fk;
-    if (__any(hit)) {
-      // block i = rel >> 5, register r = ((w >> 3) << 2) | (w & 3), w = rel & 31
-      const int bi = (rel >> 5) & 3;
-      const int w = rel & 31;
-      const int ri = ((w >> 3) << 2) | (w & 3);
-      float sel[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float lo = (bi & 1) ? acc[1][j][r] : acc[0][j][r];
-        const float hi = (bi & 1) ? acc[3][j][r] : acc[2][j][r];
-        sel[r] = (bi & 2) ? hi : lo;
-      }
-#pragma unroll
-      for (int lvl = 0; lvl < 4; ++lvl) {
-        const bool bit = (ri >> lvl) & 1;
-#pragma unroll
-        for (int q = 0; q < (8 >> lvl); ++q)
-          sel[q] = bit ? sel[2 * q + 1] : sel[2 * q];
-      }
-      if (hit) a.xt[t] = sel[0];
-    }
+    if (Ln >= total) break;
+    L = Ln;
+    m = mn;
+    n = nn;
+    rw = rwn;
+    rh = rhn;
   }
 }
 
-// The masked instantiation runs as its own launch over the last workgroup
-// column only (when V is not a multiple of TILE_V), so each kernel holds one
-// copy of the tile code.  Which column a tile is in depends on V alone.
-template <bool STATS, bool MASK>
+// Launch shapes: the unmasked statistics kernel is persistent (one workgroup
+// per compute unit walking the tiles), the masked vocabulary-tail column and
+// the logits-stage kernel use one workgroup per tile.
+template <bool STATS, bool MASK, bool PERSIST>
 __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[4 * STAGE_BYTES + PREFETCH_SINK];
-  int m, n;
-  if (MASK) {
-    m = blockIdx.x;
-    n = a.nVT - 1;
-  } else {
-    tile_of_block(blockIdx.x, a.nMT, a.nVTm, m, n);
-  }
-  gemm_tile<STATS, MASK>(a, smem, m, n);
+  gemm_body<STATS, MASK, PERSIST>(a, smem);
 }
 
 // Per row t: M = max_j m_j (exact in any order), then
@@ -507,25 +550,29 @@ __global__ __launch_bounds__(COMPARE_THREADS) void compare_kernel(
   }
 }
 
-hipError_t launch_gemm_stats(const GemmArgs &a, hipStream_t s) {
+hipError_t launch_gemm_stats(const GemmArgs &a, int workers, hipStream_t s) {
   GemmArgs g = a;
   g.nVTm = a.V / TILE_V;  // columns that need no vocabulary mask
   if (g.nVTm > 0) {
-    hipLaunchKernelGGL((gemm_kernel<true, false>), dim3(g.nMT * g.nVTm),
-                       dim3(GEMM_THREADS), 0, s, g);
+    const int tiles = g.nMT * g.nVTm;
+    // A multiple of 8 workgroups keeps each one on a fixed XCD.
+    int grid = workers >= 8 ? workers - workers % 8 : 8;
+    if (grid > tiles) grid = tiles;
+    hipLaunchKernelGGL((gemm_kernel<true, false, true>), dim3(grid), dim3(GEMM_THREADS), 0,
+                       s, g);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (g.nVTm < g.nVT)
-    hipLaunchKernelGGL((gemm_kernel<true, true>), dim3(g.nMT), dim3(GEMM_THREADS), 0,
-                       s, g);
+    hipLaunchKernelGGL((gemm_kernel<true, true, false>), dim3(g.nMT), dim3(GEMM_THREADS),
+                       0, s, g);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_logits(const GemmArgs &a, hipStream_t s) {
   GemmArgs g = a;
   g.nVTm = a.nVT;  // stores are guarded per element; no mask variant needed
-  hipLaunchKernelGGL((gemm_kernel<false, false>), dim3(g.nMT * g.nVTm),
+  hipLaunchKernelGGL((gemm_kernel<false, false, false>), dim3(g.nMT * g.nVTm),
                      dim3(GEMM_THREADS), 0, s, g);
   return hipGetLastError();
 }
