@@ -39,7 +39,6 @@ struct GemmArgs {
   int V;
   int nMT;   // token tiles, ceil(T / TILE_T)
   int nVT;   // workgroup vocabulary tiles, ceil(V / TILE_V)
-  int nVTm;  // columns covered by the unmasked launch (set by the launcher)
   int nST;   // statistics tiles, ceil(V / STAT_V)
 };
 

@@ -1,7 +1,7 @@
 // kernels.hip -- gfx950 kernels of the batch-invariant selected-token
 // log-probability path.
 //
-//   gemm_kernel<true,*> logits z = W . h^T on bf16 MFMA with fp32 accumulation
+//   gemm_kernel<true,.> logits z = W . h^T on bf16 MFMA with fp32 accumulation
 //                       (RL-Kernel blog, section 二: the K split of a GEMM is a
 //                       source of drift; sections 六/七: one workgroup per
 //                       output tile, full K in a fixed order, no split-K),
@@ -101,10 +101,7 @@ __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1
 // issues the next tile's first K-block loads before the current tile's
 // epilogue, so that their latency hides under the epilogue.  The order of
 // tiles only changes the schedule; every tile's arithmetic is the same.
-// MASK: the workgroup column that holds the end of the vocabulary when V is
-// not a multiple of TILE_V (its own launch); it depends on V alone, never on
-// T or on where a row sits.
-template <bool STATS, bool MASK, bool PERSIST>
+template <bool STATS, bool PERSIST>
 __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -114,17 +111,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   const int fr = lane & 31;  // MFMA row / column within a 32-block
   const int fk = lane >> 5;  // which 8-wide K slice of a 16-wide MFMA step
 
-  const int total = MASK ? a.nMT : a.nMT * a.nVTm;
+  const int total = a.nMT * a.nVT;
   int L = blockIdx.x;
   if (L >= total) return;
-  auto coords = [&](int l, int &m, int &n) {
-    if (MASK) {
-      m = l;
-      n = a.nVT - 1;
-    } else {
-      tile_of_block(l, a.nMT, a.nVTm, m, n);
-    }
-  };
+  auto coords = [&](int l, int &m, int &n) { tile_of_block(l, a.nMT, a.nVT, m, n); };
 
   // Global -> LDS: direct-to-LDS buffer loads (each lane's 16 bytes land in
   // LDS slot base + 16 * lane).  Load i of wave w fills the 1 KiB block
@@ -339,7 +329,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
       // A wave whose tile starts at or past V (only in the last workgroup
       // column when V mod 256 <= 128) has nothing to write.
       const int js = 2 * n + wv;
-      if (js < a.nST) {
+      auto stats_epilogue = [&](auto masked) {
+        constexpr bool MASK = decltype(masked)::value;
         // Columns past the vocabulary end count as -inf: they add nothing to
         // the max and exactly 0 to the sum.  On valid columns the masked and
         // unmasked instantiations compute the same thing.
@@ -408,6 +399,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
             if (hit) a.xt[t] = sel[0];
           }
         }
+      };
+      // The vocabulary-tail column (V not a multiple of TILE_V) masks the
+      // columns past V; the choice depends on the tile's column, i.e. on V.
+      if (js < a.nST) {
+        if (n == a.nVT - 1 && a.V % TILE_V != 0) stats_epilogue(std::true_type{});
+        else stats_epilogue(std::false_type{});
       }
     }
 
@@ -420,13 +417,13 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   }
 }
 
-// Launch shapes: the unmasked statistics kernel is persistent (one workgroup
-// per compute unit walking the tiles), the masked vocabulary-tail column and
-// the logits-stage kernel use one workgroup per tile.
-template <bool STATS, bool MASK, bool PERSIST>
+// Launch shapes: the statistics kernel is persistent (one workgroup per
+// compute unit walking the tiles); the logits-stage kernel uses one
+// workgroup per tile.
+template <bool STATS, bool PERSIST>
 __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[4 * STAGE_BYTES + PREFETCH_SINK];
-  gemm_body<STATS, MASK, PERSIST>(a, smem);
+  gemm_body<STATS, PERSIST>(a, smem);
 }
 
 // Per row t: M = max_j m_j (exact in any order), then
@@ -551,29 +548,17 @@ __global__ __launch_bounds__(COMPARE_THREADS) void compare_kernel(
 }
 
 hipError_t launch_gemm_stats(const GemmArgs &a, int workers, hipStream_t s) {
-  GemmArgs g = a;
-  g.nVTm = a.V / TILE_V;  // columns that need no vocabulary mask
-  if (g.nVTm > 0) {
-    const int tiles = g.nMT * g.nVTm;
-    // A multiple of 8 workgroups keeps each one on a fixed XCD.
-    int grid = workers >= 8 ? workers - workers % 8 : 8;
-    if (grid > tiles) grid = tiles;
-    hipLaunchKernelGGL((gemm_kernel<true, false, true>), dim3(grid), dim3(GEMM_THREADS), 0,
-                       s, g);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (g.nVTm < g.nVT)
-    hipLaunchKernelGGL((gemm_kernel<true, true, false>), dim3(g.nMT), dim3(GEMM_THREADS),
-                       0, s, g);
+  const int tiles = a.nMT * a.nVT;
+  // A multiple of 8 workgroups keeps each one on a fixed XCD.
+  int grid = workers >= 8 ? workers - workers % 8 : 8;
+  if (grid > tiles) grid = tiles;
+  hipLaunchKernelGGL((gemm_kernel<true, true>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_logits(const GemmArgs &a, hipStream_t s) {
-  GemmArgs g = a;
-  g.nVTm = a.nVT;  // stores are guarded per element; no mask variant needed
-  hipLaunchKernelGGL((gemm_kernel<false, false, false>), dim3(g.nMT * g.nVTm),
-                     dim3(GEMM_THREADS), 0, s, g);
+  hipLaunchKernelGGL((gemm_kernel<false, false>), dim3(a.nMT * a.nVT), dim3(GEMM_THREADS),
+                     0, s, a);
   return hipGetLastError();
 }
 
