@@ -48,10 +48,14 @@ constexpr int RSRC_WORD3 = 0x00020000;
 // s_waitcnt immediates for "vmcnt(0)" / "vmcnt(2)" only (expcnt and lgkmcnt
 // left at their maxima).
 constexpr int VMCNT0 = 0x0F70;
-// "vmcnt(2) lgkmcnt(0)"
+// "vmcnt(2) lgkmcnt(0)" and "vmcnt(0) lgkmcnt(0)"
 constexpr int VMCNT2_LGKMCNT0 = 0x0072;
+constexpr int VMCNT0_LGKMCNT0 = 0x0070;
 // K blocks between an L2 prefetch and the block's direct-to-LDS load.
-constexpr int PREFETCH_AHEAD = 2;
+#ifndef RLK_PREFETCH_AHEAD
+#define RLK_PREFETCH_AHEAD 1
+#endif
+constexpr int PREFETCH_AHEAD = RLK_PREFETCH_AHEAD;
 // LDS bytes past the two stages that absorb the prefetch loads' data.
 constexpr int PREFETCH_SINK = 256;
 
@@ -225,7 +229,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
         mfma(cur, q);
         if (q < 8) fread(cur ^ 1, st, ks + 1, q);
         else if (MORE && ks < 2) gload(r_w, r_h, st ^ 1, kb + 1, 8 * ks + (q - 8));
-        else if (MORE && ks == 2 && q < 10)
+        else if (MORE && ks == 2 && q < 10 && PREFETCH_AHEAD > 0)
           prefetch(q == 8 ? p_w : p_h, q - 8, kb + 1 + PREFETCH_AHEAD);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -243,7 +247,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
       // not waited for; the empty asm statements keep the compiler from
       // moving memory accesses across it.
       asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_waitcnt(VMCNT2_LGKMCNT0);
+      __builtin_amdgcn_s_waitcnt(PREFETCH_AHEAD > 0 ? VMCNT2_LGKMCNT0 : VMCNT0_LGKMCNT0);
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
     }
