@@ -147,6 +147,31 @@ int rlk_vocab_merge(const int32_t *targets, float *logp, float *lse, int64_t T,
                     int64_t V, const void *workspace, size_t workspace_bytes,
                     void *stream);
 
+/* rlk_vocab_stats on one slice of the LM head: rows [v_begin, v_begin +
+ * v_count) of the full V-row weight, passed as `weight_shard` (its row 0 is
+ * global row v_begin).  The slice's statistics tiles are written at their
+ * global positions in a workspace sized for (T, V), and the target logit of
+ * every row whose (global) target falls in the slice.  Running the slices of
+ * any partition of [0, V) into one workspace and then calling rlk_vocab_merge
+ * once gives bitwise the result of the unsliced call, whatever the number of
+ * slices: each statistics tile is computed exactly as it is there, and the
+ * merge folds the tiles in the same fixed order.  This is the RL-Kernel blog's
+ * LogP rule under tensor parallelism (section 七: every shard computes local
+ * statistics, merged in a fixed vocabulary-tile order), made independent of
+ * the shard count.  Slices written on one stream, or on streams ordered before
+ * the merge, may share the workspace: their writes are disjoint.
+ *   v_begin  multiple of 256; v_count > 0; v_begin + v_count <= V; a slice
+ *            that does not end at V has v_count a multiple of 256
+ *            (RLK_ERR_INVALID_SHAPE / RLK_ERR_UNSUPPORTED otherwise).
+ *   targets  global ids (out of [0, V): no slice writes the row's target
+ *            logit and the merge gives NaN logp).
+ * Other arguments and errors as for rlk_vocab_stats. */
+int rlk_vocab_stats_shard(const void *hidden, int64_t ld_hidden,
+                          const void *weight_shard, int64_t ld_weight,
+                          const int32_t *targets, int64_t T, int64_t H, int64_t V,
+                          int64_t v_begin, int64_t v_count, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
 /* The logits stage alone, for stage-by-stage comparison (the RL-Kernel blog,
  * section 五: compare intermediate results to find the first divergence).
  * Runs the very same GEMM main loop as rlk_selected_logp and stores the fp32

@@ -29,8 +29,8 @@ RLK_ERR_HIP = 6
 EXPORTED = (
     "rlk_abi_version", "rlk_status_string", "rlk_last_hip_error",
     "rlk_vocab_tile", "rlk_selected_logp_workspace_bytes",
-    "rlk_selected_logp", "rlk_vocab_stats", "rlk_vocab_merge", "rlk_logits",
-    "rlk_compare",
+    "rlk_selected_logp", "rlk_vocab_stats", "rlk_vocab_stats_shard",
+    "rlk_vocab_merge", "rlk_logits", "rlk_compare",
 )
 
 _lib = None
@@ -54,6 +54,11 @@ def lib() -> ctypes.CDLL:
         raise RuntimeError(
             f"{LIB_PATH} is missing: build it with "
             "`python -m invariant_selected_token_amd.build`")
+    # torch's HIP runtime must be the process's only one: librlk.so asks for
+    # libamdhip64.so.7, which binds to torch's copy (same soname) when torch is
+    # loaded first; loaded the other way round, torch would map a second
+    # runtime next to the system one and the two would not share devices.
+    _torch()
     L = ctypes.CDLL(LIB_PATH)
     i64, sz, vp, c_int = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int
     L.rlk_abi_version.restype = c_int
@@ -68,6 +73,9 @@ def lib() -> ctypes.CDLL:
     L.rlk_selected_logp.restype = c_int
     L.rlk_vocab_stats.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, vp, sz, vp]
     L.rlk_vocab_stats.restype = c_int
+    L.rlk_vocab_stats_shard.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, i64, i64,
+                                        vp, sz, vp]
+    L.rlk_vocab_stats_shard.restype = c_int
     L.rlk_vocab_merge.argtypes = [vp, vp, vp, i64, i64, vp, sz, vp]
     L.rlk_vocab_merge.restype = c_int
     L.rlk_logits.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, vp]
@@ -205,6 +213,29 @@ def rlk_vocab_stats(hidden, weight, targets, workspace, V=None, stream=None):
         hp, ldh, wp, ldw, targets.data_ptr(), T, H, V, ws.data_ptr(), ws_bytes,
         _stream_ptr(stream, dev)))
     return ws
+
+
+def rlk_vocab_stats_shard(hidden, weight_shard, targets, workspace, V, v_begin,
+                          stream=None):
+    """Stage 1 on the weight rows [v_begin, v_begin + weight_shard.shape[0])
+    of a V-row LM head, into a workspace sized for (T, V)."""
+    torch = _torch()
+    dev = hidden.device
+    hp, ldh = _bf16_operand("hidden", hidden, dev)
+    wp, ldw = _bf16_operand("weight_shard", weight_shard, dev)
+    T, H = hidden.shape
+    if weight_shard.shape[1] != H:
+        raise ValueError("hidden and weight_shard disagree on H")
+    if targets.dtype != torch.int32 or targets.shape != (T,) or not targets.is_contiguous():
+        raise ValueError("targets must be a contiguous int32 [T] tensor")
+    _check_device("targets", targets, dev)
+    _check_device("workspace", workspace, dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _call("rlk_vocab_stats_shard", lib().rlk_vocab_stats_shard(
+        hp, ldh, wp, ldw, targets.data_ptr(), T, H, int(V), int(v_begin),
+        int(weight_shard.shape[0]), workspace.data_ptr(), ws_bytes,
+        _stream_ptr(stream, dev)))
+    return workspace
 
 
 def rlk_vocab_merge(targets, workspace, V, logp=None, lse=None, stream=None):

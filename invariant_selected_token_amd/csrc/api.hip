@@ -115,26 +115,42 @@ size_t rlk_selected_logp_workspace_bytes(int64_t T, int64_t V) {
   return 2 * stats_bytes(T, V) + round_up((size_t)T * sizeof(float));
 }
 
-int rlk_vocab_stats(const void *hidden, int64_t ld_hidden, const void *weight,
-                    int64_t ld_weight, const int32_t *targets, int64_t T,
-                    int64_t H, int64_t V, void *workspace,
-                    size_t workspace_bytes, void *stream) {
+int rlk_vocab_stats_shard(const void *hidden, int64_t ld_hidden,
+                          const void *weight_shard, int64_t ld_weight,
+                          const int32_t *targets, int64_t T, int64_t H, int64_t V,
+                          int64_t v_begin, int64_t v_count, void *workspace,
+                          size_t workspace_bytes, void *stream) {
   int st = check_shapes(T, H, V, ld_hidden, ld_weight);
   if (st != RLK_OK) return st;
+  if (v_begin < 0 || v_count <= 0 || v_begin > V - v_count) return RLK_ERR_INVALID_SHAPE;
+  // Slices start on a workgroup column and all but the last are whole columns,
+  // so every statistics tile is computed exactly as in the unsliced call.
+  if (v_begin % rlk::TILE_V != 0 || (v_begin + v_count != V && v_count % rlk::TILE_V != 0))
+    return RLK_ERR_UNSUPPORTED;
   if (T == 0) return RLK_OK;
-  st = check_operands(hidden, ld_hidden, weight, ld_weight);
+  st = check_operands(hidden, ld_hidden, weight_shard, ld_weight);
   if (st != RLK_OK) return st;
   if (!targets || !workspace) return RLK_ERR_NULL_POINTER;
   if (!aligned(targets, 4) || !aligned(workspace, 16)) return RLK_ERR_MISALIGNED;
   if (workspace_bytes < rlk_selected_logp_workspace_bytes(T, V))
     return RLK_ERR_WORKSPACE_TOO_SMALL;
   char *ws = static_cast<char *>(workspace);
-  rlk::GemmArgs g = gemm_args(hidden, ld_hidden, weight, ld_weight, T, H, V);
+  rlk::GemmArgs g = gemm_args(hidden, ld_hidden, weight_shard, ld_weight, T, H, v_count);
   g.targets = targets;
   g.part_m = reinterpret_cast<float *>(ws);
   g.part_s = reinterpret_cast<float *>(ws + stats_bytes(T, V));
   g.xt = reinterpret_cast<float *>(ws + 2 * stats_bytes(T, V));
+  g.js_base = (int)(v_begin / rlk::STAT_V);
+  g.y_base = (int)v_begin;
   return hip_status(rlk::launch_gemm_stats(g, compute_units(), static_cast<hipStream_t>(stream)));
+}
+
+int rlk_vocab_stats(const void *hidden, int64_t ld_hidden, const void *weight,
+                    int64_t ld_weight, const int32_t *targets, int64_t T,
+                    int64_t H, int64_t V, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+  return rlk_vocab_stats_shard(hidden, ld_hidden, weight, ld_weight, targets, T, H, V, 0, V,
+                               workspace, workspace_bytes, stream);
 }
 
 int rlk_vocab_merge(const int32_t *targets, float *logp, float *lse, int64_t T,

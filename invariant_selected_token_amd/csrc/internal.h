@@ -37,6 +37,8 @@ struct GemmArgs {
   int T;
   int H;
   int V;
+  int js_base;  // global index of this weight slice's first statistics tile
+  int y_base;   // global vocabulary index of this weight slice's first row
   int nMT;   // token tiles, ceil(T / TILE_T)
   int nVT;   // workgroup vocabulary tiles, ceil(V / TILE_V)
   int nST;   // statistics tiles, ceil(V / STAT_V)

@@ -329,7 +329,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
       }
     } else {
       // Statistics tiles are 128 vocabulary rows wide: wave (wv, wt) owns
-      // tile js = 2 n + wv for its 128 token rows, so no data crosses waves.
+      // tile js = 2 n + wv (of this weight slice; js_base + js globally) for
+      // its 128 token rows, so no data crosses waves.
       // A wave whose tile starts at or past V (only in the last workgroup
       // column when V mod 256 <= 128) has nothing to write.
       const int js = 2 * n + wv;
@@ -371,13 +372,14 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
           const float s2 = fk == 0 ? sx + so : so + sx;
           // 3) tile-major [nST][T] statistics (coalesced over rows).
           if (t < a.T) {
-            const size_t o = (size_t)js * a.T + t;
+            const size_t o = (size_t)(a.js_base + js) * a.T + t;
             if (fk == 0) a.part_m[o] = m2;
             else a.part_s[o] = s2;
           }
           // 4) target capture: the one lane holding z[t][y[t]] writes xt[t],
           //    the value picked by a fixed select tree over its 64 values.
-          const int y = (t < a.T) ? a.targets[t] : -1;
+          // (targets are global ids; a weight slice starts at y_base)
+          const int y = (t < a.T) ? a.targets[t] - a.y_base : -1;
           const int rel = y - vbase;
           const bool hit = rel >= 0 && rel < STAT_V && ((rel >> 2) & 1) == fk;
           if (__any(hit)) {

@@ -71,3 +71,9 @@ def prefill(dev):
 def adversarial(dev):
     from invariant_selected_token_amd import synth
     return DevCase(synth.adversarial_case(), dev)
+
+
+@pytest.fixture(scope="session")
+def rollout(dev):
+    from invariant_selected_token_amd import synth
+    return DevCase(synth.long_rollout_case(), dev)

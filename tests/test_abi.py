@@ -200,3 +200,59 @@ def _merge(targets=FAKE, logp=FAKE, lse=FAKE, T=4, V=1000, ws=WS_FAKE, ws_bytes=
 ])
 def test_vocab_merge_error_paths(kw, status):
     assert _merge(**kw) == status
+
+
+def _shard(hidden=FAKE, ldh=256, weight=FAKE, ldw=256, targets=FAKE, T=4, H=256,
+           V=1000, v_begin=256, v_count=256, ws=WS_FAKE, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = rlk.rlk_selected_logp_workspace_bytes(T, V)
+    return rlk.lib().rlk_vocab_stats_shard(hidden, ldh, weight, ldw, targets, T, H, V,
+                                           v_begin, v_count, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(v_begin=-256), rlk.RLK_ERR_INVALID_SHAPE),
+    (dict(v_count=0), rlk.RLK_ERR_INVALID_SHAPE),
+    (dict(v_count=-1), rlk.RLK_ERR_INVALID_SHAPE),
+    (dict(v_begin=768, v_count=256), rlk.RLK_ERR_INVALID_SHAPE),   # past V
+    (dict(v_begin=128), rlk.RLK_ERR_UNSUPPORTED),                  # not 256-aligned
+    (dict(v_count=200), rlk.RLK_ERR_UNSUPPORTED),                  # ragged, not last
+    (dict(H=100, ldh=104, ldw=104), rlk.RLK_ERR_UNSUPPORTED),
+    (dict(T=-1), rlk.RLK_ERR_INVALID_SHAPE),
+    (dict(targets=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(weight=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(ws=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(ws=WS_FAKE + 4), rlk.RLK_ERR_MISALIGNED),
+    (dict(T=1000, ws_bytes=("for", 1000, 512)), rlk.RLK_ERR_WORKSPACE_TOO_SMALL),  # slice-sized
+    (dict(T=0, hidden=None, weight=None, targets=None, ws=None, ws_bytes=0), rlk.RLK_OK),
+])
+def test_vocab_stats_shard_error_paths(kw, status):
+    kw = dict(kw)
+    if isinstance(kw.get("ws_bytes"), tuple):     # sized in the test, not at collection
+        _, t, v = kw["ws_bytes"]
+        kw["ws_bytes"] = rlk.rlk_selected_logp_workspace_bytes(t, v)
+        assert kw["ws_bytes"] < rlk.rlk_selected_logp_workspace_bytes(kw["T"], 1000)
+    assert _shard(**kw) == status
+    assert rlk.rlk_last_hip_error() == 0
+
+
+def test_vocab_stats_shard_accepts_the_ragged_last_slice():
+    # 768 + 232 = V: validation passes up to the operands (a null hidden).
+    assert _shard(hidden=None, v_begin=768, v_count=232) == rlk.RLK_ERR_NULL_POINTER
+    assert _shard(hidden=None, v_begin=0, v_count=1000) == rlk.RLK_ERR_NULL_POINTER
+
+
+def test_one_hip_runtime_in_the_process():
+    """The library binds to torch's HIP runtime instead of mapping a second one
+    (two runtimes in one process do not share devices).  Run in a fresh
+    interpreter that loads the library before anything imports torch."""
+    import subprocess
+    import sys
+    code = ("import invariant_selected_token_amd as r; r.lib(); "
+            "import re; maps = open('/proc/self/maps').read(); "
+            "print(sorted(set(re.findall(r'\\S*libamdhip64\\S*', maps))))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True,
+                         text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    paths = eval(out.stdout.strip().splitlines()[-1])
+    assert len(paths) == 1, paths

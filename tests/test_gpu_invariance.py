@@ -167,3 +167,76 @@ def test_two_stages_equal_one_call(prefill):
     a, b = rlk.rlk_vocab_merge(prefill.targets, ws, prefill.case.V)
     _assert_bits_equal(a, lp, "two-stage logp")
     _assert_bits_equal(b, lse, "two-stage lse")
+
+
+def test_rollout_packed_vs_per_response(rollout):
+    """T=16384 packed vs 32 per-response calls of 512 rows, bitwise."""
+    lp, lse = rlk.rlk_selected_logp(rollout.hidden, rollout.weight, rollout.targets)
+    parts_lp, parts_lse = [], []
+    for s in range(32):
+        sl = slice(512 * s, 512 * (s + 1))
+        a, b = rlk.rlk_selected_logp(rollout.hidden[sl], rollout.weight, rollout.targets[sl])
+        parts_lp.append(a)
+        parts_lse.append(b)
+    _assert_bits_equal(torch.cat(parts_lp), lp, "rollout packed vs per-response logp")
+    _assert_bits_equal(torch.cat(parts_lse), lse, "rollout packed vs per-response lse")
+
+
+def _slices(V, cuts):
+    """[v_begin, v_end) slices of [0, V) cut at the given 256-aligned rows."""
+    edges = [0] + sorted(set(cuts)) + [V]
+    return [(a, b) for a, b in zip(edges[:-1], edges[1:]) if b > a]
+
+
+def _tp_cuts(V, P):
+    cols = (V + 255) // 256
+    return [round(i * cols / P) * 256 for i in range(1, P)]
+
+
+@pytest.mark.parametrize("name", ["tp2", "tp4", "tp8", "uneven", "single_columns"])
+def test_vocab_slices_merge_to_the_unsliced_bits(prefill, name):
+    """Statistics computed per slice of the vocabulary (tensor-parallel LM-head
+    shards, RL-Kernel blog section 七) and merged once give the unsliced bits
+    for any slice count.  The workspace starts as NaN so that a tile or target
+    logit that no slice writes shows up as a mismatch."""
+    c = prefill.case
+    T, V = c.T, c.V
+    cuts = {"tp2": _tp_cuts(V, 2), "tp4": _tp_cuts(V, 4), "tp8": _tp_cuts(V, 8),
+            "uneven": [256, 512, 75776, 151552],
+            "single_columns": [256 * j for j in range(1, 12)] + [V - V % 256]}[name]
+    sl = _slices(V, cuts)
+    assert all(a % 256 == 0 for a, _ in sl) and sl[-1][1] == V
+    lp, lse = rlk.rlk_selected_logp(prefill.hidden, prefill.weight, prefill.targets)
+    ws = rlk.workspace_for(T, V, lp.device)
+    ws.view(torch.uint8).fill_(0xFF)          # all-ones bits: NaN in every float slot
+    for a, b in sl:
+        rlk.rlk_vocab_stats_shard(prefill.hidden, prefill.weight[a:b], prefill.targets,
+                                  ws, V, a)
+    s_lp, s_lse = rlk.rlk_vocab_merge(prefill.targets, ws, V)
+    _assert_bits_equal(s_lp, lp, f"{name} ({len(sl)} slices) logp")
+    _assert_bits_equal(s_lse, lse, f"{name} ({len(sl)} slices) lse")
+
+
+def test_vocab_slices_on_two_streams(tiny):
+    """Two slices launched on different streams, joined before the merge."""
+    c = tiny.case
+    T, V = c.T, c.V
+    lp, lse = rlk.rlk_selected_logp(tiny.hidden, tiny.weight, tiny.targets)
+    ws = rlk.workspace_for(T, V, lp.device)
+    ws.view(torch.uint8).fill_(0xFF)
+    cut = (V // 512) * 256
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    ready = torch.cuda.current_stream().record_event()
+    s1.wait_event(ready)
+    s2.wait_event(ready)
+    with torch.cuda.stream(s1):
+        rlk.rlk_vocab_stats_shard(tiny.hidden, tiny.weight[:cut], tiny.targets, ws, V, 0,
+                                  stream=s1)
+    with torch.cuda.stream(s2):
+        rlk.rlk_vocab_stats_shard(tiny.hidden, tiny.weight[cut:], tiny.targets, ws, V, cut,
+                                  stream=s2)
+    torch.cuda.current_stream().wait_stream(s1)
+    torch.cuda.current_stream().wait_stream(s2)
+    s_lp, s_lse = rlk.rlk_vocab_merge(tiny.targets, ws, V)
+    _assert_bits_equal(s_lp, lp, "two-stream slices logp")
+    _assert_bits_equal(s_lse, lse, "two-stream slices lse")

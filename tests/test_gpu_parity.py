@@ -246,3 +246,22 @@ def test_compare_kernel_matches_oracle_stats(dev):
     t = torch.from_numpy(b).to(dev)
     st0 = rlk.consistency_report(rlk.rlk_compare(t, t))
     assert st0["mismatch_count"] == 0 and st0["max_abs_diff"] == 0.0
+
+
+def test_long_rollout_softmax_targets(rollout, dev):
+    """T=16384 (32 responses x 512): sampled rows get targets drawn from the
+    oracle's own softmax (inverse CDF with one seeded uniform per row); the
+    other rows keep uniform targets, which cannot affect the sampled rows."""
+    c = rollout.case
+    rng = np.random.Generator(np.random.PCG64(77))
+    rows = np.unique(np.concatenate([[0, 255, 256, 511, 8191, 8192, 16383],
+                                     rng.choice(c.T, 25, replace=False)]))
+    ls = orc.log_softmax(c.hidden[rows], c.weight)
+    y = c.targets.copy()
+    y[rows] = orc.sample_targets(ls, c.meta["u"][rows])
+    lp, lse = _run(rollout.hidden, rollout.weight, to_dev_i32(y, dev))
+    ref_lp, ref_lse = orc.selected_logp(c.hidden[rows], c.weight, y[rows])
+    np.testing.assert_allclose(ref_lp, ls[np.arange(rows.size), y[rows]], rtol=0, atol=1e-12)
+    _assert_close(lp[rows], ref_lp, "rollout logp")
+    _assert_close(lse[rows], ref_lse, "rollout lse")
+    assert np.all(np.isfinite(lp)) and np.all(lp <= 0.0)
