@@ -42,8 +42,24 @@
  *     nothing to the sum; a row whose logits are all -Inf has lse = -Inf and
  *     logp = NaN.
  *   - A target outside [0, V) gives logp = NaN; lse is still produced.
- *   - No temperature, no soft-capping: the LSE covers exactly the V rows of w
- *     that are passed.
+ *   - The LSE covers exactly the V rows of w that are passed.
+ *
+ * Variants of the same quantity (oracle_selected_logp_ex), for the contract
+ * options of the product library:
+ *   - Temperature: every logit is multiplied by inv_tau = 1/tau before
+ *     anything else (sampling at temperature tau draws from softmax(z / tau);
+ *     training must score the same distribution).
+ *   - bfloat16 logits: engines that hold their logits as a bf16 tensor round
+ *     each (scaled) logit to bf16 before the softmax.  The RL-Kernel blog
+ *     (sections 二 and 四) names this fp32 -> bf16 conversion point as one of
+ *     the places where training and inference drift apart.  The rounding is
+ *     to nearest, ties to even, taken on the logit as an fp32 value (the
+ *     precision in which an engine holds it before the cast): fp64 logit ->
+ *     nearest fp32 -> nearest bf16.
+ *   - Entropy of softmax(z'): H = -sum_v p_v log p_v with
+ *     p_v = exp(z'_v - lse), terms with p_v = 0 contributing 0; NaN when the
+ *     row's lse is not finite.  (The vLLM blog summary lists entropy among the
+ *     per-token quantities an RL step reads from these logits.)
  */
 #include <math.h>
 #include <stdint.h>
@@ -53,7 +69,7 @@
 #include <omp.h>
 #endif
 
-#define ORACLE_VERSION 1
+#define ORACLE_VERSION 2
 
 int oracle_version(void) { return ORACLE_VERSION; }
 
@@ -132,6 +148,53 @@ static void row_lse_logp(const double *z, int64_t V, int64_t y,
     const double lse = m + log(s);
     *lse_out = lse;
     *logp_out = (y >= 0 && y < V) ? z[y] - lse : NAN;
+}
+
+/* fp64 -> bfloat16 value, round to nearest, ties to even, from the format's
+ * definition: 8 significant bits, exponent range of fp32 (normal numbers down
+ * to 2^-126, subnormals spaced 2^-133), largest finite (2 - 2^-7) 2^127;
+ * values at or beyond the rounding boundary above it become infinities. */
+static double round_bf16(double x) {
+    if (isnan(x) || isinf(x) || x == 0.0) return x;
+    int e;
+    (void)frexp(x, &e);                 /* |x| = f 2^e, f in [0.5, 1) */
+    int q = e - 8;                      /* spacing of 8-bit significands */
+    if (q < -133) q = -133;             /* subnormal spacing */
+    const double step = ldexp(1.0, q);
+    const double n = x / step;          /* exact: a power-of-two division */
+    double r = floor(n);
+    const double frac = n - r;          /* exact */
+    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+    const double y = r * step;
+    const double max_finite = ldexp(255.0, 120);   /* (2 - 2^-7) 2^127 */
+    if (fabs(y) > max_finite) return x > 0 ? INFINITY : -INFINITY;
+    return copysign(y, x);              /* a negative value rounded to 0 is -0 */
+}
+
+/* The logit as an engine holds it before a bf16 cast: nearest fp32. */
+static double to_f32(double x) { return (double)(float)x; }
+
+/* Apply the contract options to one row of fp64 logits, in place. */
+static void row_transform(double *z, int64_t V, double inv_tau, int bf16) {
+    for (int64_t v = 0; v < V; ++v) {
+        double x = z[v] * inv_tau;
+        if (bf16) x = round_bf16(to_f32(x));
+        z[v] = x;
+    }
+}
+
+/* Entropy of softmax(z) given its lse (finite), terms with p = 0 skipped. */
+static double row_entropy(const double *z, int64_t V, double lse) {
+    if (!isfinite(lse)) return NAN;
+    double h = 0.0;
+    for (int64_t v = 0; v < V; ++v) {
+        if (z[v] == -INFINITY) continue;
+        const double lp = z[v] - lse;
+        const double p = exp(lp);
+        if (p == 0.0) continue;
+        h = h - p * lp;
+    }
+    return h;
 }
 
 static void hidden_row(const uint16_t *hidden, int64_t ldh, int64_t t,
@@ -247,6 +310,59 @@ int oracle_log_softmax(const uint16_t *hidden, int64_t ldh,
             }
         }
         free(h);
+    }
+    return fail ? -1 : 0;
+}
+
+/* Round fp32 values to bfloat16 (test of the rounding on its own). */
+void oracle_round_bf16(const float *x, int64_t n, double *out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = round_bf16((double)x[i]);
+}
+
+/* lse / logp / entropy from logits given directly, after the options. */
+void oracle_ex_from_logits(const double *z_in, const int32_t *targets, int64_t T,
+                           int64_t V, double inv_tau, int bf16, double *logp,
+                           double *lse, double *entropy) {
+    double *z = (double *)malloc((size_t)(V > 0 ? V : 1) * sizeof(double));
+    if (!z) return;
+    for (int64_t t = 0; t < T; ++t) {
+        memcpy(z, z_in + t * V, (size_t)V * sizeof(double));
+        row_transform(z, V, inv_tau, bf16);
+        row_lse_logp(z, V, (int64_t)targets[t], &lse[t], &logp[t]);
+        if (entropy) entropy[t] = row_entropy(z, V, lse[t]);
+    }
+    free(z);
+}
+
+/* The whole path with the contract options: logits, z' = z * inv_tau,
+ * optionally rounded to bf16, then lse, logp and (if entropy is not NULL) the
+ * entropy of softmax(z').  Returns 0 or -1. */
+int oracle_selected_logp_ex(const uint16_t *hidden, int64_t ldh,
+                            const uint16_t *weight, int64_t ldw,
+                            const int32_t *targets, int64_t T, int64_t H,
+                            int64_t V, double inv_tau, int bf16, double *logp,
+                            double *lse, double *entropy, int nthreads) {
+    int fail = 0;
+    set_threads(nthreads);
+#pragma omp parallel
+    {
+        double *h = (double *)malloc((size_t)(H > 0 ? H : 1) * sizeof(double));
+        double *z = (double *)malloc((size_t)(V > 0 ? V : 1) * sizeof(double));
+        if (!h || !z) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t t = 0; t < T; ++t) {
+                hidden_row(hidden, ldh, t, H, h);
+                row_logits(h, weight, ldw, H, V, z);
+                row_transform(z, V, inv_tau, bf16);
+                row_lse_logp(z, V, (int64_t)targets[t], &lse[t], &logp[t]);
+                if (entropy) entropy[t] = row_entropy(z, V, lse[t]);
+            }
+        }
+        free(h);
+        free(z);
     }
     return fail ? -1 : 0;
 }

@@ -63,6 +63,14 @@ def _load():
     lib.oracle_log_softmax.argtypes = [vp, i64, vp, i64, i64, i64, i64, vp,
                                        c_int]
     lib.oracle_log_softmax.restype = c_int
+    lib.oracle_round_bf16.argtypes = [vp, i64, vp]
+    lib.oracle_round_bf16.restype = None
+    lib.oracle_ex_from_logits.argtypes = [vp, vp, i64, i64, ctypes.c_double, c_int,
+                                          vp, vp, vp]
+    lib.oracle_ex_from_logits.restype = None
+    lib.oracle_selected_logp_ex.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64,
+                                            ctypes.c_double, c_int, vp, vp, vp, c_int]
+    lib.oracle_selected_logp_ex.restype = c_int
     _lib = lib
     return lib
 
@@ -154,6 +162,53 @@ def log_softmax(hidden, weight, nthreads: int = 0) -> np.ndarray:
                               nthreads):
         raise MemoryError("oracle_log_softmax failed")
     return out
+
+
+def round_bf16(x) -> np.ndarray:
+    """fp32 values rounded to bfloat16 (to nearest, ties to even), as fp64."""
+    lib = _load()
+    a = np.ascontiguousarray(x, dtype=np.float32).ravel()
+    out = np.empty(a.size, dtype=np.float64)
+    lib.oracle_round_bf16(_ptr(a), a.size, _ptr(out))
+    return out.reshape(np.shape(x))
+
+
+def ex_from_logits(z, targets, inv_tau: float = 1.0, bf16: bool = False):
+    """(logp, lse, entropy) of fp64 logits [T, V] given directly, after the
+    contract options (z * inv_tau, then optionally fp32 -> bf16 rounding)."""
+    lib = _load()
+    z = np.ascontiguousarray(z, dtype=np.float64)
+    if z.ndim != 2:
+        raise ValueError("z must be 2-D")
+    T, V = z.shape
+    y = np.ascontiguousarray(targets, dtype=np.int32)
+    if y.shape != (T,):
+        raise ValueError("targets must have shape [T]")
+    logp, lse, ent = (np.empty(T, dtype=np.float64) for _ in range(3))
+    lib.oracle_ex_from_logits(_ptr(z), _ptr(y), T, V, float(inv_tau), int(bool(bf16)),
+                              _ptr(logp), _ptr(lse), _ptr(ent))
+    return logp, lse, ent
+
+
+def selected_logp_ex(hidden, weight, targets, inv_tau: float = 1.0, bf16: bool = False,
+                     nthreads: int = 0):
+    """(logp, lse, entropy) in fp64 with the contract options: every logit
+    multiplied by ``inv_tau`` and, with ``bf16``, rounded fp32 -> bf16."""
+    lib = _load()
+    h, w = _bf16_2d(hidden), _bf16_2d(weight)
+    T, H = h.shape
+    V = w.shape[0]
+    if w.shape[1] != H:
+        raise ValueError("hidden and weight disagree on H")
+    y = np.ascontiguousarray(targets, dtype=np.int32)
+    if y.shape != (T,):
+        raise ValueError("targets must have shape [T]")
+    logp, lse, ent = (np.empty(T, dtype=np.float64) for _ in range(3))
+    if lib.oracle_selected_logp_ex(_ptr(h), H, _ptr(w), H, _ptr(y), T, H, V,
+                                   float(inv_tau), int(bool(bf16)), _ptr(logp),
+                                   _ptr(lse), _ptr(ent), nthreads):
+        raise MemoryError("oracle_selected_logp_ex failed")
+    return logp, lse, ent
 
 
 def sample_targets(log_probs: np.ndarray, u: np.ndarray) -> np.ndarray:
