@@ -78,6 +78,51 @@ def cpu_baseline(case, seconds: float) -> dict:
                       f"full vocabulary V={case.V}, fp64, {wall:.1f} s wall"}
 
 
+def time_variants(rlk, torch, hidden, weight, targets, T, H, V, steps, flops):
+    """The same workload through the other entry points, timed after (never
+    inside) the headline region: the contract options (1/tau = 0.7, bf16
+    logits, entropy) and the statistics computed as 4 vocabulary slices plus
+    one merge.  Mean milliseconds per call over `steps` calls after 2 warm-up
+    calls, and the GEMM+statistics rate for the options kernel."""
+    dev = hidden.device
+    flags = rlk.RLK_LOGITS_BF16 | rlk.RLK_ENTROPY
+    ws_ex = torch.empty(rlk.rlk_workspace_bytes_ex(T, V, flags), dtype=torch.uint8, device=dev)
+    ws = rlk.workspace_for(T, V, dev)
+    cols = (V + 255) // 256
+    cuts = [0] + [round(i * cols / 4) * 256 for i in range(1, 4)] + [V]
+
+    def opts_stats():
+        rlk.rlk_vocab_stats_ex(hidden, weight, targets, ws_ex, V, 0, inv_temperature=0.7,
+                               logits_bf16=True, entropy=True)
+
+    def opts_merge():
+        rlk.rlk_vocab_merge_ex(targets, ws_ex, V, logits_bf16=True, entropy=True)
+
+    def slices():
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            rlk.rlk_vocab_stats_shard(hidden, weight[a:b], targets, ws, V, a)
+        rlk.rlk_vocab_merge(targets, ws, V)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    st = timed(opts_stats)
+    mg = timed(opts_merge)
+    sl = timed(slices)
+    return {"options_tau0.7_bf16_entropy": {"gemm_stats_ms": st, "merge_ms": mg,
+                                            "gemm_TFLOP/s": flops / (st * 1e-3) / 1e12},
+            "vocab_slices_4_plus_merge_ms": sl, "steps": steps}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -86,6 +131,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-time budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--variant-steps", type=int, default=10,
+                    help="timed calls per variant (options, vocabulary slices); 0 skips")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB before the "
                          "timed region (reference kernel for HBM counters)")
@@ -198,6 +245,9 @@ def main() -> int:
                         "compared": 2 * T * K},
         "kernel_source": kernel_source_digest(),
     }
+    if args.variant_steps > 0:
+        out["variants"] = time_variants(rlk, torch, hidden, weight, targets, T, H, V,
+                                        args.variant_steps, flops)
     if not args.no_cpu_baseline:
         log("bench: timing the fp64 oracle on the host")
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)

@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define RLK_ABI_VERSION 1
+#define RLK_ABI_VERSION 2
 
 /* Status codes returned by every entry point that can fail. */
 #define RLK_OK                      0
@@ -76,6 +76,13 @@ extern "C" {
 #define RLK_ERR_WORKSPACE_TOO_SMALL 5
 #define RLK_ERR_HIP                 6  /* a launch failed; rlk_last_hip_error()
                                           has the hipError_t */
+#define RLK_ERR_INVALID_VALUE       7  /* an option out of range: inverse
+                                          temperature not finite and > 0, or
+                                          unknown flag bits */
+
+/* Option flags of the _ex entry points. */
+#define RLK_LOGITS_BF16 1  /* round every (scaled) logit to bfloat16 */
+#define RLK_ENTROPY     2  /* also produce the per-row entropy */
 
 /* Size limits: T <= 2^31 - 1 rows, V <= 2^31 - 1, H <= 65536, row strides
  * ld_hidden, ld_weight <= 2^21 elements, and ceil(T/256) * ceil(V/256) below
@@ -171,6 +178,47 @@ int rlk_vocab_stats_shard(const void *hidden, int64_t ld_hidden,
                           const int32_t *targets, int64_t T, int64_t H, int64_t V,
                           int64_t v_begin, int64_t v_count, void *workspace,
                           size_t workspace_bytes, void *stream);
+
+/* The same path with the contract options (the variants an RL step needs
+ * from one pass over the LM head):
+ *   inv_temperature  every logit is first multiplied by this fp32 value, once
+ *                    (1/tau of sampling at temperature tau: the trainer must
+ *                    score softmax(z / tau) if the sampler drew from it).
+ *                    Finite and > 0.  1.0f changes no bit.
+ *   RLK_LOGITS_BF16  then every logit is rounded to bfloat16 (nearest, ties
+ *                    to even) and used as that value, for engines whose
+ *                    logits tensor is bf16 (the RL-Kernel blog, sections 二
+ *                    and 四, names this fp32 -> bf16 conversion as one point
+ *                    where the two sides drift apart; matching it is the
+ *                    caller's choice).
+ *   RLK_ENTROPY      also write entropy[t] = -sum_v p_v log p_v of softmax(z')
+ *                    (NaN where lse is not finite).  It costs one more
+ *                    statistic per tile: the workspace grows by a third.
+ * lse and logp are those of z' (the transformed logits); the numerical
+ * contract above holds for z' unchanged: a row's lse, logp and entropy are
+ * bitwise the same whatever the batch.  With inv_temperature == 1.0f and no
+ * RLK_LOGITS_BF16, lse and logp are bitwise those of the plain calls (also
+ * with RLK_ENTROPY).
+ *   entropy  fp32 [T], 4-byte aligned; required with RLK_ENTROPY, else
+ *            ignored (may be NULL).
+ *   workspace  at least rlk_workspace_bytes_ex(T, V, flags) bytes.
+ * rlk_vocab_stats_ex takes the slice arguments of rlk_vocab_stats_shard
+ * (v_begin = 0, v_count = V for the whole head); rlk_vocab_merge_ex must get
+ * the same flags as the stats call that filled the workspace.  Errors as for
+ * the plain calls, plus RLK_ERR_INVALID_VALUE. */
+size_t rlk_workspace_bytes_ex(int64_t T, int64_t V, int flags);
+int rlk_selected_logp_ex(const void *hidden, int64_t ld_hidden, const void *weight,
+                         int64_t ld_weight, const int32_t *targets, float *logp,
+                         float *lse, float *entropy, int64_t T, int64_t H, int64_t V,
+                         float inv_temperature, int flags, void *workspace,
+                         size_t workspace_bytes, void *stream);
+int rlk_vocab_stats_ex(const void *hidden, int64_t ld_hidden, const void *weight_shard,
+                       int64_t ld_weight, const int32_t *targets, int64_t T, int64_t H,
+                       int64_t V, int64_t v_begin, int64_t v_count, float inv_temperature,
+                       int flags, void *workspace, size_t workspace_bytes, void *stream);
+int rlk_vocab_merge_ex(const int32_t *targets, float *logp, float *lse, float *entropy,
+                       int64_t T, int64_t V, int flags, const void *workspace,
+                       size_t workspace_bytes, void *stream);
 
 /* The logits stage alone, for stage-by-stage comparison (the RL-Kernel blog,
  * section 五: compare intermediate results to find the first divergence).

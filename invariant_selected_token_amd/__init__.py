@@ -25,12 +25,17 @@ RLK_ERR_UNSUPPORTED = 3
 RLK_ERR_MISALIGNED = 4
 RLK_ERR_WORKSPACE_TOO_SMALL = 5
 RLK_ERR_HIP = 6
+RLK_ERR_INVALID_VALUE = 7
+
+RLK_LOGITS_BF16 = 1
+RLK_ENTROPY = 2
 
 EXPORTED = (
     "rlk_abi_version", "rlk_status_string", "rlk_last_hip_error",
     "rlk_vocab_tile", "rlk_selected_logp_workspace_bytes",
     "rlk_selected_logp", "rlk_vocab_stats", "rlk_vocab_stats_shard",
-    "rlk_vocab_merge", "rlk_logits", "rlk_compare",
+    "rlk_vocab_merge", "rlk_logits", "rlk_compare", "rlk_workspace_bytes_ex",
+    "rlk_selected_logp_ex", "rlk_vocab_stats_ex", "rlk_vocab_merge_ex",
 )
 
 _lib = None
@@ -82,6 +87,17 @@ def lib() -> ctypes.CDLL:
     L.rlk_logits.restype = c_int
     L.rlk_compare.argtypes = [vp, vp, i64, vp, vp]
     L.rlk_compare.restype = c_int
+    f32 = ctypes.c_float
+    L.rlk_workspace_bytes_ex.argtypes = [i64, i64, c_int]
+    L.rlk_workspace_bytes_ex.restype = sz
+    L.rlk_selected_logp_ex.argtypes = [vp, i64, vp, i64, vp, vp, vp, vp, i64, i64, i64,
+                                       f32, c_int, vp, sz, vp]
+    L.rlk_selected_logp_ex.restype = c_int
+    L.rlk_vocab_stats_ex.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, i64, i64, f32,
+                                     c_int, vp, sz, vp]
+    L.rlk_vocab_stats_ex.restype = c_int
+    L.rlk_vocab_merge_ex.argtypes = [vp, vp, vp, vp, i64, i64, c_int, vp, sz, vp]
+    L.rlk_vocab_merge_ex.restype = c_int
     _lib = L
     return L
 
@@ -104,6 +120,10 @@ def rlk_vocab_tile() -> int:
 
 def rlk_selected_logp_workspace_bytes(T: int, V: int) -> int:
     return int(lib().rlk_selected_logp_workspace_bytes(int(T), int(V)))
+
+
+def rlk_workspace_bytes_ex(T: int, V: int, flags: int) -> int:
+    return int(lib().rlk_workspace_bytes_ex(int(T), int(V), int(flags)))
 
 
 # ---------------------------------------------------------------- tensors --
@@ -253,6 +273,89 @@ def rlk_vocab_merge(targets, workspace, V, logp=None, lse=None, stream=None):
         targets.data_ptr(), logp.data_ptr(), lse.data_ptr(), T, int(V),
         workspace.data_ptr(), ws_bytes, _stream_ptr(stream, dev)))
     return logp, lse
+
+
+def _flags(logits_bf16, entropy):
+    return (RLK_LOGITS_BF16 if logits_bf16 else 0) | (RLK_ENTROPY if entropy else 0)
+
+
+def _entropy_out(dev, T, entropy, want):
+    torch = _torch()
+    if not want:
+        return None
+    if entropy is None or entropy is True:
+        entropy = torch.empty(T, dtype=torch.float32, device=dev)
+    if entropy.dtype != torch.float32 or entropy.shape != (T,) or not entropy.is_contiguous():
+        raise ValueError("entropy must be a contiguous float32 [T] tensor")
+    _check_device("entropy", entropy, dev)
+    return entropy
+
+
+def rlk_selected_logp_ex(hidden, weight, targets, inv_temperature=1.0, logits_bf16=False,
+                         entropy=False, logp=None, lse=None, workspace=None, V=None,
+                         stream=None):
+    """(logp, lse, entropy) with the contract options: logits times
+    ``inv_temperature``, optionally rounded to bf16; ``entropy`` True (or an
+    output tensor) also returns the per-row entropy, else None."""
+    dev, hp, ldh, wp, ldw, T, H, V = _prepare(hidden, weight, targets, V)
+    logp, lse = _outputs(dev, T, logp, lse)
+    flags = _flags(logits_bf16, entropy is not False and entropy is not None)
+    ent = _entropy_out(dev, T, entropy, flags & RLK_ENTROPY)
+    if workspace is None:
+        workspace = _torch().empty(max(rlk_workspace_bytes_ex(T, V, flags), 1),
+                                   dtype=_torch().uint8, device=dev)
+    _check_device("workspace", workspace, dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _call("rlk_selected_logp_ex", lib().rlk_selected_logp_ex(
+        hp, ldh, wp, ldw, targets.data_ptr(), logp.data_ptr(), lse.data_ptr(),
+        ent.data_ptr() if ent is not None else None, T, H, V, float(inv_temperature),
+        flags, workspace.data_ptr(), ws_bytes, _stream_ptr(stream, dev)))
+    return logp, lse, ent
+
+
+def rlk_vocab_stats_ex(hidden, weight_shard, targets, workspace, V, v_begin=0,
+                       inv_temperature=1.0, logits_bf16=False, entropy=False, stream=None):
+    """Stage 1 with the contract options on weight rows [v_begin, v_begin +
+    weight_shard.shape[0]) of a V-row head; workspace sized by
+    rlk_workspace_bytes_ex(T, V, flags)."""
+    torch = _torch()
+    dev = hidden.device
+    hp, ldh = _bf16_operand("hidden", hidden, dev)
+    wp, ldw = _bf16_operand("weight_shard", weight_shard, dev)
+    T, H = hidden.shape
+    if weight_shard.shape[1] != H:
+        raise ValueError("hidden and weight_shard disagree on H")
+    if targets.dtype != torch.int32 or targets.shape != (T,) or not targets.is_contiguous():
+        raise ValueError("targets must be a contiguous int32 [T] tensor")
+    _check_device("targets", targets, dev)
+    _check_device("workspace", workspace, dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _call("rlk_vocab_stats_ex", lib().rlk_vocab_stats_ex(
+        hp, ldh, wp, ldw, targets.data_ptr(), T, H, int(V), int(v_begin),
+        int(weight_shard.shape[0]), float(inv_temperature), _flags(logits_bf16, entropy),
+        workspace.data_ptr(), ws_bytes, _stream_ptr(stream, dev)))
+    return workspace
+
+
+def rlk_vocab_merge_ex(targets, workspace, V, logits_bf16=False, entropy=False, logp=None,
+                       lse=None, stream=None):
+    """Stage 2 with the same flags as stage 1 -> (logp, lse, entropy or None)."""
+    torch = _torch()
+    dev = targets.device
+    _check_device("targets", targets, dev)
+    if targets.dtype != torch.int32 or targets.dim() != 1 or not targets.is_contiguous():
+        raise ValueError("targets must be a contiguous int32 [T] tensor")
+    T = targets.shape[0]
+    logp, lse = _outputs(dev, T, logp, lse)
+    flags = _flags(logits_bf16, entropy is not False and entropy is not None)
+    ent = _entropy_out(dev, T, entropy, flags & RLK_ENTROPY)
+    _check_device("workspace", workspace, dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _call("rlk_vocab_merge_ex", lib().rlk_vocab_merge_ex(
+        targets.data_ptr(), logp.data_ptr(), lse.data_ptr(),
+        ent.data_ptr() if ent is not None else None, T, int(V), flags,
+        workspace.data_ptr(), ws_bytes, _stream_ptr(stream, dev)))
+    return logp, lse, ent
 
 
 def rlk_logits(hidden, weight, logits=None, V=None, stream=None):

@@ -49,6 +49,19 @@ int check_operands(const void *hidden, int64_t ldh, const void *weight,
   return RLK_OK;
 }
 
+// Contract options of the _ex entry points.
+int check_options(float inv_tau, int flags) {
+  if (!(inv_tau > 0.0f) || !(inv_tau <= 3.402823466e38f)) return RLK_ERR_INVALID_VALUE;
+  if (flags & ~(RLK_LOGITS_BF16 | RLK_ENTROPY)) return RLK_ERR_INVALID_VALUE;
+  return RLK_OK;
+}
+
+// Workspace: part_m, part_s, xt, then part_u when the entropy is asked for.
+size_t ws_bytes_for(int64_t T, int64_t V, int flags) {
+  return 2 * stats_bytes(T, V) + round_up((size_t)T * sizeof(float)) +
+         ((flags & RLK_ENTROPY) ? stats_bytes(T, V) : 0);
+}
+
 rlk::GemmArgs gemm_args(const void *hidden, int64_t ldh, const void *weight,
                         int64_t ldw, int64_t T, int64_t H, int64_t V) {
   rlk::GemmArgs g{};
@@ -106,21 +119,29 @@ const char *rlk_status_string(int status) {
              "4-byte vectors)";
     case RLK_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case RLK_ERR_HIP: return "HIP launch error (see rlk_last_hip_error)";
+    case RLK_ERR_INVALID_VALUE:
+      return "invalid option (inverse temperature not finite and > 0, or unknown flag bits)";
     default: return "unknown status";
   }
 }
 
-size_t rlk_selected_logp_workspace_bytes(int64_t T, int64_t V) {
+size_t rlk_workspace_bytes_ex(int64_t T, int64_t V, int flags) {
   if (T <= 0 || V <= 0 || T > MAX_ROWS || V > MAX_ROWS) return 0;
-  return 2 * stats_bytes(T, V) + round_up((size_t)T * sizeof(float));
+  if (check_options(1.0f, flags) != RLK_OK) return 0;
+  return ws_bytes_for(T, V, flags);
 }
 
-int rlk_vocab_stats_shard(const void *hidden, int64_t ld_hidden,
-                          const void *weight_shard, int64_t ld_weight,
-                          const int32_t *targets, int64_t T, int64_t H, int64_t V,
-                          int64_t v_begin, int64_t v_count, void *workspace,
-                          size_t workspace_bytes, void *stream) {
+size_t rlk_selected_logp_workspace_bytes(int64_t T, int64_t V) {
+  return rlk_workspace_bytes_ex(T, V, 0);
+}
+
+int rlk_vocab_stats_ex(const void *hidden, int64_t ld_hidden, const void *weight_shard,
+                       int64_t ld_weight, const int32_t *targets, int64_t T, int64_t H,
+                       int64_t V, int64_t v_begin, int64_t v_count, float inv_temperature,
+                       int flags, void *workspace, size_t workspace_bytes, void *stream) {
   int st = check_shapes(T, H, V, ld_hidden, ld_weight);
+  if (st != RLK_OK) return st;
+  st = check_options(inv_temperature, flags);
   if (st != RLK_OK) return st;
   if (v_begin < 0 || v_count <= 0 || v_begin > V - v_count) return RLK_ERR_INVALID_SHAPE;
   // Slices start on a workgroup column and all but the last are whole columns,
@@ -132,17 +153,31 @@ int rlk_vocab_stats_shard(const void *hidden, int64_t ld_hidden,
   if (st != RLK_OK) return st;
   if (!targets || !workspace) return RLK_ERR_NULL_POINTER;
   if (!aligned(targets, 4) || !aligned(workspace, 16)) return RLK_ERR_MISALIGNED;
-  if (workspace_bytes < rlk_selected_logp_workspace_bytes(T, V))
-    return RLK_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace_bytes < ws_bytes_for(T, V, flags)) return RLK_ERR_WORKSPACE_TOO_SMALL;
   char *ws = static_cast<char *>(workspace);
   rlk::GemmArgs g = gemm_args(hidden, ld_hidden, weight_shard, ld_weight, T, H, v_count);
   g.targets = targets;
   g.part_m = reinterpret_cast<float *>(ws);
   g.part_s = reinterpret_cast<float *>(ws + stats_bytes(T, V));
   g.xt = reinterpret_cast<float *>(ws + 2 * stats_bytes(T, V));
+  g.part_u = reinterpret_cast<float *>(ws + ws_bytes_for(T, V, 0));
   g.js_base = (int)(v_begin / rlk::STAT_V);
   g.y_base = (int)v_begin;
+  g.inv_tau = inv_temperature;
+  g.bf16_logits = (flags & RLK_LOGITS_BF16) ? 1 : 0;
+  // The plain kernel when no option changes a logit (its bits are those of
+  // the option kernel at inv_tau = 1 without rounding; the tests check it).
+  g.ex = (flags & RLK_ENTROPY) ? 2 : (inv_temperature != 1.0f || g.bf16_logits) ? 1 : 0;
   return hip_status(rlk::launch_gemm_stats(g, compute_units(), static_cast<hipStream_t>(stream)));
+}
+
+int rlk_vocab_stats_shard(const void *hidden, int64_t ld_hidden,
+                          const void *weight_shard, int64_t ld_weight,
+                          const int32_t *targets, int64_t T, int64_t H, int64_t V,
+                          int64_t v_begin, int64_t v_count, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  return rlk_vocab_stats_ex(hidden, ld_hidden, weight_shard, ld_weight, targets, T, H, V,
+                            v_begin, v_count, 1.0f, 0, workspace, workspace_bytes, stream);
 }
 
 int rlk_vocab_stats(const void *hidden, int64_t ld_hidden, const void *weight,
@@ -153,23 +188,26 @@ int rlk_vocab_stats(const void *hidden, int64_t ld_hidden, const void *weight,
                                workspace, workspace_bytes, stream);
 }
 
-int rlk_vocab_merge(const int32_t *targets, float *logp, float *lse, int64_t T,
-                    int64_t V, const void *workspace, size_t workspace_bytes,
-                    void *stream) {
+int rlk_vocab_merge_ex(const int32_t *targets, float *logp, float *lse, float *entropy,
+                       int64_t T, int64_t V, int flags, const void *workspace,
+                       size_t workspace_bytes, void *stream) {
   if (T < 0 || V <= 0) return RLK_ERR_INVALID_SHAPE;
   if (T > MAX_ROWS || V > MAX_ROWS) return RLK_ERR_UNSUPPORTED;
+  if (check_options(1.0f, flags) != RLK_OK) return RLK_ERR_INVALID_VALUE;
   if (T == 0) return RLK_OK;
-  if (!targets || !logp || !lse || !workspace) return RLK_ERR_NULL_POINTER;
+  const bool ent = (flags & RLK_ENTROPY) != 0;
+  if (!targets || !logp || !lse || !workspace || (ent && !entropy)) return RLK_ERR_NULL_POINTER;
   if (!aligned(targets, 4) || !aligned(logp, 4) || !aligned(lse, 4) ||
-      !aligned(workspace, 16))
+      !aligned(workspace, 16) || (ent && !aligned(entropy, 4)))
     return RLK_ERR_MISALIGNED;
-  if (workspace_bytes < rlk_selected_logp_workspace_bytes(T, V))
-    return RLK_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace_bytes < ws_bytes_for(T, V, flags)) return RLK_ERR_WORKSPACE_TOO_SMALL;
   const char *ws = static_cast<const char *>(workspace);
   rlk::MergeArgs mg{};
   mg.part_m = reinterpret_cast<const float *>(ws);
   mg.part_s = reinterpret_cast<const float *>(ws + stats_bytes(T, V));
   mg.xt = reinterpret_cast<const float *>(ws + 2 * stats_bytes(T, V));
+  mg.part_u = ent ? reinterpret_cast<const float *>(ws + ws_bytes_for(T, V, 0)) : nullptr;
+  mg.entropy = ent ? entropy : nullptr;
   mg.targets = targets;
   mg.logp = logp;
   mg.lse = lse;
@@ -179,24 +217,44 @@ int rlk_vocab_merge(const int32_t *targets, float *logp, float *lse, int64_t T,
   return hip_status(rlk::launch_merge(mg, static_cast<hipStream_t>(stream)));
 }
 
+int rlk_vocab_merge(const int32_t *targets, float *logp, float *lse, int64_t T,
+                    int64_t V, const void *workspace, size_t workspace_bytes,
+                    void *stream) {
+  return rlk_vocab_merge_ex(targets, logp, lse, nullptr, T, V, 0, workspace,
+                            workspace_bytes, stream);
+}
+
+int rlk_selected_logp_ex(const void *hidden, int64_t ld_hidden, const void *weight,
+                         int64_t ld_weight, const int32_t *targets, float *logp,
+                         float *lse, float *entropy, int64_t T, int64_t H, int64_t V,
+                         float inv_temperature, int flags, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+  // Validate everything both stages need before launching the first one.
+  int st = check_shapes(T, H, V, ld_hidden, ld_weight);
+  if (st != RLK_OK) return st;
+  st = check_options(inv_temperature, flags);
+  if (st != RLK_OK) return st;
+  if (T == 0) return RLK_OK;
+  st = check_operands(hidden, ld_hidden, weight, ld_weight);
+  if (st != RLK_OK) return st;
+  const bool ent = (flags & RLK_ENTROPY) != 0;
+  if (!targets || !logp || !lse || !workspace || (ent && !entropy)) return RLK_ERR_NULL_POINTER;
+  if (!aligned(logp, 4) || !aligned(lse, 4) || (ent && !aligned(entropy, 4)))
+    return RLK_ERR_MISALIGNED;
+  st = rlk_vocab_stats_ex(hidden, ld_hidden, weight, ld_weight, targets, T, H, V, 0, V,
+                          inv_temperature, flags, workspace, workspace_bytes, stream);
+  if (st != RLK_OK) return st;
+  return rlk_vocab_merge_ex(targets, logp, lse, entropy, T, V, flags, workspace,
+                            workspace_bytes, stream);
+}
+
 int rlk_selected_logp(const void *hidden, int64_t ld_hidden,
                       const void *weight, int64_t ld_weight,
                       const int32_t *targets, float *logp, float *lse,
                       int64_t T, int64_t H, int64_t V, void *workspace,
                       size_t workspace_bytes, void *stream) {
-  // Validate everything both stages need before launching the first one.
-  int st = check_shapes(T, H, V, ld_hidden, ld_weight);
-  if (st != RLK_OK) return st;
-  if (T == 0) return RLK_OK;
-  st = check_operands(hidden, ld_hidden, weight, ld_weight);
-  if (st != RLK_OK) return st;
-  if (!targets || !logp || !lse || !workspace) return RLK_ERR_NULL_POINTER;
-  if (!aligned(logp, 4) || !aligned(lse, 4)) return RLK_ERR_MISALIGNED;
-  st = rlk_vocab_stats(hidden, ld_hidden, weight, ld_weight, targets, T, H, V,
-                       workspace, workspace_bytes, stream);
-  if (st != RLK_OK) return st;
-  return rlk_vocab_merge(targets, logp, lse, T, V, workspace, workspace_bytes,
-                         stream);
+  return rlk_selected_logp_ex(hidden, ld_hidden, weight, ld_weight, targets, logp, lse,
+                              nullptr, T, H, V, 1.0f, 0, workspace, workspace_bytes, stream);
 }
 
 int rlk_logits(const void *hidden, int64_t ld_hidden, const void *weight,

@@ -32,6 +32,13 @@ struct GemmArgs {
   float *part_s;   // [nST][T] per-statistics-tile sums of exp(z - m)
   float *xt;       // [T] target logits
   float *logits;   // [T][V] (logits stage only)
+  float *part_u;   // [nST][T] per-tile sums of exp(z - m) (z - m) (entropy only)
+  // Contract options (statistics kernel, ex variants only): every logit is
+  // multiplied by inv_tau and, when bf16_logits, rounded to bf16.
+  float inv_tau;
+  int bf16_logits;
+  // 0: plain statistics; 1: with the options; 2: options and entropy partials
+  int ex;
   int64_t ldh;
   int64_t ldw;
   int T;
@@ -48,9 +55,11 @@ struct MergeArgs {
   const float *part_m;
   const float *part_s;
   const float *xt;
+  const float *part_u;   // entropy partials (when entropy != nullptr)
   const int32_t *targets;
   float *logp;
   float *lse;
+  float *entropy;        // nullptr: no entropy
   int T;
   int V;
   int nST;

@@ -14,7 +14,15 @@
 //                       stage-by-stage comparison of section 五).
 //   merge_kernel        per row, folds the tile statistics in a fixed order
 //                       that depends only on the number of vocabulary tiles,
-//                       then lse = M + log(s) and logp = z_y - lse.
+//                       then lse = M + log(s) and logp = z_y - lse (and, with
+//                       the entropy partials, H = log S - U / S).
+//
+// Contract options (the EX instantiations of the statistics kernel): the
+// logits are multiplied by 1/tau (sampling temperature) and optionally
+// rounded to bf16 (engines that keep a bf16 logits tensor; the blog's
+// sections 二/四 name that cast as a drift point) before the statistics and
+// the target capture; with EX == 2 each tile also yields
+// u = sum exp(z - m) (z - m), from which the merge forms the entropy.
 //   compare_kernel      mismatch count / max |diff| / k3 of two fp32 arrays
 //                       (sections 六/七; the vLLM blog summary's diff = 0).
 //
@@ -26,6 +34,7 @@
 // merge's fold depends only on ceil(V / STAT_V).  No split-K, no atomics, no
 // shape-dependent kernel choice.
 #include <hip/hip_runtime.h>
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -105,7 +114,7 @@ __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1
 // issues the next tile's first K-block loads before the current tile's
 // epilogue, so that their latency hides under the epilogue.  The order of
 // tiles only changes the schedule; every tile's arithmetic is the same.
-template <bool STATS, bool PERSIST>
+template <bool STATS, bool PERSIST, int EX>
 __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -334,6 +343,27 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
       // A wave whose tile starts at or past V (only in the last workgroup
       // column when V mod 256 <= 128) has nothing to write.
       const int js = 2 * n + wv;
+      if constexpr (EX > 0) {
+        // The options, once per logit: one fp32 multiply (exact for
+        // inv_tau == 1), then the fp32 -> bf16 cast (nearest, ties to even)
+        // and back.
+        if (a.bf16_logits) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int r = 0; r < 16; ++r)
+                acc[i][j][r] = (float)(__bf16)(acc[i][j][r] * a.inv_tau);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) acc[i][j][r] = acc[i][j][r] * a.inv_tau;
+        }
+      }
       auto stats_epilogue = [&](auto masked) {
         constexpr bool MASK = decltype(masked)::value;
         // Columns past the vocabulary end count as -inf: they add nothing to
@@ -359,22 +389,36 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
           //    tile is -inf so that such a tile adds exactly 0.  z == m gives
           //    exp(0) = 1 exactly, so the sum is >= 1 when the max is finite.
           const float ms = (m2 == -INFINITY) ? 0.0f : m2;
-          float sx = 0.0f;
+          float sx = 0.0f, ux = 0.0f;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const bool out = MASK && (32 * i + 8 * (r >> 2) + (r & 3) >= lim);
               const float z = out ? -INFINITY : acc[i][j][r];
-              sx = sx + __builtin_amdgcn_exp2f((z - ms) * LOG2E);
+              const float d = z - ms;
+              const float e = __builtin_amdgcn_exp2f(d * LOG2E);
+              sx = sx + e;
+              // entropy partial: e (z - m); a -inf logit has e == 0 and
+              // adds -0 (d clamped to the finite range first)
+              if constexpr (EX == 2) ux = ux + e * fmaxf(d, -FLT_MAX);
             }
           const float so = __shfl_xor(sx, 32);
           const float s2 = fk == 0 ? sx + so : so + sx;
+          float u2 = 0.0f;
+          if constexpr (EX == 2) {
+            const float uo = __shfl_xor(ux, 32);
+            u2 = fk == 0 ? ux + uo : uo + ux;
+          }
           // 3) tile-major [nST][T] statistics (coalesced over rows).
           if (t < a.T) {
             const size_t o = (size_t)(a.js_base + js) * a.T + t;
-            if (fk == 0) a.part_m[o] = m2;
-            else a.part_s[o] = s2;
+            if (fk == 0) {
+              a.part_m[o] = m2;
+              if constexpr (EX == 2) a.part_u[o] = u2;
+            } else {
+              a.part_s[o] = s2;
+            }
           }
           // 4) target capture: the one lane holding z[t][y[t]] writes xt[t],
           //    the value picked by a fixed select tree over its 64 values.
@@ -426,10 +470,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
 // Launch shapes: the statistics kernel is persistent (one workgroup per
 // compute unit walking the tiles); the logits-stage kernel uses one
 // workgroup per tile.
-template <bool STATS, bool PERSIST>
+template <bool STATS, bool PERSIST, int EX>
 __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[4 * STAGE_BYTES + PREFETCH_SINK];
-  gemm_body<STATS, PERSIST>(a, smem);
+  gemm_body<STATS, PERSIST, EX>(a, smem);
 }
 
 // Per row t: M = max_j m_j (exact in any order), then
@@ -439,9 +483,15 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmArgs a) {
 // Loads are issued MERGE_UNROLL at a time ahead of the fold; slots past the
 // group's end contribute max(-inf) and + 0 * exp(-inf) = + 0, which changes
 // nothing (the running sum is never -0).
+//
+// With ENT, the same fold also carries U = sum_j e_j (u_j + (m_j - M) s_j),
+// e_j = exp(m_j - M): the sum over the row of exp(z - M) (z - M), all terms
+// <= 0, so H = log S - U / S involves no cancellation.
+template <bool ENT>
 __global__ __launch_bounds__(MERGE_GROUPS * MERGE_ROWS) void merge_kernel(
     const MergeArgs a) {
   __shared__ float red[MERGE_GROUPS][MERGE_ROWS];
+  __shared__ float redu[ENT ? MERGE_GROUPS : 1][MERGE_ROWS];
   const int lane = threadIdx.x & (MERGE_ROWS - 1);
   const int g = threadIdx.x / MERGE_ROWS;
   const int t = blockIdx.x * MERGE_ROWS + lane;
@@ -451,6 +501,7 @@ __global__ __launch_bounds__(MERGE_GROUPS * MERGE_ROWS) void merge_kernel(
   const int j1 = min(a.nST, j0 + gs);
   const float *pm = a.part_m + (valid ? t : 0);
   const float *ps = a.part_s + (valid ? t : 0);
+  const float *pu = ENT ? a.part_u + (valid ? t : 0) : nullptr;
   const size_t T = (size_t)a.T;
 
   float mg = -INFINITY;
@@ -470,29 +521,45 @@ __global__ __launch_bounds__(MERGE_GROUPS * MERGE_ROWS) void merge_kernel(
   __syncthreads();
   const float Ms = (M == -INFINITY) ? 0.0f : M;
 
-  float sg = 0.0f;
+  float sg = 0.0f, ug = 0.0f;
   for (int j = j0; j < j1; j += MERGE_UNROLL) {
-    float vm[MERGE_UNROLL], vs[MERGE_UNROLL];
+    float vm[MERGE_UNROLL], vs[MERGE_UNROLL], vu[ENT ? MERGE_UNROLL : 1];
 #pragma unroll
     for (int u = 0; u < MERGE_UNROLL; ++u) {
       const bool in = valid && j + u < j1;
       vm[u] = in ? pm[(size_t)(j + u) * T] : -INFINITY;
       vs[u] = in ? ps[(size_t)(j + u) * T] : 0.0f;
+      if constexpr (ENT) vu[u] = in ? pu[(size_t)(j + u) * T] : 0.0f;
     }
 #pragma unroll
-    for (int u = 0; u < MERGE_UNROLL; ++u)
-      sg = sg + vs[u] * __builtin_amdgcn_exp2f((vm[u] - Ms) * LOG2E);
+    for (int u = 0; u < MERGE_UNROLL; ++u) {
+      const float dm = vm[u] - Ms;
+      const float e = __builtin_amdgcn_exp2f(dm * LOG2E);
+      sg = sg + vs[u] * e;
+      // a tile with m_j = -inf has s_j = u_j = 0 and e = 0: it adds 0
+      if constexpr (ENT) ug = ug + e * (vu[u] + fmaxf(dm, -FLT_MAX) * vs[u]);
+    }
   }
   red[g][lane] = sg;
+  if constexpr (ENT) redu[g][lane] = ug;
   __syncthreads();
   if (g == 0 && valid) {
     float sum = red[0][lane];
 #pragma unroll
     for (int q = 1; q < MERGE_GROUPS; ++q) sum = sum + red[q][lane];
-    const float lse = M + __builtin_amdgcn_logf(sum) * LN2;
+    const float logs = __builtin_amdgcn_logf(sum) * LN2;
+    const float lse = M + logs;
     const int y = a.targets[t];
     a.lse[t] = lse;
     a.logp[t] = (y >= 0 && y < a.V) ? a.xt[t] - lse : __builtin_nanf("");
+    if constexpr (ENT) {
+      float us = redu[0][lane];
+#pragma unroll
+      for (int q = 1; q < MERGE_GROUPS; ++q) us = us + redu[q][lane];
+      // a row whose lse is not finite has no entropy
+      a.entropy[t] = (lse == lse && fabsf(lse) != INFINITY) ? logs - us / sum
+                                                            : __builtin_nanf("");
+    }
   }
 }
 
@@ -558,19 +625,28 @@ hipError_t launch_gemm_stats(const GemmArgs &a, int workers, hipStream_t s) {
   // A multiple of 8 workgroups keeps each one on a fixed XCD.
   int grid = workers >= 8 ? workers - workers % 8 : 8;
   if (grid > tiles) grid = tiles;
-  hipLaunchKernelGGL((gemm_kernel<true, true>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
+  if (a.ex == 2)
+    hipLaunchKernelGGL((gemm_kernel<true, true, 2>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
+  else if (a.ex == 1)
+    hipLaunchKernelGGL((gemm_kernel<true, true, 1>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel<true, true, 0>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_logits(const GemmArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_kernel<false, false>), dim3(a.nMT * a.nVT), dim3(GEMM_THREADS),
+  hipLaunchKernelGGL((gemm_kernel<false, false, 0>), dim3(a.nMT * a.nVT), dim3(GEMM_THREADS),
                      0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_merge(const MergeArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(merge_kernel, dim3(ceil_div(a.T, MERGE_ROWS)),
-                     dim3(MERGE_GROUPS * MERGE_ROWS), 0, s, a);
+  if (a.entropy)
+    hipLaunchKernelGGL(merge_kernel<true>, dim3(ceil_div(a.T, MERGE_ROWS)),
+                       dim3(MERGE_GROUPS * MERGE_ROWS), 0, s, a);
+  else
+    hipLaunchKernelGGL(merge_kernel<false>, dim3(ceil_div(a.T, MERGE_ROWS)),
+                       dim3(MERGE_GROUPS * MERGE_ROWS), 0, s, a);
   return hipGetLastError();
 }
 

@@ -37,10 +37,10 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_constants():
-    assert rlk.rlk_abi_version() == 1
+    assert rlk.rlk_abi_version() == 2
     assert rlk.rlk_vocab_tile() == 128
-    msgs = {rlk.rlk_status_string(s) for s in range(7)}
-    assert len(msgs) == 7 and all(msgs)
+    msgs = {rlk.rlk_status_string(s) for s in range(8)}
+    assert len(msgs) == 8 and all(msgs)
     assert rlk.rlk_status_string(99) == "unknown status"
 
 
@@ -256,3 +256,101 @@ def test_one_hip_runtime_in_the_process():
     assert out.returncode == 0, out.stderr
     paths = eval(out.stdout.strip().splitlines()[-1])
     assert len(paths) == 1, paths
+
+
+# ------------------------------------------------------ contract options --
+
+def test_workspace_size_ex():
+    ws, wx = rlk.rlk_selected_logp_workspace_bytes, rlk.rlk_workspace_bytes_ex
+    r = lambda x: (x + 255) // 256 * 256
+    for T, V in [(1, 1), (64, 4096), (4096, 151936), (257, 129)]:
+        assert wx(T, V, 0) == ws(T, V)
+        assert wx(T, V, rlk.RLK_LOGITS_BF16) == ws(T, V)
+        stats = r(((V + 127) // 128) * T * 4)
+        assert wx(T, V, rlk.RLK_ENTROPY) == ws(T, V) + stats
+        assert wx(T, V, rlk.RLK_ENTROPY | rlk.RLK_LOGITS_BF16) == ws(T, V) + stats
+    assert wx(4, 1000, 4) == 0 and wx(4, 1000, -1) == 0 and wx(0, 10, 0) == 0
+
+
+def _ex(hidden=FAKE, ldh=256, weight=FAKE, ldw=256, targets=FAKE, logp=FAKE, lse=FAKE,
+        entropy=FAKE, T=4, H=256, V=1000, inv_tau=1.0, flags=rlk.RLK_ENTROPY, ws=WS_FAKE,
+        ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = rlk.rlk_workspace_bytes_ex(T, V, flags if flags in (0, 1, 2, 3) else 0)
+    return rlk.lib().rlk_selected_logp_ex(hidden, ldh, weight, ldw, targets, logp, lse,
+                                          entropy, T, H, V, inv_tau, flags, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(inv_tau=0.0), rlk.RLK_ERR_INVALID_VALUE),
+    (dict(inv_tau=-1.0), rlk.RLK_ERR_INVALID_VALUE),
+    (dict(inv_tau=float("inf")), rlk.RLK_ERR_INVALID_VALUE),
+    (dict(inv_tau=float("nan")), rlk.RLK_ERR_INVALID_VALUE),
+    (dict(flags=4), rlk.RLK_ERR_INVALID_VALUE),
+    (dict(flags=-1), rlk.RLK_ERR_INVALID_VALUE),
+    (dict(T=0, inv_tau=0.0), rlk.RLK_ERR_INVALID_VALUE),          # options before T == 0
+    (dict(entropy=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(entropy=FAKE + 2), rlk.RLK_ERR_MISALIGNED),
+    (dict(H=100, ldh=104, ldw=104), rlk.RLK_ERR_UNSUPPORTED),
+    (dict(T=-1), rlk.RLK_ERR_INVALID_SHAPE),
+    (dict(logp=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(ws=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(T=0, hidden=None, weight=None, targets=None, logp=None, lse=None, entropy=None,
+          ws=None, ws_bytes=0), rlk.RLK_OK),
+])
+def test_selected_logp_ex_error_paths(kw, status):
+    assert _ex(**kw) == status
+    assert rlk.rlk_last_hip_error() == 0
+
+
+def test_selected_logp_ex_entropy_needs_the_larger_workspace():
+    T, V = 1000, 1000
+    plain = rlk.rlk_workspace_bytes_ex(T, V, 0)
+    assert plain < rlk.rlk_workspace_bytes_ex(T, V, rlk.RLK_ENTROPY)
+    assert _ex(T=T, V=V, ws_bytes=plain) == rlk.RLK_ERR_WORKSPACE_TOO_SMALL
+    # without the entropy flag the entropy pointer is ignored (may be NULL),
+    # and validation gets as far as the workspace size
+    assert _ex(T=T, V=V, flags=rlk.RLK_LOGITS_BF16, entropy=None,
+               ws_bytes=plain - 1) == rlk.RLK_ERR_WORKSPACE_TOO_SMALL
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(inv_tau=0.0), rlk.RLK_ERR_INVALID_VALUE),
+    (dict(flags=8), rlk.RLK_ERR_INVALID_VALUE),
+    (dict(v_begin=128, v_count=256), rlk.RLK_ERR_UNSUPPORTED),
+    (dict(v_begin=128), rlk.RLK_ERR_INVALID_SHAPE),                 # past V
+    (dict(ws_bytes=64), rlk.RLK_ERR_WORKSPACE_TOO_SMALL),
+    (dict(targets=None), rlk.RLK_ERR_NULL_POINTER),
+])
+def test_vocab_stats_ex_error_paths(kw, status):
+    a = dict(hidden=FAKE, ldh=256, weight=FAKE, ldw=256, targets=FAKE, T=4, H=256, V=1000,
+             v_begin=0, v_count=1000, inv_tau=1.0, flags=rlk.RLK_ENTROPY, ws=WS_FAKE,
+             ws_bytes=None)
+    a.update(kw)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = rlk.rlk_workspace_bytes_ex(4, 1000, rlk.RLK_ENTROPY)
+    assert rlk.lib().rlk_vocab_stats_ex(
+        a["hidden"], a["ldh"], a["weight"], a["ldw"], a["targets"], a["T"], a["H"], a["V"],
+        a["v_begin"], a["v_count"], a["inv_tau"], a["flags"], a["ws"], a["ws_bytes"],
+        None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(flags=4), rlk.RLK_ERR_INVALID_VALUE),
+    (dict(entropy=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(entropy=FAKE + 1), rlk.RLK_ERR_MISALIGNED),
+    (dict(ws_bytes=("plain",)), rlk.RLK_ERR_WORKSPACE_TOO_SMALL),
+    (dict(T=0, targets=None, logp=None, lse=None, entropy=None, ws=None, ws_bytes=0),
+     rlk.RLK_OK),
+])
+def test_vocab_merge_ex_error_paths(kw, status):
+    a = dict(targets=FAKE, logp=FAKE, lse=FAKE, entropy=FAKE, T=1000, V=1000,
+             flags=rlk.RLK_ENTROPY, ws=WS_FAKE, ws_bytes=None)
+    a.update(kw)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = rlk.rlk_workspace_bytes_ex(1000, 1000, rlk.RLK_ENTROPY)
+    elif isinstance(a["ws_bytes"], tuple):
+        a["ws_bytes"] = rlk.rlk_workspace_bytes_ex(1000, 1000, 0)
+    assert rlk.lib().rlk_vocab_merge_ex(a["targets"], a["logp"], a["lse"], a["entropy"],
+                                        a["T"], a["V"], a["flags"], a["ws"], a["ws_bytes"],
+                                        None) == status
