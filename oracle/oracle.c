@@ -56,6 +56,17 @@
  *     to nearest, ties to even, taken on the logit as an fp32 value (the
  *     precision in which an engine holds it before the cast): fp64 logit ->
  *     nearest fp32 -> nearest bf16.
+ *   - Backward (oracle_selected_logp_backward): for an upstream gradient
+ *     g[t] = dL/dlogp[t], the gradient of L = sum_t g[t] logp[t] with respect
+ *     to the logits is dz[t][v] = g[t] inv_tau (1[v == y_t] - p[t][v]),
+ *     p = softmax(z'), and by the chain rule through z = h w^T:
+ *       grad_hidden[t][k] = sum_v dz[t][v] w[v][k],
+ *       grad_weight[v][k] = sum_t dz[t][v] h[t][k].
+ *     A row whose target lies outside [0, V) has no log-probability to
+ *     differentiate (its logp is NaN); it contributes no gradient (dz = 0),
+ *     like an ignored index.  The training side of the vLLM blog summary
+ *     differentiates the logprob it recomputes in a graph; the backward is
+ *     verified on its own (its C7 check).
  *   - Entropy of softmax(z'): H = -sum_v p_v log p_v with
  *     p_v = exp(z'_v - lse), terms with p_v = 0 contributing 0; NaN when the
  *     row's lse is not finite.  (The vLLM blog summary lists entropy among the
@@ -69,7 +80,7 @@
 #include <omp.h>
 #endif
 
-#define ORACLE_VERSION 2
+#define ORACLE_VERSION 3
 
 int oracle_version(void) { return ORACLE_VERSION; }
 
@@ -365,4 +376,93 @@ int oracle_selected_logp_ex(const uint16_t *hidden, int64_t ldh,
         free(z);
     }
     return fail ? -1 : 0;
+}
+
+/* dz[t][v] of one row from its fp64 logits (already scaled by inv_tau). */
+static void row_dz(const double *zs, int64_t V, int64_t y, double g, double inv_tau,
+                   double *dz) {
+    double lse, logp;
+    row_lse_logp(zs, V, y, &lse, &logp);
+    if (y < 0 || y >= V) {
+        for (int64_t v = 0; v < V; ++v) dz[v] = 0.0;
+        return;
+    }
+    for (int64_t v = 0; v < V; ++v) {
+        const double p = exp(zs[v] - lse);
+        dz[v] = g * inv_tau * ((v == y ? 1.0 : 0.0) - p);
+    }
+}
+
+/* Gradient with respect to the logits, dz [T][V] (fp64).  Returns 0 or -1. */
+int oracle_logp_grad_logits(const uint16_t *hidden, int64_t ldh,
+                            const uint16_t *weight, int64_t ldw,
+                            const int32_t *targets, const double *grad_logp,
+                            int64_t T, int64_t H, int64_t V, double inv_tau,
+                            double *dz, int nthreads) {
+    int fail = 0;
+    set_threads(nthreads);
+#pragma omp parallel
+    {
+        double *h = (double *)malloc((size_t)(H > 0 ? H : 1) * sizeof(double));
+        double *z = (double *)malloc((size_t)(V > 0 ? V : 1) * sizeof(double));
+        if (!h || !z) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t t = 0; t < T; ++t) {
+                hidden_row(hidden, ldh, t, H, h);
+                row_logits(h, weight, ldw, H, V, z);
+                row_transform(z, V, inv_tau, 0);
+                row_dz(z, V, (int64_t)targets[t], grad_logp[t], inv_tau, dz + t * V);
+            }
+        }
+        free(h);
+        free(z);
+    }
+    return fail ? -1 : 0;
+}
+
+/* grad_hidden [T][H] and / or grad_weight [V][H] (either may be NULL), fp64.
+ * Each output element is one sum in increasing index order (v for
+ * grad_hidden, t for grad_weight).  Returns 0 or -1. */
+int oracle_selected_logp_backward(const uint16_t *hidden, int64_t ldh,
+                                  const uint16_t *weight, int64_t ldw,
+                                  const int32_t *targets, const double *grad_logp,
+                                  int64_t T, int64_t H, int64_t V, double inv_tau,
+                                  double *grad_hidden, double *grad_weight,
+                                  int nthreads) {
+    double *dz = (double *)malloc((size_t)(T * V > 0 ? T * V : 1) * sizeof(double));
+    if (!dz) return -1;
+    if (oracle_logp_grad_logits(hidden, ldh, weight, ldw, targets, grad_logp, T, H, V,
+                                inv_tau, dz, nthreads)) {
+        free(dz);
+        return -1;
+    }
+    if (grad_hidden) {
+#pragma omp parallel for schedule(static)
+        for (int64_t t = 0; t < T; ++t) {
+            double *out = grad_hidden + t * H;
+            for (int64_t k = 0; k < H; ++k) out[k] = 0.0;
+            for (int64_t v = 0; v < V; ++v) {
+                const double d = dz[t * V + v];
+                const uint16_t *wv = weight + v * ldw;
+                for (int64_t k = 0; k < H; ++k) out[k] = out[k] + d * bf16_to_f64(wv[k]);
+            }
+        }
+    }
+    if (grad_weight) {
+#pragma omp parallel for schedule(static)
+        for (int64_t v = 0; v < V; ++v) {
+            double *out = grad_weight + v * H;
+            for (int64_t k = 0; k < H; ++k) out[k] = 0.0;
+            for (int64_t t = 0; t < T; ++t) {
+                const double d = dz[t * V + v];
+                const uint16_t *ht = hidden + t * ldh;
+                for (int64_t k = 0; k < H; ++k) out[k] = out[k] + d * bf16_to_f64(ht[k]);
+            }
+        }
+    }
+    free(dz);
+    return 0;
 }

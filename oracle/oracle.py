@@ -71,6 +71,12 @@ def _load():
     lib.oracle_selected_logp_ex.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64,
                                             ctypes.c_double, c_int, vp, vp, vp, c_int]
     lib.oracle_selected_logp_ex.restype = c_int
+    lib.oracle_logp_grad_logits.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64,
+                                            ctypes.c_double, vp, c_int]
+    lib.oracle_logp_grad_logits.restype = c_int
+    lib.oracle_selected_logp_backward.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64,
+                                                  ctypes.c_double, vp, vp, c_int]
+    lib.oracle_selected_logp_backward.restype = c_int
     _lib = lib
     return lib
 
@@ -209,6 +215,49 @@ def selected_logp_ex(hidden, weight, targets, inv_tau: float = 1.0, bf16: bool =
                                    _ptr(lse), _ptr(ent), nthreads):
         raise MemoryError("oracle_selected_logp_ex failed")
     return logp, lse, ent
+
+
+def _bwd_args(hidden, weight, targets, grad_logp):
+    h, w = _bf16_2d(hidden), _bf16_2d(weight)
+    T, H = h.shape
+    V = w.shape[0]
+    if w.shape[1] != H:
+        raise ValueError("hidden and weight disagree on H")
+    y = np.ascontiguousarray(targets, dtype=np.int32)
+    g = np.ascontiguousarray(grad_logp, dtype=np.float64)
+    if y.shape != (T,) or g.shape != (T,):
+        raise ValueError("targets and grad_logp must have shape [T]")
+    return h, w, y, g, T, H, V
+
+
+def grad_logits(hidden, weight, targets, grad_logp, inv_tau: float = 1.0,
+                nthreads: int = 0) -> np.ndarray:
+    """dz [T, V] = g inv_tau (onehot(y) - softmax(inv_tau z)), fp64; rows with
+    an out-of-range target are 0."""
+    lib = _load()
+    h, w, y, g, T, H, V = _bwd_args(hidden, weight, targets, grad_logp)
+    dz = np.empty((T, V), dtype=np.float64)
+    if lib.oracle_logp_grad_logits(_ptr(h), H, _ptr(w), H, _ptr(y), _ptr(g), T, H, V,
+                                   float(inv_tau), _ptr(dz), nthreads):
+        raise MemoryError("oracle_logp_grad_logits failed")
+    return dz
+
+
+def selected_logp_backward(hidden, weight, targets, grad_logp, inv_tau: float = 1.0,
+                           want_hidden: bool = True, want_weight: bool = True,
+                           nthreads: int = 0):
+    """(grad_hidden [T, H] or None, grad_weight [V, H] or None) in fp64 for
+    L = sum_t grad_logp[t] logp[t]."""
+    lib = _load()
+    h, w, y, g, T, H, V = _bwd_args(hidden, weight, targets, grad_logp)
+    gh = np.empty((T, H), dtype=np.float64) if want_hidden else None
+    gw = np.empty((V, H), dtype=np.float64) if want_weight else None
+    if lib.oracle_selected_logp_backward(_ptr(h), H, _ptr(w), H, _ptr(y), _ptr(g), T, H, V,
+                                         float(inv_tau),
+                                         _ptr(gh) if gh is not None else None,
+                                         _ptr(gw) if gw is not None else None, nthreads):
+        raise MemoryError("oracle_selected_logp_backward failed")
+    return gh, gw
 
 
 def sample_targets(log_probs: np.ndarray, u: np.ndarray) -> np.ndarray:
