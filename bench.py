@@ -118,9 +118,27 @@ def time_variants(rlk, torch, hidden, weight, targets, T, H, V, steps, flops):
     st = timed(opts_stats)
     mg = timed(opts_merge)
     sl = timed(slices)
+    del ws_ex
+
+    # backward: transposes, dz pass, grad_hidden and grad_weight GEMMs
+    g = torch.linspace(-1.0, 1.0, T, dtype=torch.float32, device=dev)
+    _, lse = rlk.rlk_selected_logp(hidden, weight, targets)
+    gh = torch.empty((T, H), dtype=torch.float32, device=dev)
+    gw = torch.empty((V, H), dtype=torch.float32, device=dev)
+    ws_b = torch.empty(rlk.rlk_selected_logp_backward_workspace_bytes(T, H, V),
+                       dtype=torch.uint8, device=dev)
+
+    def backward():
+        rlk.rlk_selected_logp_backward(hidden, weight, targets, lse, g, grad_hidden=gh,
+                                       grad_weight=gw, workspace=ws_b)
+
+    bw = timed(backward)
     return {"options_tau0.7_bf16_entropy": {"gemm_stats_ms": st, "merge_ms": mg,
                                             "gemm_TFLOP/s": flops / (st * 1e-3) / 1e12},
-            "vocab_slices_4_plus_merge_ms": sl, "steps": steps}
+            "vocab_slices_4_plus_merge_ms": sl,
+            "backward": {"ms": bw, "TFLOP/s": 3 * flops / (bw * 1e-3) / 1e12,
+                         "frac_of_bf16_peak": 3 * flops / (bw * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+            "steps": steps}
 
 
 def main() -> int:

@@ -220,6 +220,56 @@ int rlk_vocab_merge_ex(const int32_t *targets, float *logp, float *lse, float *e
                        int64_t T, int64_t V, int flags, const void *workspace,
                        size_t workspace_bytes, void *stream);
 
+/* Backward of the selected-token log-probability (the training side's
+ * gradient; the vLLM blog summary's trainer differentiates the logprob it
+ * recomputes, and checks the backward on its own).  For an upstream gradient
+ * g[t] = dL/dlogp[t] of L = sum_t g[t] logp[t]:
+ *     dz[t][v]          = g[t] inv_tau (1[v == y_t] - exp(inv_tau z[t][v] - lse[t]))
+ *     grad_hidden[t][k] = sum_v dz[t][v] w[v][k]
+ *     grad_weight[v][k] = sum_t dz[t][v] h[t][k]
+ * Rows whose target lies outside [0, V) contribute nothing (dz = 0).
+ * Numerical contract:
+ *   - z is recomputed by the forward's GEMM main loop (the forward's bits);
+ *     lse is the forward's output for the same inv_temperature (plain or _ex
+ *     without RLK_LOGITS_BF16; rounded logits are not differentiated).
+ *   - dz is formed in fp32 and rounded to bf16 (nearest, ties to even): it is
+ *     the bf16 operand of the two gradient GEMMs, each accumulated in fp32
+ *     with one workgroup per output tile over the whole contraction in
+ *     increasing order (v for grad_hidden, t for grad_weight), no split, no
+ *     atomics.
+ *   - grad_hidden[t] depends only on row t: bitwise the same whatever the
+ *     batch.  grad_weight sums over the rows of the call in order: bitwise
+ *     reproducible for the same rows, and unchanged by appending rows whose
+ *     dz is zero (g = 0 or ignored targets).
+ *   hidden, weight, targets, T, H, V  as for the forward.
+ *   lse, grad_logp  fp32 [T], 4-byte aligned.
+ *   grad_hidden     fp32 [T][H] (row stride H) or NULL: not computed.
+ *   grad_weight     fp32 [V][H] (row stride H) or NULL: not computed.
+ *                   Both NULL: returns RLK_OK, launches nothing.  T == 0:
+ *                   grad_weight is set to zero.
+ *   inv_temperature finite, > 0 (RLK_ERR_INVALID_VALUE otherwise).
+ *   workspace       rlk_selected_logp_backward_workspace_bytes(T, H, V)
+ *                   bytes, 16-byte aligned: bf16 dz [T][Vp], dz^T [V][Tp],
+ *                   w^T [H][Vp] and h^T [H][Tp] with Vp, Tp = V, T rounded up
+ *                   to 64 (zero padded); about 3 * 2 V (T + H) bytes.
+ * Extra limit: V and T rounded up to 64 must not exceed 2^21
+ * (RLK_ERR_UNSUPPORTED). */
+size_t rlk_selected_logp_backward_workspace_bytes(int64_t T, int64_t H, int64_t V);
+int rlk_selected_logp_backward(const void *hidden, int64_t ld_hidden, const void *weight,
+                               int64_t ld_weight, const int32_t *targets, const float *lse,
+                               const float *grad_logp, float *grad_hidden, float *grad_weight,
+                               int64_t T, int64_t H, int64_t V, float inv_temperature,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/* The backward's first stage alone (stage comparison): the bf16 bits of dz
+ * as defined above, written to dz[t * ld_dz + v] for t < T, v < V, with
+ * columns V .. Vp-1 set to 0.  ld_dz >= V rounded up to 64, a multiple of 8;
+ * dz 16-byte aligned. */
+int rlk_logp_grad_logits(const void *hidden, int64_t ld_hidden, const void *weight,
+                         int64_t ld_weight, const int32_t *targets, const float *lse,
+                         const float *grad_logp, void *dz, int64_t ld_dz, int64_t T,
+                         int64_t H, int64_t V, float inv_temperature, void *stream);
+
 /* The logits stage alone, for stage-by-stage comparison (the RL-Kernel blog,
  * section 五: compare intermediate results to find the first divergence).
  * Runs the very same GEMM main loop as rlk_selected_logp and stores the fp32

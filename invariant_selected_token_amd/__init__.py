@@ -36,6 +36,8 @@ EXPORTED = (
     "rlk_selected_logp", "rlk_vocab_stats", "rlk_vocab_stats_shard",
     "rlk_vocab_merge", "rlk_logits", "rlk_compare", "rlk_workspace_bytes_ex",
     "rlk_selected_logp_ex", "rlk_vocab_stats_ex", "rlk_vocab_merge_ex",
+    "rlk_selected_logp_backward_workspace_bytes", "rlk_selected_logp_backward",
+    "rlk_logp_grad_logits",
 )
 
 _lib = None
@@ -98,6 +100,14 @@ def lib() -> ctypes.CDLL:
     L.rlk_vocab_stats_ex.restype = c_int
     L.rlk_vocab_merge_ex.argtypes = [vp, vp, vp, vp, i64, i64, c_int, vp, sz, vp]
     L.rlk_vocab_merge_ex.restype = c_int
+    L.rlk_selected_logp_backward_workspace_bytes.argtypes = [i64, i64, i64]
+    L.rlk_selected_logp_backward_workspace_bytes.restype = sz
+    L.rlk_selected_logp_backward.argtypes = [vp, i64, vp, i64, vp, vp, vp, vp, vp, i64, i64,
+                                             i64, f32, vp, sz, vp]
+    L.rlk_selected_logp_backward.restype = c_int
+    L.rlk_logp_grad_logits.argtypes = [vp, i64, vp, i64, vp, vp, vp, vp, i64, i64, i64, i64,
+                                       f32, vp]
+    L.rlk_logp_grad_logits.restype = c_int
     _lib = L
     return L
 
@@ -356,6 +366,69 @@ def rlk_vocab_merge_ex(targets, workspace, V, logits_bf16=False, entropy=False, 
         ent.data_ptr() if ent is not None else None, T, int(V), flags,
         workspace.data_ptr(), ws_bytes, _stream_ptr(stream, dev)))
     return logp, lse, ent
+
+
+def rlk_selected_logp_backward_workspace_bytes(T: int, H: int, V: int) -> int:
+    return int(lib().rlk_selected_logp_backward_workspace_bytes(int(T), int(H), int(V)))
+
+
+def _f32_vec(name, t, T, dev):
+    torch = _torch()
+    if t.dtype != torch.float32 or t.shape != (T,) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 [T] tensor")
+    _check_device(name, t, dev)
+    return t.data_ptr()
+
+
+def rlk_selected_logp_backward(hidden, weight, targets, lse, grad_logp, inv_temperature=1.0,
+                               want_hidden=True, want_weight=True, grad_hidden=None,
+                               grad_weight=None, workspace=None, V=None, stream=None):
+    """(grad_hidden [T, H] or None, grad_weight [V, H] or None), fp32, of
+    L = sum_t grad_logp[t] logp[t], using the forward's ``lse``."""
+    torch = _torch()
+    dev, hp, ldh, wp, ldw, T, H, V = _prepare(hidden, weight, targets, V)
+    lp_ = _f32_vec("lse", lse, T, dev)
+    gp_ = _f32_vec("grad_logp", grad_logp, T, dev)
+    if want_hidden and grad_hidden is None:
+        grad_hidden = torch.empty((T, H), dtype=torch.float32, device=dev)
+    if want_weight and grad_weight is None:
+        grad_weight = torch.empty((V, H), dtype=torch.float32, device=dev)
+    for name, t, shape in (("grad_hidden", grad_hidden if want_hidden else None, (T, H)),
+                           ("grad_weight", grad_weight if want_weight else None, (V, H))):
+        if t is not None:
+            if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous float32 {list(shape)} tensor")
+            _check_device(name, t, dev)
+    gh = grad_hidden if want_hidden else None
+    gw = grad_weight if want_weight else None
+    if workspace is None:
+        workspace = torch.empty(max(rlk_selected_logp_backward_workspace_bytes(T, H, V), 1),
+                                dtype=torch.uint8, device=dev)
+    _check_device("workspace", workspace, dev)
+    _call("rlk_selected_logp_backward", lib().rlk_selected_logp_backward(
+        hp, ldh, wp, ldw, targets.data_ptr(), lp_, gp_,
+        gh.data_ptr() if gh is not None else None, gw.data_ptr() if gw is not None else None,
+        T, H, V, float(inv_temperature), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream_ptr(stream, dev)))
+    return gh, gw
+
+
+def rlk_logp_grad_logits(hidden, weight, targets, lse, grad_logp, inv_temperature=1.0,
+                         dz=None, V=None, stream=None):
+    """bf16 dz [T, Vp] (Vp = V rounded up to 64, padding columns 0)."""
+    torch = _torch()
+    dev, hp, ldh, wp, ldw, T, H, V = _prepare(hidden, weight, targets, V)
+    Vp = (V + 63) // 64 * 64
+    if dz is None:
+        dz = torch.empty((T, Vp), dtype=torch.bfloat16, device=dev)
+    if dz.dim() != 2 or dz.shape[0] != T or dz.stride(1) != 1 or dz.element_size() != 2:
+        raise ValueError("dz must be a 2-D 16-bit [T, >= Vp] tensor with unit column stride")
+    _check_device("dz", dz, dev)
+    _call("rlk_logp_grad_logits", lib().rlk_logp_grad_logits(
+        hp, ldh, wp, ldw, targets.data_ptr(), _f32_vec("lse", lse, T, dev),
+        _f32_vec("grad_logp", grad_logp, T, dev), dz.data_ptr(), dz.stride(0), T, H, V,
+        float(inv_temperature), _stream_ptr(stream, dev)))
+    return dz
 
 
 def rlk_logits(hidden, weight, logits=None, V=None, stream=None):

@@ -95,6 +95,60 @@ int hip_status(hipError_t e) {
   return RLK_ERR_HIP;
 }
 
+// Backward: workspace layout, limits and launch helpers.
+int64_t pad64(int64_t x) { return (x + 63) / 64 * 64; }
+
+struct BwdLayout {
+  size_t dz, dzt, wt, ht, total;  // byte offsets and size
+};
+
+BwdLayout bwd_layout(int64_t T, int64_t H, int64_t V, bool want_h, bool want_w) {
+  BwdLayout L{};
+  size_t o = 0;
+  L.dz = o;
+  if (want_h) o += round_up((size_t)T * pad64(V) * 2);
+  L.dzt = o;
+  if (want_w) o += round_up((size_t)V * pad64(T) * 2);
+  L.wt = o;
+  if (want_h) o += round_up((size_t)H * pad64(V) * 2);
+  L.ht = o;
+  if (want_w) o += round_up((size_t)H * pad64(T) * 2);
+  L.total = o;
+  return L;
+}
+
+// The backward's own size limits: V and T become GEMM depths (row strides of
+// the transposed copies), so both must fit the stride limit.
+int check_backward(int64_t T, int64_t H, int64_t V, int64_t ldh, int64_t ldw,
+                   float inv_tau) {
+  int st = check_shapes(T, H, V, ldh, ldw);
+  if (st != RLK_OK) return st;
+  if (pad64(V) > MAX_LD || pad64(T) > MAX_LD) return RLK_ERR_UNSUPPORTED;
+  return check_options(inv_tau, 0);
+}
+
+rlk::GemmArgs dz_args(const void *hidden, int64_t ldh, const void *weight, int64_t ldw,
+                      const int32_t *targets, const float *lse, const float *grad, int64_t T,
+                      int64_t H, int64_t V, float inv_tau) {
+  rlk::GemmArgs g = gemm_args(hidden, ldh, weight, ldw, T, H, V);
+  g.targets = targets;
+  g.lse = lse;
+  g.grad = grad;
+  g.inv_tau = inv_tau;
+  g.ex = 3;
+  g.Vp = (int)pad64(V);
+  g.Tp = (int)pad64(T);
+  return g;
+}
+
+// out [B rows][A rows] fp32 = A . B^T over depth K (both operands K-contiguous).
+int plain_gemm(const uint16_t *A, int64_t lda, int64_t Arows, const uint16_t *B,
+               int64_t ldb, int64_t Brows, int64_t K, float *out, hipStream_t s) {
+  rlk::GemmArgs g = gemm_args(B, ldb, A, lda, Brows, K, Arows);
+  g.logits = out;
+  return hip_status(rlk::launch_gemm_logits(g, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -255,6 +309,95 @@ int rlk_selected_logp(const void *hidden, int64_t ld_hidden,
                       size_t workspace_bytes, void *stream) {
   return rlk_selected_logp_ex(hidden, ld_hidden, weight, ld_weight, targets, logp, lse,
                               nullptr, T, H, V, 1.0f, 0, workspace, workspace_bytes, stream);
+}
+
+
+// ---------------------------------------------------------------- backward --
+
+size_t rlk_selected_logp_backward_workspace_bytes(int64_t T, int64_t H, int64_t V) {
+  if (T <= 0 || H <= 0 || V <= 0 || T > MAX_ROWS || V > MAX_ROWS || H > MAX_H) return 0;
+  return bwd_layout(T, H, V, true, true).total;
+}
+
+int rlk_logp_grad_logits(const void *hidden, int64_t ld_hidden, const void *weight,
+                         int64_t ld_weight, const int32_t *targets, const float *lse,
+                         const float *grad_logp, void *dz, int64_t ld_dz, int64_t T,
+                         int64_t H, int64_t V, float inv_temperature, void *stream) {
+  int st = check_backward(T, H, V, ld_hidden, ld_weight, inv_temperature);
+  if (st != RLK_OK) return st;
+  if (ld_dz < pad64(V)) return RLK_ERR_INVALID_SHAPE;
+  if (ld_dz > MAX_LD) return RLK_ERR_UNSUPPORTED;
+  if (T == 0) return RLK_OK;
+  st = check_operands(hidden, ld_hidden, weight, ld_weight);
+  if (st != RLK_OK) return st;
+  if (!targets || !lse || !grad_logp || !dz) return RLK_ERR_NULL_POINTER;
+  if (!aligned(targets, 4) || !aligned(lse, 4) || !aligned(grad_logp, 4) || !aligned(dz, 16) ||
+      ld_dz % 8 != 0)
+    return RLK_ERR_MISALIGNED;
+  rlk::GemmArgs g = dz_args(hidden, ld_hidden, weight, ld_weight, targets, lse, grad_logp, T,
+                            H, V, inv_temperature);
+  g.dz = static_cast<uint16_t *>(dz);
+  g.ld_dz = ld_dz;
+  return hip_status(rlk::launch_gemm_stats(g, compute_units(), static_cast<hipStream_t>(stream)));
+}
+
+int rlk_selected_logp_backward(const void *hidden, int64_t ld_hidden, const void *weight,
+                               int64_t ld_weight, const int32_t *targets, const float *lse,
+                               const float *grad_logp, float *grad_hidden, float *grad_weight,
+                               int64_t T, int64_t H, int64_t V, float inv_temperature,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+  int st = check_backward(T, H, V, ld_hidden, ld_weight, inv_temperature);
+  if (st != RLK_OK) return st;
+  const bool want_h = grad_hidden != nullptr, want_w = grad_weight != nullptr;
+  if (!want_h && !want_w) return RLK_OK;
+  if ((want_h && !aligned(grad_hidden, 4)) || (want_w && !aligned(grad_weight, 4)))
+    return RLK_ERR_MISALIGNED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) {  // no rows: grad_weight is a sum over nothing
+    return want_w ? hip_status(rlk::launch_zero(grad_weight, V * H, s)) : RLK_OK;
+  }
+  st = check_operands(hidden, ld_hidden, weight, ld_weight);
+  if (st != RLK_OK) return st;
+  if (!targets || !lse || !grad_logp || !workspace) return RLK_ERR_NULL_POINTER;
+  if (!aligned(targets, 4) || !aligned(lse, 4) || !aligned(grad_logp, 4) ||
+      !aligned(workspace, 16))
+    return RLK_ERR_MISALIGNED;
+  const BwdLayout L = bwd_layout(T, H, V, want_h, want_w);
+  if (workspace_bytes < L.total) return RLK_ERR_WORKSPACE_TOO_SMALL;
+  char *ws = static_cast<char *>(workspace);
+  const int64_t Vp = pad64(V), Tp = pad64(T);
+  uint16_t *dz = reinterpret_cast<uint16_t *>(ws + L.dz);
+  uint16_t *dzt = reinterpret_cast<uint16_t *>(ws + L.dzt);
+  uint16_t *wt = reinterpret_cast<uint16_t *>(ws + L.wt);
+  uint16_t *ht = reinterpret_cast<uint16_t *>(ws + L.ht);
+  const uint16_t *h16 = static_cast<const uint16_t *>(hidden);
+  const uint16_t *w16 = static_cast<const uint16_t *>(weight);
+  // Transposed operands: the gradient GEMMs contract over V (grad_hidden)
+  // and over T (grad_weight), so those become the contiguous dimension.
+  if (want_h) {
+    st = hip_status(rlk::launch_transpose(w16, ld_weight, (int)V, (int)H, wt, Vp, s));
+    if (st != RLK_OK) return st;
+  }
+  if (want_w) {
+    st = hip_status(rlk::launch_transpose(h16, ld_hidden, (int)T, (int)H, ht, Tp, s));
+    if (st != RLK_OK) return st;
+  }
+  rlk::GemmArgs g = dz_args(hidden, ld_hidden, weight, ld_weight, targets, lse, grad_logp, T,
+                            H, V, inv_temperature);
+  g.dz = want_h ? dz : nullptr;
+  g.ld_dz = Vp;
+  g.dzt = want_w ? dzt : nullptr;
+  g.ld_dzt = Tp;
+  st = hip_status(rlk::launch_gemm_stats(g, compute_units(), s));
+  if (st != RLK_OK) return st;
+  // grad_hidden [T][H] = dz [T][Vp] . wt [H][Vp]^T
+  if (want_h) {
+    st = plain_gemm(wt, Vp, H, dz, Vp, T, Vp, grad_hidden, s);
+    if (st != RLK_OK) return st;
+  }
+  // grad_weight [V][H] = dzt [V][Tp] . ht [H][Tp]^T
+  if (want_w) st = plain_gemm(ht, Tp, H, dzt, Tp, V, Tp, grad_weight, s);
+  return st;
 }
 
 int rlk_logits(const void *hidden, int64_t ld_hidden, const void *weight,

@@ -37,8 +37,20 @@ struct GemmArgs {
   // multiplied by inv_tau and, when bf16_logits, rounded to bf16.
   float inv_tau;
   int bf16_logits;
-  // 0: plain statistics; 1: with the options; 2: options and entropy partials
+  // 0: plain statistics; 1: with the options; 2: options and entropy partials;
+  // 3: the backward's logit gradient instead of statistics
   int ex;
+  // Logit gradient (ex == 3): dz = g inv_tau (onehot(y) - exp(z inv_tau - lse))
+  // rounded to bf16, written to dz [T][ld_dz] (columns V .. Vp-1 zero) and / or
+  // dzt [V][ld_dzt] (columns T .. Tp-1 zero); either pointer may be null.
+  const float *lse;
+  const float *grad;
+  uint16_t *dz;
+  uint16_t *dzt;
+  int64_t ld_dz;
+  int64_t ld_dzt;
+  int Vp;
+  int Tp;
   int64_t ldh;
   int64_t ldw;
   int T;
@@ -72,6 +84,11 @@ inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 hipError_t launch_gemm_stats(const GemmArgs &a, int workers, hipStream_t s);
 hipError_t launch_gemm_logits(const GemmArgs &a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t s);
+// out[c][r] = in[r][c] for r < R, c < C, and 0 for R <= r < ldo (bf16 bits).
+hipError_t launch_transpose(const uint16_t *in, int64_t ldi, int R, int C, uint16_t *out,
+                            int64_t ldo, hipStream_t s);
+// x[0 .. n) = 0.0f
+hipError_t launch_zero(float *x, int64_t n, hipStream_t s);
 hipError_t launch_compare(const float *a, const float *b, int n,
                           double *stats, hipStream_t s);
 

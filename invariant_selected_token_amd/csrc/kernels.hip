@@ -343,7 +343,49 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
       // A wave whose tile starts at or past V (only in the last workgroup
       // column when V mod 256 <= 128) has nothing to write.
       const int js = 2 * n + wv;
-      if constexpr (EX > 0) {
+      if constexpr (EX == 3) {
+        // The backward's logit gradient.  The logits are the forward's bits
+        // (same main loop, same 1/tau multiply); with the forward's lse,
+        // p = exp(z' - lse) and dz = g inv_tau (1[v == y] - p), in fp32, then
+        // rounded to bf16 (nearest, ties to even) as the operand of the two
+        // gradient GEMMs.  Rows past T, columns past V and rows whose target
+        // is outside [0, V) hold 0.
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int t = t0 + wt * 128 + 32 * j + fr;
+          const bool trow = t < a.T;
+          const int y = trow ? a.targets[t] : -1;
+          const bool live = trow && y >= 0 && y < a.V;
+          const float lse_t = live ? a.lse[t] : 0.0f;
+          const float gs = live ? a.grad[t] * a.inv_tau : 0.0f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int v4 = vbase + 32 * i + 8 * q + 4 * fk;   // 4 consecutive columns
+              uint16_t b[4];
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) {
+                const int v = v4 + rr;
+                const float zs = acc[i][j][4 * q + rr] * a.inv_tau;
+                const float p = __builtin_amdgcn_exp2f((zs - lse_t) * LOG2E);
+                const float d = gs * ((v == y ? 1.0f : 0.0f) - p);
+                b[rr] = __builtin_bit_cast(uint16_t, (__bf16)((live && v < a.V) ? d : 0.0f));
+              }
+              if (a.dz && trow && v4 < a.Vp) {
+                const uint64_t packed = (uint64_t)b[0] | ((uint64_t)b[1] << 16) |
+                                        ((uint64_t)b[2] << 32) | ((uint64_t)b[3] << 48);
+                *(uint64_t *)(a.dz + (size_t)t * a.ld_dz + v4) = packed;
+              }
+              if (a.dzt && t < a.Tp) {
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                  if (v4 + rr < a.V) a.dzt[(size_t)(v4 + rr) * a.ld_dzt + t] = b[rr];
+              }
+            }
+        }
+      } else {
+      if constexpr (EX == 1 || EX == 2) {
         // The options, once per logit: one fp32 multiply (exact for
         // inv_tau == 1), then the fp32 -> bf16 cast (nearest, ties to even)
         // and back.
@@ -456,6 +498,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
         if (n == a.nVT - 1 && a.V % TILE_V != 0) stats_epilogue(std::true_type{});
         else stats_epilogue(std::false_type{});
       }
+      }  // EX != 3
     }
 
     if (Ln >= total) break;
@@ -625,7 +668,9 @@ hipError_t launch_gemm_stats(const GemmArgs &a, int workers, hipStream_t s) {
   // A multiple of 8 workgroups keeps each one on a fixed XCD.
   int grid = workers >= 8 ? workers - workers % 8 : 8;
   if (grid > tiles) grid = tiles;
-  if (a.ex == 2)
+  if (a.ex == 3)
+    hipLaunchKernelGGL((gemm_kernel<true, true, 3>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
+  else if (a.ex == 2)
     hipLaunchKernelGGL((gemm_kernel<true, true, 2>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
   else if (a.ex == 1)
     hipLaunchKernelGGL((gemm_kernel<true, true, 1>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
@@ -647,6 +692,53 @@ hipError_t launch_merge(const MergeArgs &a, hipStream_t s) {
   else
     hipLaunchKernelGGL(merge_kernel<false>, dim3(ceil_div(a.T, MERGE_ROWS)),
                        dim3(MERGE_GROUPS * MERGE_ROWS), 0, s, a);
+  return hipGetLastError();
+}
+
+// 64 x 64 tiles through LDS: reads along input rows and writes along output
+// rows are both contiguous across a wave.
+constexpr int TR_TILE = 64;
+__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t *__restrict__ in,
+                                                        int64_t ldi, int R, int C,
+                                                        uint16_t *__restrict__ out,
+                                                        int64_t ldo) {
+  __shared__ uint16_t tile[TR_TILE][TR_TILE + 2];
+  const int r0 = blockIdx.x * TR_TILE;   // output columns (the long side) in x
+  const int c0 = blockIdx.y * TR_TILE;
+  const int x = threadIdx.x & 63, y0 = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < TR_TILE / 4; ++k) {
+    const int yy = y0 * (TR_TILE / 4) + k;
+    const int r = r0 + yy, c = c0 + x;
+    tile[yy][x] = (r < R && c < C) ? in[(size_t)r * ldi + c] : (uint16_t)0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < TR_TILE / 4; ++k) {
+    const int yy = y0 * (TR_TILE / 4) + k;
+    const int c = c0 + yy, r = r0 + x;
+    if (c < C && r < ldo) out[(size_t)c * ldo + r] = tile[x][yy];
+  }
+}
+
+hipError_t launch_transpose(const uint16_t *in, int64_t ldi, int R, int C, uint16_t *out,
+                            int64_t ldo, hipStream_t s) {
+  hipLaunchKernelGGL(transpose_kernel, dim3(ceil_div(ldo, TR_TILE), ceil_div(C, TR_TILE)),
+                     dim3(256), 0, s, in, ldi, R, C, out, ldo);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(float *x, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    x[i] = 0.0f;
+}
+
+hipError_t launch_zero(float *x, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256),
+                     0, s, x, n);
   return hipGetLastError();
 }
 
