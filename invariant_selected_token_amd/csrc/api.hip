@@ -146,7 +146,7 @@ int plain_gemm(const uint16_t *A, int64_t lda, int64_t Arows, const uint16_t *B,
                int64_t ldb, int64_t Brows, int64_t K, float *out, hipStream_t s) {
   rlk::GemmArgs g = gemm_args(B, ldb, A, lda, Brows, K, Arows);
   g.logits = out;
-  return hip_status(rlk::launch_gemm_logits(g, s));
+  return hip_status(rlk::launch_gemm_logits(g, compute_units(), s));
 }
 
 }  // namespace
@@ -412,7 +412,7 @@ int rlk_logits(const void *hidden, int64_t ld_hidden, const void *weight,
   if (!aligned(logits, 4)) return RLK_ERR_MISALIGNED;
   rlk::GemmArgs g = gemm_args(hidden, ld_hidden, weight, ld_weight, T, H, V);
   g.logits = logits;
-  return hip_status(rlk::launch_gemm_logits(g, static_cast<hipStream_t>(stream)));
+  return hip_status(rlk::launch_gemm_logits(g, compute_units(), static_cast<hipStream_t>(stream)));
 }
 
 int rlk_compare(const float *a, const float *b, int64_t n, double *stats,

@@ -82,9 +82,10 @@ inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 // `workers`: workgroups of the persistent statistics kernel (the device's
 // compute-unit count); it changes the schedule, never the results.
 hipError_t launch_gemm_stats(const GemmArgs &a, int workers, hipStream_t s);
-hipError_t launch_gemm_logits(const GemmArgs &a, hipStream_t s);
+hipError_t launch_gemm_logits(const GemmArgs &a, int workers, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t s);
-// out[c][r] = in[r][c] for r < R, c < C, and 0 for R <= r < ldo (bf16 bits).
+// out[c][r] = in[r][c] for r < R, c < C, and 0 for R <= r < ldo (bf16 bits);
+// C % 64 == 0, ldi % 8 == 0, ldo % 64 == 0, 16-byte aligned pointers.
 hipError_t launch_transpose(const uint16_t *in, int64_t ldi, int R, int C, uint16_t *out,
                             int64_t ldo, hipStream_t s);
 // x[0 .. n) = 0.0f

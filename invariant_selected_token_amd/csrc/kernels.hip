@@ -323,6 +323,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     const int t0 = m * TILE_T;
     const int vbase = v0 + wv * 128;
     if (!STATS) {
+      // Registers 4q .. 4q+3 hold four consecutive columns: one 16-byte
+      // store per lane when rows are 16-byte aligned (the two lane halves
+      // cover 32 contiguous bytes of a row), else element by element.
+      const bool vec = (a.V & 3) == 0 && ((uintptr_t)a.logits & 15) == 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int t = t0 + wt * 128 + 32 * j + fr;
@@ -331,9 +335,20 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int v = vbase + 32 * i + 8 * (r >> 2) + 4 * fk + (r & 3);
-            if (v < a.V) row[v] = acc[i][j][r];
+          for (int q = 0; q < 4; ++q) {
+            const int v4 = vbase + 32 * i + 8 * q + 4 * fk;
+            if (vec && v4 + 3 < a.V) {
+              float4 x;
+              x.x = acc[i][j][4 * q];
+              x.y = acc[i][j][4 * q + 1];
+              x.z = acc[i][j][4 * q + 2];
+              x.w = acc[i][j][4 * q + 3];
+              *(float4 *)(row + v4) = x;
+            } else {
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr)
+                if (v4 + rr < a.V) row[v4 + rr] = acc[i][j][4 * q + rr];
+            }
           }
       }
     } else {
@@ -377,10 +392,23 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
                                         ((uint64_t)b[2] << 32) | ((uint64_t)b[3] << 48);
                 *(uint64_t *)(a.dz + (size_t)t * a.ld_dz + v4) = packed;
               }
-              if (a.dzt && t < a.Tp) {
+              if (a.dzt) {
+                // dz^T rows are contiguous in t, i.e. across lanes.  Lanes
+                // fr and fr ^ 1 swap values so that each writes one aligned
+                // pair (t even, t + 1): the even lane the pair of column
+                // v4 + rr, the odd lane that of v4 + rr + 1.
+                const bool odd = fr & 1;
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr)
-                  if (v4 + rr < a.V) a.dzt[(size_t)(v4 + rr) * a.ld_dzt + t] = b[rr];
+                for (int rr = 0; rr < 4; rr += 2) {
+                  const uint32_t mine = odd ? b[rr + 1] : b[rr];
+                  const uint32_t give = odd ? b[rr] : b[rr + 1];
+                  const uint32_t got = (uint32_t)__shfl_xor((int)give, 1);
+                  const int v = v4 + rr + (odd ? 1 : 0);
+                  const int te = t & ~1;
+                  const uint32_t pair = odd ? (got | (mine << 16)) : (mine | (got << 16));
+                  if (te < a.Tp && v < a.V)
+                    *(uint32_t *)(a.dzt + (size_t)v * a.ld_dzt + te) = pair;
+                }
               }
             }
         }
@@ -679,9 +707,11 @@ hipError_t launch_gemm_stats(const GemmArgs &a, int workers, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_logits(const GemmArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_kernel<false, false, 0>), dim3(a.nMT * a.nVT), dim3(GEMM_THREADS),
-                     0, s, a);
+hipError_t launch_gemm_logits(const GemmArgs &a, int workers, hipStream_t s) {
+  const int tiles = a.nMT * a.nVT;
+  int grid = workers >= 8 ? workers - workers % 8 : 8;
+  if (grid > tiles) grid = tiles;
+  hipLaunchKernelGGL((gemm_kernel<false, true, 0>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
   return hipGetLastError();
 }
 
@@ -695,29 +725,41 @@ hipError_t launch_merge(const MergeArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// 64 x 64 tiles through LDS: reads along input rows and writes along output
-// rows are both contiguous across a wave.
+// 64 x 64 tiles through LDS, moved as 16-byte chunks of 8 elements: a
+// thread reads 8 consecutive columns of one input row and writes 8
+// consecutive columns (input rows) of one output row.  Requires C % 64 == 0,
+// ldi % 8 == 0 and ldo % 64 == 0 (checked by the caller).
 constexpr int TR_TILE = 64;
+constexpr int TR_PITCH = TR_TILE + 8;   // LDS row pitch in elements (16-byte aligned)
 __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t *__restrict__ in,
                                                         int64_t ldi, int R, int C,
                                                         uint16_t *__restrict__ out,
                                                         int64_t ldo) {
-  __shared__ uint16_t tile[TR_TILE][TR_TILE + 2];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[TR_TILE][TR_PITCH];
   const int r0 = blockIdx.x * TR_TILE;   // output columns (the long side) in x
   const int c0 = blockIdx.y * TR_TILE;
-  const int x = threadIdx.x & 63, y0 = threadIdx.x >> 6;
+  const int chunk = threadIdx.x & 7, y0 = threadIdx.x >> 3;   // 32 rows x 8 chunks
 #pragma unroll
-  for (int k = 0; k < TR_TILE / 4; ++k) {
-    const int yy = y0 * (TR_TILE / 4) + k;
-    const int r = r0 + yy, c = c0 + x;
-    tile[yy][x] = (r < R && c < C) ? in[(size_t)r * ldi + c] : (uint16_t)0;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int rr = y0 + 32 * pass;
+    const int r = r0 + rr;
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (r < R) x = *(const uint4 *)(in + (size_t)r * ldi + c0 + 8 * chunk);
+    *(uint4 *)&tile[rr][8 * chunk] = x;
   }
   __syncthreads();
 #pragma unroll
-  for (int k = 0; k < TR_TILE / 4; ++k) {
-    const int yy = y0 * (TR_TILE / 4) + k;
-    const int c = c0 + yy, r = r0 + x;
-    if (c < C && r < ldo) out[(size_t)c * ldo + r] = tile[x][yy];
+  for (int pass = 0; pass < 2; ++pass) {
+    const int cc = y0 + 32 * pass;       // output row c0 + cc
+    uint16_t e[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) e[k] = tile[8 * chunk + k][cc];
+    uint4 x;
+    x.x = e[0] | ((uint32_t)e[1] << 16);
+    x.y = e[2] | ((uint32_t)e[3] << 16);
+    x.z = e[4] | ((uint32_t)e[5] << 16);
+    x.w = e[6] | ((uint32_t)e[7] << 16);
+    if (r0 + 8 * chunk < ldo) *(uint4 *)(out + (size_t)(c0 + cc) * ldo + r0 + 8 * chunk) = x;
   }
 }
 
