@@ -67,6 +67,15 @@
  *     like an ignored index.  The training side of the vLLM blog summary
  *     differentiates the logprob it recomputes in a graph; the backward is
  *     verified on its own (its C7 check).
+ *   - RMSNorm feeding the LM head (oracle_rmsnorm): the RL-Kernel blog
+ *     (section 四) puts RMSNorm among the reductions whose result depends on
+ *     the order of accumulation over the hidden dimension, and its H100
+ *     recipe (section 六) switches to torch's RMSNorm for one normalisation
+ *     semantics.  The model's convention, taken here: per row
+ *     r = 1 / sqrt(mean_k x_k^2 + eps), y_k = bf16(bf16(x_k r) gamma_k);
+ *     the first rounding is decided on x_k r as an fp32 value (fp64 -> fp32
+ *     -> bf16, the precision the normalisation runs in), the second on the
+ *     product of two bf16 values, which is exact.
  *   - Entropy of softmax(z'): H = -sum_v p_v log p_v with
  *     p_v = exp(z'_v - lse), terms with p_v = 0 contributing 0; NaN when the
  *     row's lse is not finite.  (The vLLM blog summary lists entropy among the
@@ -80,7 +89,7 @@
 #include <omp.h>
 #endif
 
-#define ORACLE_VERSION 3
+#define ORACLE_VERSION 4
 
 int oracle_version(void) { return ORACLE_VERSION; }
 
@@ -465,4 +474,37 @@ int oracle_selected_logp_backward(const uint16_t *hidden, int64_t ldh,
     }
     free(dz);
     return 0;
+}
+
+/* bf16 value -> bit pattern (the value is a bf16 value or an infinity / NaN). */
+static uint16_t f64_to_bf16_bits(double x) {
+    const float f = (float)x;              /* exact: x is a bf16 value */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if (isnan(x)) u = 0x7FC00000u;
+    return (uint16_t)(u >> 16);
+}
+
+/* RMSNorm of T rows of x (bf16 [T][ldx], first H columns) with weight gamma
+ * (bf16 [H]): out bf16 bits [T][H]; xr (optional, fp64 [T][H]) receives the
+ * unrounded x_k r.  Per row: ms = sum_k x_k^2 / H in fp64 (increasing k),
+ * r = 1 / sqrt(ms + eps). */
+void oracle_rmsnorm(const uint16_t *x, int64_t ldx, const uint16_t *gamma, double eps,
+                    int64_t T, int64_t H, uint16_t *out, double *xr) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t *row = x + t * ldx;
+        double ss = 0.0;
+        for (int64_t k = 0; k < H; ++k) {
+            const double v = bf16_to_f64(row[k]);
+            ss = ss + v * v;
+        }
+        const double r = 1.0 / sqrt(ss / (double)H + eps);
+        for (int64_t k = 0; k < H; ++k) {
+            const double a = bf16_to_f64(row[k]) * r;
+            if (xr) xr[t * H + k] = a;
+            const double n = round_bf16(to_f32(a));
+            out[t * H + k] = f64_to_bf16_bits(round_bf16(n * bf16_to_f64(gamma[k])));
+        }
+    }
 }

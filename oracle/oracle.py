@@ -77,6 +77,8 @@ def _load():
     lib.oracle_selected_logp_backward.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64,
                                                   ctypes.c_double, vp, vp, c_int]
     lib.oracle_selected_logp_backward.restype = c_int
+    lib.oracle_rmsnorm.argtypes = [vp, i64, vp, ctypes.c_double, i64, i64, vp, vp]
+    lib.oracle_rmsnorm.restype = None
     _lib = lib
     return lib
 
@@ -258,6 +260,23 @@ def selected_logp_backward(hidden, weight, targets, grad_logp, inv_tau: float = 
                                          _ptr(gw) if gw is not None else None, nthreads):
         raise MemoryError("oracle_selected_logp_backward failed")
     return gh, gw
+
+
+def rmsnorm(x, gamma, eps: float = 1e-6, want_xr: bool = False):
+    """bf16 bits [T, H] of y = bf16(bf16(x r) gamma), r = 1/sqrt(mean(x^2) + eps)
+    per row (fp64 arithmetic, roundings as the module doc states); with
+    ``want_xr`` also the unrounded x r (fp64)."""
+    lib = _load()
+    xb = _bf16_2d(x)
+    T, H = xb.shape
+    g = np.ascontiguousarray(gamma)
+    if g.dtype != np.uint16 or g.shape != (H,):
+        raise TypeError("gamma must be a uint16 [H] array of bfloat16 bit patterns")
+    out = np.empty((T, H), dtype=np.uint16)
+    xr = np.empty((T, H), dtype=np.float64) if want_xr else None
+    lib.oracle_rmsnorm(_ptr(xb), H, _ptr(g), float(eps), T, H, _ptr(out),
+                       _ptr(xr) if xr is not None else None)
+    return (out, xr) if want_xr else out
 
 
 def sample_targets(log_probs: np.ndarray, u: np.ndarray) -> np.ndarray:
