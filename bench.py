@@ -133,7 +133,21 @@ def time_variants(rlk, torch, hidden, weight, targets, T, H, V, steps, flops):
                                        grad_weight=gw, workspace=ws_b)
 
     bw = timed(backward)
-    return {"options_tau0.7_bf16_entropy": {"gemm_stats_ms": st, "merge_ms": mg,
+    del ws_b, gw
+
+    # RMSNorm feeding the LM head, on the same [T, H] shape (HBM-bound)
+    gamma = torch.ones(H, dtype=torch.bfloat16, device=dev)
+    xn = torch.empty_like(hidden)
+
+    def rmsnorm():
+        rlk.rlk_rmsnorm(hidden, gamma, 1e-6, y=xn)
+
+    rn = timed(rmsnorm)
+    rn_bytes = 2.0 * T * H * 2 + 2.0 * H
+    return {
+            "rmsnorm": {"ms": rn, "GB/s": rn_bytes / (rn * 1e-3) / 1e9,
+                        "frac_of_hbm_peak": rn_bytes / (rn * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                        "bytes": rn_bytes},"options_tau0.7_bf16_entropy": {"gemm_stats_ms": st, "merge_ms": mg,
                                             "gemm_TFLOP/s": flops / (st * 1e-3) / 1e12},
             "vocab_slices_4_plus_merge_ms": sl,
             "backward": {"ms": bw, "TFLOP/s": 3 * flops / (bw * 1e-3) / 1e12,

@@ -270,6 +270,24 @@ int rlk_logp_grad_logits(const void *hidden, int64_t ld_hidden, const void *weig
                          const float *grad_logp, void *dz, int64_t ld_dz, int64_t T,
                          int64_t H, int64_t V, float inv_temperature, void *stream);
 
+/* RMSNorm feeding the LM head: the final normalisation whose output is the
+ * `hidden` of rlk_selected_logp.  The RL-Kernel blog (section 四) lists RMSNorm
+ * among the reductions whose result depends on the order of accumulation
+ * over the hidden dimension, and its H100 recipe (section 六) fixes one
+ * normalisation semantics.  Per row t:
+ *     r    = 1 / sqrt(sum_k x[t][k]^2 / H + eps)        (fp32)
+ *     y[k] = bf16( bf16(x[t][k] * r) * gamma[k] )       (nearest, ties to even)
+ * The sum of squares runs in an order fixed by H alone (one wave per row:
+ * lane l takes the 8-element chunks l, l+64, ..., in element order, then a
+ * butterfly over the 64 lanes), so a row's output is bitwise the same
+ * whatever the batch.
+ *   x      bf16 [T][ld_x], y bf16 [T][ld_y] (may not alias x), gamma bf16 [H];
+ *          16-byte aligned, ld_x, ld_y >= H and multiples of 8.
+ *   H      a multiple of 8 (RLK_ERR_UNSUPPORTED otherwise).
+ *   eps    finite, >= 0 (Qwen3: 1e-6); RLK_ERR_INVALID_VALUE otherwise. */
+int rlk_rmsnorm(const void *x, int64_t ld_x, const void *gamma, float eps, void *y,
+                int64_t ld_y, int64_t T, int64_t H, void *stream);
+
 /* The logits stage alone, for stage-by-stage comparison (the RL-Kernel blog,
  * section 五: compare intermediate results to find the first divergence).
  * Runs the very same GEMM main loop as rlk_selected_logp and stores the fp32

@@ -37,7 +37,7 @@ EXPORTED = (
     "rlk_vocab_merge", "rlk_logits", "rlk_compare", "rlk_workspace_bytes_ex",
     "rlk_selected_logp_ex", "rlk_vocab_stats_ex", "rlk_vocab_merge_ex",
     "rlk_selected_logp_backward_workspace_bytes", "rlk_selected_logp_backward",
-    "rlk_logp_grad_logits",
+    "rlk_logp_grad_logits", "rlk_rmsnorm",
 )
 
 _lib = None
@@ -108,6 +108,8 @@ def lib() -> ctypes.CDLL:
     L.rlk_logp_grad_logits.argtypes = [vp, i64, vp, i64, vp, vp, vp, vp, i64, i64, i64, i64,
                                        f32, vp]
     L.rlk_logp_grad_logits.restype = c_int
+    L.rlk_rmsnorm.argtypes = [vp, i64, vp, f32, vp, i64, i64, i64, vp]
+    L.rlk_rmsnorm.restype = c_int
     _lib = L
     return L
 
@@ -429,6 +431,25 @@ def rlk_logp_grad_logits(hidden, weight, targets, lse, grad_logp, inv_temperatur
         _f32_vec("grad_logp", grad_logp, T, dev), dz.data_ptr(), dz.stride(0), T, H, V,
         float(inv_temperature), _stream_ptr(stream, dev)))
     return dz
+
+
+def rlk_rmsnorm(x, gamma, eps=1e-6, y=None, stream=None):
+    """bf16 y [T, H] = RMSNorm(x) * gamma (the LM head's input)."""
+    torch = _torch()
+    dev = x.device
+    xp, ldx = _bf16_operand("x", x, dev)
+    T, H = x.shape
+    if gamma.dim() != 1 or gamma.shape[0] != H or not gamma.is_contiguous():
+        raise ValueError("gamma must be a contiguous [H] tensor")
+    gp, _ = _bf16_operand("gamma", gamma.view(1, H), dev)
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    yp, ldy = _bf16_operand("y", y, dev)
+    if tuple(y.shape) != (T, H):
+        raise ValueError("y must have shape [T, H]")
+    _call("rlk_rmsnorm", lib().rlk_rmsnorm(xp, ldx, gp, float(eps), yp, ldy, T, H,
+                                           _stream_ptr(stream, dev)))
+    return y
 
 
 def rlk_logits(hidden, weight, logits=None, V=None, stream=None):

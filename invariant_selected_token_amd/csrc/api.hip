@@ -400,6 +400,22 @@ int rlk_selected_logp_backward(const void *hidden, int64_t ld_hidden, const void
   return st;
 }
 
+int rlk_rmsnorm(const void *x, int64_t ld_x, const void *gamma, float eps, void *y,
+                int64_t ld_y, int64_t T, int64_t H, void *stream) {
+  if (T < 0 || H <= 0 || ld_x < H || ld_y < H) return RLK_ERR_INVALID_SHAPE;
+  if (H % 8 != 0 || T > MAX_ROWS || ld_x > MAX_LD || ld_y > MAX_LD) return RLK_ERR_UNSUPPORTED;
+  if (!(eps >= 0.0f) || !(eps <= 3.402823466e38f)) return RLK_ERR_INVALID_VALUE;
+  if (T == 0) return RLK_OK;
+  if (!x || !gamma || !y) return RLK_ERR_NULL_POINTER;
+  if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(y, 16) || ld_x % 8 != 0 ||
+      ld_y % 8 != 0)
+    return RLK_ERR_MISALIGNED;
+  return hip_status(rlk::launch_rmsnorm(static_cast<const uint16_t *>(x), ld_x,
+                                        static_cast<const uint16_t *>(gamma), eps,
+                                        static_cast<uint16_t *>(y), ld_y, (int)T, (int)H,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 int rlk_logits(const void *hidden, int64_t ld_hidden, const void *weight,
                int64_t ld_weight, float *logits, int64_t T, int64_t H,
                int64_t V, void *stream) {

@@ -88,6 +88,10 @@ hipError_t launch_merge(const MergeArgs &a, hipStream_t s);
 // C % 64 == 0, ldi % 8 == 0, ldo % 64 == 0, 16-byte aligned pointers.
 hipError_t launch_transpose(const uint16_t *in, int64_t ldi, int R, int C, uint16_t *out,
                             int64_t ldo, hipStream_t s);
+// RMSNorm of T rows (bf16 [T][ldx]) with weight gamma (bf16 [H]) into y; H % 8
+// == 0, ldx and ldy multiples of 8, 16-byte aligned pointers.
+hipError_t launch_rmsnorm(const uint16_t *x, int64_t ldx, const uint16_t *gamma, float eps,
+                          uint16_t *y, int64_t ldy, int T, int H, hipStream_t s);
 // x[0 .. n) = 0.0f
 hipError_t launch_zero(float *x, int64_t n, hipStream_t s);
 hipError_t launch_compare(const float *a, const float *b, int n,

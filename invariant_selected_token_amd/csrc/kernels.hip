@@ -23,6 +23,10 @@
 // sections 二/四 name that cast as a drift point) before the statistics and
 // the target capture; with EX == 2 each tile also yields
 // u = sum exp(z - m) (z - m), from which the merge forms the entropy.
+//   rmsnorm_kernel      the RMSNorm feeding the LM head, one wave per row with
+//                       a fixed reduction order over the hidden dimension
+//                       (section 四 lists RMSNorm among the reductions whose
+//                       order matters).
 //   compare_kernel      mismatch count / max |diff| / k3 of two fp32 arrays
 //                       (sections 六/七; the vLLM blog summary's diff = 0).
 //
@@ -767,6 +771,66 @@ hipError_t launch_transpose(const uint16_t *in, int64_t ldi, int R, int C, uint1
                             int64_t ldo, hipStream_t s) {
   hipLaunchKernelGGL(transpose_kernel, dim3(ceil_div(ldo, TR_TILE), ceil_div(C, TR_TILE)),
                      dim3(256), 0, s, in, ldi, R, C, out, ldo);
+  return hipGetLastError();
+}
+
+// RMSNorm, one wave per row, RMS_ROWS rows per workgroup.  Lane l owns the
+// 16-byte chunks l, l + 64, l + 128, ... of the row; it sums their squares in
+// element order, then the lanes combine in a butterfly (xor 32, 16, .., 1):
+// partners add the same two numbers, so every lane ends with the same total,
+// whose association depends only on H.  r = 1 / sqrt(ss / H + eps) with IEEE
+// square root and division; y = bf16(bf16(x r) gamma), where the second
+// product, of two bf16 values, is exact in fp32.
+constexpr int RMS_ROWS = 4;
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+__global__ __launch_bounds__(64 * RMS_ROWS) void rmsnorm_kernel(
+    const uint16_t *__restrict__ x, int64_t ldx, const uint16_t *__restrict__ gamma, float eps,
+    uint16_t *__restrict__ y, int64_t ldy, int T, int H) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * RMS_ROWS + (threadIdx.x >> 6);
+  if (t >= T) return;                      // a whole wave
+  const uint16_t *row = x + (size_t)t * ldx;
+  const int nch = H >> 3;
+  float ss = 0.0f;
+  for (int c = lane; c < nch; c += 64) {
+    const uint4 v = *(const uint4 *)(row + 8 * c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float a = bf16_lo(w[k]), b = bf16_hi(w[k]);
+      ss = ss + a * a;
+      ss = ss + b * b;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss = ss + __shfl_xor(ss, o);
+  const float r = 1.0f / sqrtf(ss / (float)H + eps);
+  uint16_t *out = y + (size_t)t * ldy;
+  for (int c = lane; c < nch; c += 64) {
+    const uint4 v = *(const uint4 *)(row + 8 * c);
+    const uint4 g = *(const uint4 *)(gamma + 8 * c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float n0 = bf16_lo(bf16_bits(bf16_lo(w[k]) * r));
+      const float n1 = bf16_lo(bf16_bits(bf16_hi(w[k]) * r));
+      o[k] = bf16_bits(n0 * bf16_lo(gw[k])) | (bf16_bits(n1 * bf16_hi(gw[k])) << 16);
+    }
+    *(uint4 *)(out + 8 * c) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+hipError_t launch_rmsnorm(const uint16_t *x, int64_t ldx, const uint16_t *gamma, float eps,
+                          uint16_t *y, int64_t ldy, int T, int H, hipStream_t s) {
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(ceil_div(T, RMS_ROWS)), dim3(64 * RMS_ROWS), 0, s, x,
+                     ldx, gamma, eps, y, ldy, T, H);
   return hipGetLastError();
 }
 

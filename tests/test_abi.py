@@ -430,3 +430,29 @@ def test_grad_logits_error_paths(kw, status):
                                           a["targets"], a["lse"], a["grad"], a["dz"],
                                           a["ld_dz"], a["T"], a["H"], a["V"], a["inv_tau"],
                                           None) == status
+
+
+# ---------------------------------------------------------------- rmsnorm --
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), rlk.RLK_ERR_INVALID_SHAPE),
+    (dict(H=0), rlk.RLK_ERR_INVALID_SHAPE),
+    (dict(ldx=56), rlk.RLK_ERR_INVALID_SHAPE),
+    (dict(ldy=56), rlk.RLK_ERR_INVALID_SHAPE),
+    (dict(H=60, ldx=64, ldy=64), rlk.RLK_ERR_UNSUPPORTED),
+    (dict(eps=-1.0), rlk.RLK_ERR_INVALID_VALUE),
+    (dict(eps=float("nan")), rlk.RLK_ERR_INVALID_VALUE),
+    (dict(eps=float("inf")), rlk.RLK_ERR_INVALID_VALUE),
+    (dict(x=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(gamma=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(y=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(x=FAKE + 8), rlk.RLK_ERR_MISALIGNED),
+    (dict(gamma=FAKE + 4), rlk.RLK_ERR_MISALIGNED),
+    (dict(ldy=68), rlk.RLK_ERR_MISALIGNED),
+    (dict(T=0, x=None, gamma=None, y=None), rlk.RLK_OK),
+])
+def test_rmsnorm_error_paths(kw, status):
+    a = dict(x=FAKE, ldx=64, gamma=FAKE, eps=1e-6, y=FAKE, ldy=64, T=4, H=64)
+    a.update(kw)
+    assert rlk.lib().rlk_rmsnorm(a["x"], a["ldx"], a["gamma"], a["eps"], a["y"], a["ldy"],
+                                 a["T"], a["H"], None) == status
