@@ -144,7 +144,22 @@ def time_variants(rlk, torch, hidden, weight, targets, T, H, V, steps, flops):
 
     rn = timed(rmsnorm)
     rn_bytes = 2.0 * T * H * 2 + 2.0 * H
+
+    # decode batches: the whole head is streamed for a handful of rows
+    decode = {}
+    for B in (1, 16, 64, 256):
+        hb, yb = hidden[:B].contiguous(), targets[:B].contiguous()
+        lpb = torch.empty(B, dtype=torch.float32, device=dev)
+        lseb = torch.empty_like(lpb)
+        wsb = rlk.workspace_for(B, V, dev)
+
+        def dec():
+            rlk.rlk_selected_logp(hb, weight, yb, logp=lpb, lse=lseb, workspace=wsb)
+
+        ms = timed(dec)
+        decode[f"B={B}"] = {"ms": ms, "weight_GB/s": 2.0 * V * H / (ms * 1e-3) / 1e9}
     return {
+            "decode": decode,
             "rmsnorm": {"ms": rn, "GB/s": rn_bytes / (rn * 1e-3) / 1e9,
                         "frac_of_hbm_peak": rn_bytes / (rn * 1e-3) / 1e9 / PEAK_HBM_GBS,
                         "bytes": rn_bytes},"options_tau0.7_bf16_entropy": {"gemm_stats_ms": st, "merge_ms": mg,
