@@ -265,3 +265,18 @@ def test_long_rollout_softmax_targets(rollout, dev):
     _assert_close(lp[rows], ref_lp, "rollout logp")
     _assert_close(lse[rows], ref_lse, "rollout lse")
     assert np.all(np.isfinite(lp)) and np.all(lp <= 0.0)
+
+
+@pytest.mark.parametrize("T,H,V", [(3, 65536, 300), (4, 64, 1_000_003), (70_000, 64, 300)])
+def test_maximum_sizes(dev, T, H, V):
+    """The limits of the contract: H at its maximum (1024 K blocks), a vocabulary
+    of a million rows (7813 statistics tiles, ragged last tile), 70 000 rows
+    (274 token tiles); every row against the oracle, targets including 0 and
+    V - 1."""
+    c = synth.normal_case(f"max_{T}x{H}x{V}", 880 + T % 97, T, H, V)
+    y = c.targets.copy()
+    y[0], y[-1] = 0, V - 1
+    lp, lse = _run(to_dev_bf16(c.hidden, dev), to_dev_bf16(c.weight, dev), to_dev_i32(y, dev))
+    ref_lp, ref_lse = orc.selected_logp(c.hidden, c.weight, y)
+    _assert_close(lp, ref_lp, f"logp {T}x{H}x{V}")
+    _assert_close(lse, ref_lse, f"lse {T}x{H}x{V}")
