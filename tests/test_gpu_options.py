@@ -274,3 +274,13 @@ def test_options_vocab_slices_merge_to_unsliced_bits(prefill):
     part = rlk.rlk_vocab_merge_ex(prefill.targets, ws, V, logits_bf16=True, entropy=True)
     for a, b in zip(full, part):
         assert torch.equal(_bits(a), _bits(b))
+
+
+@pytest.mark.parametrize("rows", [1, 16, 32, 33, 200, 256])
+def test_options_small_batches_match_the_full_batch(prefill, rows):
+    """Decode-size batches (one token tile, mostly padding) against the same
+    rows inside the 4096-row batch: same bits, options on."""
+    full = _ex(prefill.hidden, prefill.weight, prefill.targets, 0.7, True, True)
+    part = _ex(prefill.hidden[:rows], prefill.weight, prefill.targets[:rows], 0.7, True, True)
+    for a, b in zip(full, part):
+        assert torch.equal(_bits(a[:rows]), _bits(b))
