@@ -240,3 +240,26 @@ def test_vocab_slices_on_two_streams(tiny):
     s_lp, s_lse = rlk.rlk_vocab_merge(tiny.targets, ws, V)
     _assert_bits_equal(s_lp, lp, "two-stream slices logp")
     _assert_bits_equal(s_lse, lse, "two-stream slices lse")
+
+
+@pytest.mark.parametrize("H", [192, 4096])
+def test_odd_block_count_and_zero_rows_batch_invariant(dev, H):
+    """1024 rows (280 tiles over 70 columns of 256: more than one round of
+    the persistent grid) against four 256-row calls.  H = 192 has an odd
+    number of 64-deep K blocks (a phantom zero block is appended), and rows of
+    zeros make logits of exactly 0, whose sign must agree too."""
+    T, V = 1024, 256 * 70 - 37
+    c = synth.normal_case(f"tail_{H}", 990 + H, T, H, V)
+    hid = c.hidden.copy()
+    hid[[5, 300, 777, 1023]] = 0
+    h, w, y = to_dev_bf16(hid, dev), to_dev_bf16(c.weight, dev), to_dev_i32(c.targets, dev)
+    lp, lse = rlk.rlk_selected_logp(h, w, y)
+    for s in range(4):
+        sl = slice(256 * s, 256 * (s + 1))
+        a, b = rlk.rlk_selected_logp(h[sl], w, y[sl])
+        _assert_bits_equal(a, lp[sl], f"H={H} logp rows {sl}")
+        _assert_bits_equal(b, lse[sl], f"H={H} lse rows {sl}")
+    _, _, e_full = rlk.rlk_selected_logp_ex(h, w, y, inv_temperature=0.8, entropy=True)
+    _, _, e_part = rlk.rlk_selected_logp_ex(h[:256], w, y[:256], inv_temperature=0.8,
+                                            entropy=True)
+    _assert_bits_equal(e_part, e_full[:256], f"H={H} entropy")
