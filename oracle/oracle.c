@@ -76,6 +76,11 @@
  *     the first rounding is decided on x_k r as an fp32 value (fp64 -> fp32
  *     -> bf16, the precision the normalisation runs in), the second on the
  *     product of two bf16 values, which is exact.
+ *   - Top-k log-probabilities (oracle_topk_logp): the k entries of
+ *     log softmax(z') with the largest values, in decreasing order, ties
+ *     broken by the smaller token id; NaN entries are never selected.  The
+ *     vLLM blog summary counts them among the per-token outputs an RL step
+ *     reads (its logprob outputs).
  *   - Entropy of softmax(z'): H = -sum_v p_v log p_v with
  *     p_v = exp(z'_v - lse), terms with p_v = 0 contributing 0; NaN when the
  *     row's lse is not finite.  (The vLLM blog summary lists entropy among the
@@ -89,7 +94,7 @@
 #include <omp.h>
 #endif
 
-#define ORACLE_VERSION 4
+#define ORACLE_VERSION 5
 
 int oracle_version(void) { return ORACLE_VERSION; }
 
@@ -507,4 +512,82 @@ void oracle_rmsnorm(const uint16_t *x, int64_t ldx, const uint16_t *gamma, doubl
             out[t * H + k] = f64_to_bf16_bits(round_bf16(n * bf16_to_f64(gamma[k])));
         }
     }
+}
+
+/* Top-k of one row of (transformed) logits by repeated selection of the
+ * largest remaining entry under the order (value descending, id ascending).
+ * Entries that are NaN are skipped; when fewer than k entries remain, the
+ * tail gets id -1 and value -inf. */
+static void row_topk(const double *z, int64_t V, int k, double lse, double *out_lp,
+                     int32_t *out_id, unsigned char *taken) {
+    memset(taken, 0, (size_t)V);
+    for (int q = 0; q < k; ++q) {
+        int64_t best = -1;
+        for (int64_t v = 0; v < V; ++v) {
+            if (taken[v] || isnan(z[v])) continue;
+            if (best < 0 || z[v] > z[best]) best = v;
+        }
+        if (best < 0) {
+            out_lp[q] = -INFINITY;
+            out_id[q] = -1;
+            continue;
+        }
+        taken[best] = 1;
+        out_lp[q] = z[best] - lse;
+        out_id[q] = (int32_t)best;
+    }
+}
+
+/* Top-k log-probabilities [T][k] and token ids [T][k] with the contract
+ * options (z' = z inv_tau, optionally rounded fp32 -> bf16).  Returns 0 or -1. */
+int oracle_topk_logp(const uint16_t *hidden, int64_t ldh, const uint16_t *weight, int64_t ldw,
+                     int64_t T, int64_t H, int64_t V, int k, double inv_tau, int bf16,
+                     double *out_lp, int32_t *out_id, int nthreads) {
+    int fail = 0;
+    set_threads(nthreads);
+#pragma omp parallel
+    {
+        double *h = (double *)malloc((size_t)(H > 0 ? H : 1) * sizeof(double));
+        double *z = (double *)malloc((size_t)(V > 0 ? V : 1) * sizeof(double));
+        unsigned char *taken = (unsigned char *)malloc((size_t)(V > 0 ? V : 1));
+        if (!h || !z || !taken) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t t = 0; t < T; ++t) {
+                double lse, logp;
+                hidden_row(hidden, ldh, t, H, h);
+                row_logits(h, weight, ldw, H, V, z);
+                row_transform(z, V, inv_tau, bf16);
+                row_lse_logp(z, V, 0, &lse, &logp);
+                row_topk(z, V, k, lse, out_lp + t * k, out_id + t * k, taken);
+            }
+        }
+        free(h);
+        free(z);
+        free(taken);
+    }
+    return fail ? -1 : 0;
+}
+
+/* The same selection on logits given directly (fp64 [T][V]). */
+void oracle_topk_from_logits(const double *z_in, int64_t T, int64_t V, int k, double inv_tau,
+                             int bf16, double *out_lp, int32_t *out_id) {
+    double *z = (double *)malloc((size_t)(V > 0 ? V : 1) * sizeof(double));
+    unsigned char *taken = (unsigned char *)malloc((size_t)(V > 0 ? V : 1));
+    if (!z || !taken) {
+        free(z);
+        free(taken);
+        return;
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        double lse, logp;
+        memcpy(z, z_in + t * V, (size_t)V * sizeof(double));
+        row_transform(z, V, inv_tau, bf16);
+        row_lse_logp(z, V, 0, &lse, &logp);
+        row_topk(z, V, k, lse, out_lp + t * k, out_id + t * k, taken);
+    }
+    free(z);
+    free(taken);
 }

@@ -79,6 +79,11 @@ def _load():
     lib.oracle_selected_logp_backward.restype = c_int
     lib.oracle_rmsnorm.argtypes = [vp, i64, vp, ctypes.c_double, i64, i64, vp, vp]
     lib.oracle_rmsnorm.restype = None
+    lib.oracle_topk_logp.argtypes = [vp, i64, vp, i64, i64, i64, i64, c_int, ctypes.c_double,
+                                     c_int, vp, vp, c_int]
+    lib.oracle_topk_logp.restype = c_int
+    lib.oracle_topk_from_logits.argtypes = [vp, i64, i64, c_int, ctypes.c_double, c_int, vp, vp]
+    lib.oracle_topk_from_logits.restype = None
     _lib = lib
     return lib
 
@@ -277,6 +282,34 @@ def rmsnorm(x, gamma, eps: float = 1e-6, want_xr: bool = False):
     lib.oracle_rmsnorm(_ptr(xb), H, _ptr(g), float(eps), T, H, _ptr(out),
                        _ptr(xr) if xr is not None else None)
     return (out, xr) if want_xr else out
+
+
+def topk_logp(hidden, weight, k: int, inv_tau: float = 1.0, bf16: bool = False,
+              nthreads: int = 0):
+    """(logp [T, k] fp64, ids [T, k] int32): the k largest entries of
+    log softmax(z') per row, decreasing, ties to the smaller id."""
+    lib = _load()
+    h, w = _bf16_2d(hidden), _bf16_2d(weight)
+    T, H = h.shape
+    V = w.shape[0]
+    lp = np.empty((T, k), dtype=np.float64)
+    ids = np.empty((T, k), dtype=np.int32)
+    if lib.oracle_topk_logp(_ptr(h), H, _ptr(w), H, T, H, V, int(k), float(inv_tau),
+                            int(bool(bf16)), _ptr(lp), _ptr(ids), nthreads):
+        raise MemoryError("oracle_topk_logp failed")
+    return lp, ids
+
+
+def topk_from_logits(z, k: int, inv_tau: float = 1.0, bf16: bool = False):
+    """The same selection on fp64 logits [T, V] given directly."""
+    lib = _load()
+    z = np.ascontiguousarray(z, dtype=np.float64)
+    T, V = z.shape
+    lp = np.empty((T, k), dtype=np.float64)
+    ids = np.empty((T, k), dtype=np.int32)
+    lib.oracle_topk_from_logits(_ptr(z), T, V, int(k), float(inv_tau), int(bool(bf16)),
+                                _ptr(lp), _ptr(ids))
+    return lp, ids
 
 
 def sample_targets(log_probs: np.ndarray, u: np.ndarray) -> np.ndarray:
