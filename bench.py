@@ -145,6 +145,22 @@ def time_variants(rlk, torch, hidden, weight, targets, T, H, V, steps, flops):
     rn = timed(rmsnorm)
     rn_bytes = 2.0 * T * H * 2 + 2.0 * H
 
+    # top-k log-probabilities (k = 20): logits stored once, then the selection
+    z = torch.empty((T, V), dtype=torch.float32, device=dev)
+    tl = torch.empty((T, 20), dtype=torch.float32, device=dev)
+    ti = torch.empty((T, 20), dtype=torch.int32, device=dev)
+    _, lse_t = rlk.rlk_selected_logp(hidden, weight, targets)
+
+    def store_logits():
+        rlk.rlk_logits(hidden, weight, logits=z)
+
+    def select():
+        rlk.rlk_topk_logp(z, lse_t, 20, topk_logp=tl, topk_ids=ti)
+
+    lg = timed(store_logits)
+    sel = timed(select)
+    del z
+
     # decode batches: the whole head is streamed for a handful of rows
     decode = {}
     for B in (1, 16, 64, 256):
@@ -159,6 +175,8 @@ def time_variants(rlk, torch, hidden, weight, targets, T, H, V, steps, flops):
         ms = timed(dec)
         decode[f"B={B}"] = {"ms": ms, "weight_GB/s": 2.0 * V * H / (ms * 1e-3) / 1e9}
     return {
+            "topk20": {"logits_store_ms": lg, "select_ms": sel,
+                       "select_GB/s": 4.0 * T * V / (sel * 1e-3) / 1e9},
             "decode": decode,
             "rmsnorm": {"ms": rn, "GB/s": rn_bytes / (rn * 1e-3) / 1e9,
                         "frac_of_hbm_peak": rn_bytes / (rn * 1e-3) / 1e9 / PEAK_HBM_GBS,

@@ -37,7 +37,7 @@ EXPORTED = (
     "rlk_vocab_merge", "rlk_logits", "rlk_compare", "rlk_workspace_bytes_ex",
     "rlk_selected_logp_ex", "rlk_vocab_stats_ex", "rlk_vocab_merge_ex",
     "rlk_selected_logp_backward_workspace_bytes", "rlk_selected_logp_backward",
-    "rlk_logp_grad_logits", "rlk_rmsnorm",
+    "rlk_logp_grad_logits", "rlk_rmsnorm", "rlk_topk_logp",
 )
 
 _lib = None
@@ -110,6 +110,8 @@ def lib() -> ctypes.CDLL:
     L.rlk_logp_grad_logits.restype = c_int
     L.rlk_rmsnorm.argtypes = [vp, i64, vp, f32, vp, i64, i64, i64, vp]
     L.rlk_rmsnorm.restype = c_int
+    L.rlk_topk_logp.argtypes = [vp, i64, vp, i64, i64, c_int, f32, c_int, vp, vp, vp]
+    L.rlk_topk_logp.restype = c_int
     _lib = L
     return L
 
@@ -450,6 +452,40 @@ def rlk_rmsnorm(x, gamma, eps=1e-6, y=None, stream=None):
     _call("rlk_rmsnorm", lib().rlk_rmsnorm(xp, ldx, gp, float(eps), yp, ldy, T, H,
                                            _stream_ptr(stream, dev)))
     return y
+
+
+def rlk_topk_logp(logits, lse, k, inv_temperature=1.0, logits_bf16=False, V=None,
+                  topk_logp=None, topk_ids=None, stream=None):
+    """(topk_logp [T, k] fp32, topk_ids [T, k] int32) from stored logits."""
+    torch = _torch()
+    dev = logits.device
+    _check_device("logits", logits, dev)
+    if logits.dtype != torch.float32 or logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be a 2-D float32 tensor with unit column stride")
+    T = logits.shape[0]
+    V = int(logits.shape[1] if V is None else V)
+    lp_ = _f32_vec("lse", lse, T, dev)
+    if topk_logp is None:
+        topk_logp = torch.empty((T, k), dtype=torch.float32, device=dev)
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    _call("rlk_topk_logp", lib().rlk_topk_logp(
+        logits.data_ptr(), logits.stride(0), lp_, T, V, int(k), float(inv_temperature),
+        RLK_LOGITS_BF16 if logits_bf16 else 0, topk_logp.data_ptr(), topk_ids.data_ptr(),
+        _stream_ptr(stream, dev)))
+    return topk_logp, topk_ids
+
+
+def topk_logprobs(hidden, weight, targets, k, inv_temperature=1.0, logits_bf16=False,
+                  stream=None):
+    """Selected-token logp and lse plus the top-k log-probabilities of every
+    row: the statistics pass, the stored logits, then the selection."""
+    logp, lse, _ = rlk_selected_logp_ex(hidden, weight, targets,
+                                        inv_temperature=inv_temperature,
+                                        logits_bf16=logits_bf16, stream=stream)
+    z = rlk_logits(hidden, weight, stream=stream)
+    tl, ti = rlk_topk_logp(z, lse, k, inv_temperature, logits_bf16, stream=stream)
+    return logp, lse, tl, ti
 
 
 def rlk_logits(hidden, weight, logits=None, V=None, stream=None):

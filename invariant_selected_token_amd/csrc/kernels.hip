@@ -27,6 +27,8 @@
 //                       a fixed reduction order over the hidden dimension
 //                       (section 四 lists RMSNorm among the reductions whose
 //                       order matters).
+//   topk_kernel         the k largest log-probabilities of a row from stored
+//                       logits (same options, same subtraction as the merge).
 //   compare_kernel      mismatch count / max |diff| / k3 of two fp32 arrays
 //                       (sections 六/七; the vLLM blog summary's diff = 0).
 //
@@ -831,6 +833,139 @@ hipError_t launch_rmsnorm(const uint16_t *x, int64_t ldx, const uint16_t *gamma,
                           uint16_t *y, int64_t ldy, int T, int H, hipStream_t s) {
   hipLaunchKernelGGL(rmsnorm_kernel, dim3(ceil_div(T, RMS_ROWS)), dim3(64 * RMS_ROWS), 0, s, x,
                      ldx, gamma, eps, y, ldy, T, H);
+  return hipGetLastError();
+}
+
+// Top-k of one row per workgroup under the order (value descending, id
+// ascending), a total order on (value, id) pairs, so the selection does not
+// depend on how candidates are combined.  1) Thread i scans entries i, i +
+// 256, ... once, keeping its best k (unsorted, with the current minimum
+// tracked; entries come in increasing id, so an equal value never displaces
+// a kept one).  2) k rounds of a block-wide maximum over the threads' best
+// remaining candidates; the owner drops the winner.  Values are
+// z' = z inv_tau (then rounded to bf16 if asked), exactly as the statistics
+// kernel forms them, and logp = z' - lse as the merge does; NaN entries are
+// never selected; missing entries (fewer than k non-NaN) get id -1, -inf.
+constexpr int TOPK_THREADS = 256;
+struct Cand {
+  float v;
+  int i;
+};
+__device__ __forceinline__ bool cand_gt(float av, int ai, float bv, int bi) {
+  return av > bv || (av == bv && ai < bi);
+}
+template <int KC>
+__global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(
+    const float *__restrict__ logits, int64_t ld, const float *__restrict__ lse, int V, int k,
+    float inv_tau, int bf16, float *__restrict__ out_lp, int32_t *__restrict__ out_id) {
+  __shared__ Cand red[TOPK_THREADS / 64];
+  __shared__ Cand win;
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float *row = logits + (size_t)t * ld;
+  constexpr int NONE = 0x7FFFFFFF;          // id of an empty slot: below every entry
+  float val[KC];
+  int idx[KC];
+#pragma unroll
+  for (int q = 0; q < KC; ++q) {
+    val[q] = -INFINITY;
+    idx[q] = NONE;
+  }
+  float mval = -INFINITY;
+  int midx = NONE, mpos = 0;
+  // TOPK_AHEAD loads in flight per thread, then processed in increasing id
+  constexpr int TOPK_AHEAD = 16;
+  for (int v0 = tid; v0 < V; v0 += TOPK_AHEAD * TOPK_THREADS) {
+    float zz[TOPK_AHEAD];
+#pragma unroll
+    for (int u = 0; u < TOPK_AHEAD; ++u) {
+      const int v = v0 + u * TOPK_THREADS;
+      zz[u] = v < V ? row[v] : __builtin_nanf("");
+    }
+#pragma unroll
+    for (int u = 0; u < TOPK_AHEAD; ++u) {
+      const int v = v0 + u * TOPK_THREADS;
+      float z = zz[u] * inv_tau;
+      if (bf16) z = (float)(__bf16)z;
+      if (!(z == z)) continue;                // NaN, or past the row
+      if (cand_gt(z, v, mval, midx)) {
+#pragma unroll
+        for (int q = 0; q < KC; ++q)
+          if (q == mpos) {
+            val[q] = z;
+            idx[q] = v;
+          }
+        // the new minimum among the k slots in use
+        mval = val[0];
+        midx = idx[0];
+        mpos = 0;
+#pragma unroll
+        for (int q = 1; q < KC; ++q)
+          if (q < k && cand_gt(mval, midx, val[q], idx[q])) {
+            mval = val[q];
+            midx = idx[q];
+            mpos = q;
+          }
+      }
+    }
+  }
+  const float l = lse[t];
+  for (int r = 0; r < k; ++r) {
+    // this thread's best remaining candidate
+    float bv = -INFINITY;
+    int bi = NONE;
+#pragma unroll
+    for (int q = 0; q < KC; ++q)
+      if (q < k && cand_gt(val[q], idx[q], bv, bi)) {
+        bv = val[q];
+        bi = idx[q];
+      }
+    // wave maximum, then across the four waves
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oi = __shfl_xor(bi, o);
+      if (cand_gt(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if ((tid & 63) == 0) red[tid >> 6] = Cand{bv, bi};
+    __syncthreads();
+    if (tid == 0) {
+      Cand w = red[0];
+#pragma unroll
+      for (int q = 1; q < TOPK_THREADS / 64; ++q)
+        if (cand_gt(red[q].v, red[q].i, w.v, w.i)) w = red[q];
+      win = w;
+      out_lp[(size_t)t * k + r] = w.i == NONE ? -INFINITY : w.v - l;
+      out_id[(size_t)t * k + r] = w.i == NONE ? -1 : w.i;
+    }
+    __syncthreads();
+    const int wi = win.i;
+#pragma unroll
+    for (int q = 0; q < KC; ++q)
+      if (idx[q] == wi && wi != NONE) {
+        val[q] = -INFINITY;
+        idx[q] = NONE;
+      }
+  }
+}
+
+hipError_t launch_topk(const float *logits, int64_t ld, const float *lse, int T, int V, int k,
+                       float inv_tau, int bf16, float *out_lp, int32_t *out_id, hipStream_t s) {
+  if (k <= 8)
+    hipLaunchKernelGGL(topk_kernel<8>, dim3(T), dim3(TOPK_THREADS), 0, s, logits, ld, lse, V, k,
+                       inv_tau, bf16, out_lp, out_id);
+  else if (k <= 16)
+    hipLaunchKernelGGL(topk_kernel<16>, dim3(T), dim3(TOPK_THREADS), 0, s, logits, ld, lse, V,
+                       k, inv_tau, bf16, out_lp, out_id);
+  else if (k <= 32)
+    hipLaunchKernelGGL(topk_kernel<32>, dim3(T), dim3(TOPK_THREADS), 0, s, logits, ld, lse, V,
+                       k, inv_tau, bf16, out_lp, out_id);
+  else
+    hipLaunchKernelGGL(topk_kernel<64>, dim3(T), dim3(TOPK_THREADS), 0, s, logits, ld, lse, V,
+                       k, inv_tau, bf16, out_lp, out_id);
   return hipGetLastError();
 }
 

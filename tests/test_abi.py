@@ -456,3 +456,31 @@ def test_rmsnorm_error_paths(kw, status):
     a.update(kw)
     assert rlk.lib().rlk_rmsnorm(a["x"], a["ldx"], a["gamma"], a["eps"], a["y"], a["ldy"],
                                  a["T"], a["H"], None) == status
+
+
+# ------------------------------------------------------------------ top-k --
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), rlk.RLK_ERR_INVALID_SHAPE),
+    (dict(V=0), rlk.RLK_ERR_INVALID_SHAPE),
+    (dict(ld=999), rlk.RLK_ERR_INVALID_SHAPE),
+    (dict(k=0), rlk.RLK_ERR_INVALID_VALUE),
+    (dict(k=65), rlk.RLK_ERR_INVALID_VALUE),
+    (dict(k=20, V=10, ld=10), rlk.RLK_ERR_INVALID_VALUE),
+    (dict(inv_tau=0.0), rlk.RLK_ERR_INVALID_VALUE),
+    (dict(flags=8), rlk.RLK_ERR_INVALID_VALUE),
+    (dict(logits=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(lse=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(out_lp=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(out_id=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(logits=FAKE + 2), rlk.RLK_ERR_MISALIGNED),
+    (dict(out_id=FAKE + 1), rlk.RLK_ERR_MISALIGNED),
+    (dict(T=0, logits=None, lse=None, out_lp=None, out_id=None), rlk.RLK_OK),
+])
+def test_topk_error_paths(kw, status):
+    a = dict(logits=FAKE, ld=1000, lse=FAKE, T=4, V=1000, k=5, inv_tau=1.0, flags=0,
+             out_lp=FAKE, out_id=FAKE)
+    a.update(kw)
+    assert rlk.lib().rlk_topk_logp(a["logits"], a["ld"], a["lse"], a["T"], a["V"], a["k"],
+                                   a["inv_tau"], a["flags"], a["out_lp"], a["out_id"],
+                                   None) == status
