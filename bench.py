@@ -149,13 +149,14 @@ def time_variants(rlk, torch, hidden, weight, targets, T, H, V, steps, flops):
     z = torch.empty((T, V), dtype=torch.float32, device=dev)
     tl = torch.empty((T, 20), dtype=torch.float32, device=dev)
     ti = torch.empty((T, 20), dtype=torch.int32, device=dev)
-    _, lse_t = rlk.rlk_selected_logp(hidden, weight, targets)
+    ws_t = rlk.workspace_for(T, V, dev)
+    _, lse_t = rlk.rlk_selected_logp(hidden, weight, targets, workspace=ws_t)
 
     def store_logits():
         rlk.rlk_logits(hidden, weight, logits=z)
 
     def select():
-        rlk.rlk_topk_logp(z, lse_t, 20, topk_logp=tl, topk_ids=ti)
+        rlk.rlk_topk_logp(z, lse_t, ws_t, 20, topk_logp=tl, topk_ids=ti)
 
     lg = timed(store_logits)
     sel = timed(select)

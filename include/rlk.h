@@ -300,21 +300,26 @@ int rlk_logits(const void *hidden, int64_t ld_hidden, const void *weight,
 
 /* Top-k log-probabilities of each row (the per-token logprob outputs an RL
  * step reads next to the selected token's; the vLLM blog summary lists
- * them), from the logits rlk_logits stores and the lse of the forward with
- * the same options.  Per row: the k largest entries of
+ * them), from the logits rlk_logits stores and the lse and workspace of the
+ * statistics pass with the same options.  Per row: the k largest entries of
  * z' - lse, z' = z * inv_temperature (then rounded to bf16 with
  * RLK_LOGITS_BF16), in decreasing order, ties to the smaller token id; NaN
  * entries are never selected; with fewer than k others the tail holds id -1
  * and -inf.  z' and the subtraction are those of the statistics pass, so
- * the entry for a row's target is bitwise its logp.
+ * the entry of any id is bitwise the selected-token logp of that id.  The
+ * workspace's tile maxima limit the search to the tiles whose maximum is at
+ * least the k-th largest tile maximum (no other tile can hold a top-k entry).
  *   logits       fp32 [T][ld_logits] (ld_logits >= V), 4-byte aligned.
  *   lse          fp32 [T] from rlk_selected_logp(_ex) with the same options.
+ *   workspace    the workspace that call (or rlk_vocab_stats(_ex), with the
+ *                same T, V and options) filled; only read.
  *   k            1 .. 64 and <= V (RLK_ERR_INVALID_VALUE otherwise).
  *   flags        as for the _ex calls (RLK_ENTROPY is ignored here).
  *   topk_logp    fp32 [T][k], topk_ids int32 [T][k], 4-byte aligned. */
-int rlk_topk_logp(const float *logits, int64_t ld_logits, const float *lse, int64_t T,
-                  int64_t V, int k, float inv_temperature, int flags, float *topk_logp,
-                  int32_t *topk_ids, void *stream);
+int rlk_topk_logp(const float *logits, int64_t ld_logits, const float *lse,
+                  const void *workspace, size_t workspace_bytes, int64_t T, int64_t V, int k,
+                  float inv_temperature, int flags, float *topk_logp, int32_t *topk_ids,
+                  void *stream);
 
 /* Consistency statistics of two fp32 arrays a (the side under test, e.g.
  * training) and b (the reference, e.g. rollout), as the pages measure them:

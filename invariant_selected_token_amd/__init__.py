@@ -110,7 +110,7 @@ def lib() -> ctypes.CDLL:
     L.rlk_logp_grad_logits.restype = c_int
     L.rlk_rmsnorm.argtypes = [vp, i64, vp, f32, vp, i64, i64, i64, vp]
     L.rlk_rmsnorm.restype = c_int
-    L.rlk_topk_logp.argtypes = [vp, i64, vp, i64, i64, c_int, f32, c_int, vp, vp, vp]
+    L.rlk_topk_logp.argtypes = [vp, i64, vp, vp, sz, i64, i64, c_int, f32, c_int, vp, vp, vp]
     L.rlk_topk_logp.restype = c_int
     _lib = L
     return L
@@ -454,9 +454,10 @@ def rlk_rmsnorm(x, gamma, eps=1e-6, y=None, stream=None):
     return y
 
 
-def rlk_topk_logp(logits, lse, k, inv_temperature=1.0, logits_bf16=False, V=None,
+def rlk_topk_logp(logits, lse, workspace, k, inv_temperature=1.0, logits_bf16=False, V=None,
                   topk_logp=None, topk_ids=None, stream=None):
-    """(topk_logp [T, k] fp32, topk_ids [T, k] int32) from stored logits."""
+    """(topk_logp [T, k] fp32, topk_ids [T, k] int32) from stored logits and
+    the statistics pass's lse and workspace (same options)."""
     torch = _torch()
     dev = logits.device
     _check_device("logits", logits, dev)
@@ -465,12 +466,14 @@ def rlk_topk_logp(logits, lse, k, inv_temperature=1.0, logits_bf16=False, V=None
     T = logits.shape[0]
     V = int(logits.shape[1] if V is None else V)
     lp_ = _f32_vec("lse", lse, T, dev)
+    _check_device("workspace", workspace, dev)
     if topk_logp is None:
         topk_logp = torch.empty((T, k), dtype=torch.float32, device=dev)
     if topk_ids is None:
         topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
     _call("rlk_topk_logp", lib().rlk_topk_logp(
-        logits.data_ptr(), logits.stride(0), lp_, T, V, int(k), float(inv_temperature),
+        logits.data_ptr(), logits.stride(0), lp_, workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), T, V, int(k), float(inv_temperature),
         RLK_LOGITS_BF16 if logits_bf16 else 0, topk_logp.data_ptr(), topk_ids.data_ptr(),
         _stream_ptr(stream, dev)))
     return topk_logp, topk_ids
@@ -480,11 +483,15 @@ def topk_logprobs(hidden, weight, targets, k, inv_temperature=1.0, logits_bf16=F
                   stream=None):
     """Selected-token logp and lse plus the top-k log-probabilities of every
     row: the statistics pass, the stored logits, then the selection."""
+    dev, _, _, _, _, T, _, V = _prepare(hidden, weight, targets, None)
+    flags = RLK_LOGITS_BF16 if logits_bf16 else 0
+    ws = _torch().empty(max(rlk_workspace_bytes_ex(T, V, flags), 1), dtype=_torch().uint8,
+                        device=dev)
     logp, lse, _ = rlk_selected_logp_ex(hidden, weight, targets,
                                         inv_temperature=inv_temperature,
-                                        logits_bf16=logits_bf16, stream=stream)
+                                        logits_bf16=logits_bf16, workspace=ws, stream=stream)
     z = rlk_logits(hidden, weight, stream=stream)
-    tl, ti = rlk_topk_logp(z, lse, k, inv_temperature, logits_bf16, stream=stream)
+    tl, ti = rlk_topk_logp(z, lse, ws, k, inv_temperature, logits_bf16, stream=stream)
     return logp, lse, tl, ti
 
 

@@ -416,21 +416,24 @@ int rlk_rmsnorm(const void *x, int64_t ld_x, const void *gamma, float eps, void 
                                         static_cast<hipStream_t>(stream)));
 }
 
-int rlk_topk_logp(const float *logits, int64_t ld_logits, const float *lse, int64_t T,
-                  int64_t V, int k, float inv_temperature, int flags, float *topk_logp,
-                  int32_t *topk_ids, void *stream) {
+int rlk_topk_logp(const float *logits, int64_t ld_logits, const float *lse,
+                  const void *workspace, size_t workspace_bytes, int64_t T, int64_t V, int k,
+                  float inv_temperature, int flags, float *topk_logp, int32_t *topk_ids,
+                  void *stream) {
   if (T < 0 || V <= 0 || ld_logits < V) return RLK_ERR_INVALID_SHAPE;
   if (T > MAX_ROWS || V > MAX_ROWS) return RLK_ERR_UNSUPPORTED;
   if (check_options(inv_temperature, flags) != RLK_OK || k < 1 || k > 64 || k > V)
     return RLK_ERR_INVALID_VALUE;
   if (T == 0) return RLK_OK;
-  if (!logits || !lse || !topk_logp || !topk_ids) return RLK_ERR_NULL_POINTER;
-  if (!aligned(logits, 4) || !aligned(lse, 4) || !aligned(topk_logp, 4) ||
-      !aligned(topk_ids, 4))
+  if (!logits || !lse || !workspace || !topk_logp || !topk_ids) return RLK_ERR_NULL_POINTER;
+  if (!aligned(logits, 4) || !aligned(lse, 4) || !aligned(workspace, 16) ||
+      !aligned(topk_logp, 4) || !aligned(topk_ids, 4))
     return RLK_ERR_MISALIGNED;
-  return hip_status(rlk::launch_topk(logits, ld_logits, lse, (int)T, (int)V, k, inv_temperature,
-                                     (flags & RLK_LOGITS_BF16) ? 1 : 0, topk_logp, topk_ids,
-                                     static_cast<hipStream_t>(stream)));
+  if (workspace_bytes < stats_bytes(T, V)) return RLK_ERR_WORKSPACE_TOO_SMALL;
+  return hip_status(rlk::launch_topk(logits, ld_logits, lse,
+                                     static_cast<const float *>(workspace), (int)T, (int)V, k,
+                                     inv_temperature, (flags & RLK_LOGITS_BF16) ? 1 : 0,
+                                     topk_logp, topk_ids, static_cast<hipStream_t>(stream)));
 }
 
 int rlk_logits(const void *hidden, int64_t ld_hidden, const void *weight,

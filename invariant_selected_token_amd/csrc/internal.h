@@ -92,9 +92,11 @@ hipError_t launch_transpose(const uint16_t *in, int64_t ldi, int R, int C, uint1
 // == 0, ldx and ldy multiples of 8, 16-byte aligned pointers.
 hipError_t launch_rmsnorm(const uint16_t *x, int64_t ldx, const uint16_t *gamma, float eps,
                           uint16_t *y, int64_t ldy, int T, int H, hipStream_t s);
-// Top-k log-probabilities of T rows of stored fp32 logits [T][ld] (1 <= k <= 64).
-hipError_t launch_topk(const float *logits, int64_t ld, const float *lse, int T, int V, int k,
-                       float inv_tau, int bf16, float *out_lp, int32_t *out_id, hipStream_t s);
+// Top-k log-probabilities of T rows of stored fp32 logits [T][ld] (1 <= k <= 64),
+// filtered by the statistics pass's tile maxima part_m [ceil(V/128)][T].
+hipError_t launch_topk(const float *logits, int64_t ld, const float *lse, const float *part_m,
+                       int T, int V, int k, float inv_tau, int bf16, float *out_lp,
+                       int32_t *out_id, hipStream_t s);
 // x[0 .. n) = 0.0f
 hipError_t launch_zero(float *x, int64_t n, hipStream_t s);
 hipError_t launch_compare(const float *a, const float *b, int n,

@@ -838,15 +838,23 @@ hipError_t launch_rmsnorm(const uint16_t *x, int64_t ldx, const uint16_t *gamma,
 
 // Top-k of one row per workgroup under the order (value descending, id
 // ascending), a total order on (value, id) pairs, so the selection does not
-// depend on how candidates are combined.  1) Thread i scans entries i, i +
-// 256, ... once, keeping its best k (unsorted, with the current minimum
-// tracked; entries come in increasing id, so an equal value never displaces
-// a kept one).  2) k rounds of a block-wide maximum over the threads' best
-// remaining candidates; the owner drops the winner.  Values are
+// depend on the order candidates are visited or combined in.  Values are
 // z' = z inv_tau (then rounded to bf16 if asked), exactly as the statistics
 // kernel forms them, and logp = z' - lse as the merge does; NaN entries are
 // never selected; missing entries (fewer than k non-NaN) get id -1, -inf.
+//
+// The statistics pass already holds every 128-wide tile's maximum of z'.
+// If m* is the k-th largest of a row's tile maxima, the k tiles with the
+// largest maxima hold k distinct entries >= m*, so the k-th largest entry is
+// >= m*, and no tile whose maximum is below m* can hold a top-k entry.  So:
+//   1) m* by a top-k selection over the row's tile maxima;
+//   2) the list of tiles with maximum >= m* (more than TOPK_LIST of them,
+//      possible only with ties, e.g. constant rows: scan the whole row);
+//   3) a top-k selection over those tiles' entries: each thread keeps its
+//      best k (unsorted, current minimum tracked), then k rounds of a
+//      block-wide maximum in which the owner drops the winner.
 constexpr int TOPK_THREADS = 256;
+constexpr int TOPK_LIST = 512;
 struct Cand {
   float v;
   int i;
@@ -855,63 +863,46 @@ __device__ __forceinline__ bool cand_gt(float av, int ai, float bv, int bi) {
   return av > bv || (av == bv && ai < bi);
 }
 template <int KC>
-__global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(
-    const float *__restrict__ logits, int64_t ld, const float *__restrict__ lse, int V, int k,
-    float inv_tau, int bf16, float *__restrict__ out_lp, int32_t *__restrict__ out_id) {
-  __shared__ Cand red[TOPK_THREADS / 64];
-  __shared__ Cand win;
-  const int t = blockIdx.x;
-  const int tid = threadIdx.x;
-  const float *row = logits + (size_t)t * ld;
-  constexpr int NONE = 0x7FFFFFFF;          // id of an empty slot: below every entry
+struct TopK {
+  static constexpr int NONE = 0x7FFFFFFF;   // id of an empty slot: below every entry
   float val[KC];
   int idx[KC];
+  float mval;
+  int midx, mpos;
+  __device__ __forceinline__ void reset() {
 #pragma unroll
-  for (int q = 0; q < KC; ++q) {
-    val[q] = -INFINITY;
-    idx[q] = NONE;
-  }
-  float mval = -INFINITY;
-  int midx = NONE, mpos = 0;
-  // TOPK_AHEAD loads in flight per thread, then processed in increasing id
-  constexpr int TOPK_AHEAD = 16;
-  for (int v0 = tid; v0 < V; v0 += TOPK_AHEAD * TOPK_THREADS) {
-    float zz[TOPK_AHEAD];
-#pragma unroll
-    for (int u = 0; u < TOPK_AHEAD; ++u) {
-      const int v = v0 + u * TOPK_THREADS;
-      zz[u] = v < V ? row[v] : __builtin_nanf("");
+    for (int q = 0; q < KC; ++q) {
+      val[q] = -INFINITY;
+      idx[q] = NONE;
     }
+    mval = -INFINITY;
+    midx = NONE;
+    mpos = 0;
+  }
+  __device__ __forceinline__ void offer(float z, int v, int k) {
+    if (!(z == z) || !cand_gt(z, v, mval, midx)) return;     // NaN, or not better
+    // unconditional selects keep the slots in registers
 #pragma unroll
-    for (int u = 0; u < TOPK_AHEAD; ++u) {
-      const int v = v0 + u * TOPK_THREADS;
-      float z = zz[u] * inv_tau;
-      if (bf16) z = (float)(__bf16)z;
-      if (!(z == z)) continue;                // NaN, or past the row
-      if (cand_gt(z, v, mval, midx)) {
+    for (int q = 0; q < KC; ++q) {
+      const bool hit = q == mpos;
+      val[q] = hit ? z : val[q];
+      idx[q] = hit ? v : idx[q];
+    }
+    mval = val[0];
+    midx = idx[0];
+    mpos = 0;
 #pragma unroll
-        for (int q = 0; q < KC; ++q)
-          if (q == mpos) {
-            val[q] = z;
-            idx[q] = v;
-          }
-        // the new minimum among the k slots in use
-        mval = val[0];
-        midx = idx[0];
-        mpos = 0;
-#pragma unroll
-        for (int q = 1; q < KC; ++q)
-          if (q < k && cand_gt(mval, midx, val[q], idx[q])) {
-            mval = val[q];
-            midx = idx[q];
-            mpos = q;
-          }
+    for (int q = 1; q < KC; ++q)
+      if (q < k && cand_gt(mval, midx, val[q], idx[q])) {
+        mval = val[q];
+        midx = idx[q];
+        mpos = q;
       }
-    }
   }
-  const float l = lse[t];
-  for (int r = 0; r < k; ++r) {
-    // this thread's best remaining candidate
+  // Round r of the block-wide selection: the winner of the remaining
+  // candidates, dropped by its owner, returned to every thread.
+  __device__ __forceinline__ Cand next(int k, Cand *red, Cand *win) {
+    const int tid = threadIdx.x;
     float bv = -INFINITY;
     int bi = NONE;
 #pragma unroll
@@ -920,7 +911,6 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(
         bv = val[q];
         bi = idx[q];
       }
-    // wave maximum, then across the four waves
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       const float ov = __shfl_xor(bv, o);
@@ -937,35 +927,97 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(
 #pragma unroll
       for (int q = 1; q < TOPK_THREADS / 64; ++q)
         if (cand_gt(red[q].v, red[q].i, w.v, w.i)) w = red[q];
-      win = w;
-      out_lp[(size_t)t * k + r] = w.i == NONE ? -INFINITY : w.v - l;
-      out_id[(size_t)t * k + r] = w.i == NONE ? -1 : w.i;
+      *win = w;
     }
     __syncthreads();
-    const int wi = win.i;
+    const Cand w = *win;
+    __syncthreads();   // every thread has read *win before the next round writes it
 #pragma unroll
-    for (int q = 0; q < KC; ++q)
-      if (idx[q] == wi && wi != NONE) {
-        val[q] = -INFINITY;
-        idx[q] = NONE;
-      }
+    for (int q = 0; q < KC; ++q) {
+      const bool hit = idx[q] == w.i && w.i != NONE;
+      val[q] = hit ? -INFINITY : val[q];
+      idx[q] = hit ? NONE : idx[q];
+    }
+    return w;
+  }
+};
+
+template <int KC>
+__global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(
+    const float *__restrict__ logits, int64_t ld, const float *__restrict__ lse,
+    const float *__restrict__ part_m, int T, int V, int nST, int k, float inv_tau, int bf16,
+    float *__restrict__ out_lp, int32_t *__restrict__ out_id) {
+  __shared__ Cand red[TOPK_THREADS / 64];
+  __shared__ Cand win;
+  __shared__ int list[TOPK_LIST];
+  __shared__ int nlist;
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float *row = logits + (size_t)t * ld;
+  TopK<KC> sel;
+
+  // 1) m*: the k-th largest tile maximum (entries of a row are the tiles)
+  sel.reset();
+  for (int j = tid; j < nST; j += TOPK_THREADS) sel.offer(part_m[(size_t)j * T + t], j, k);
+  Cand kth{-INFINITY, TopK<KC>::NONE};
+  const int kk = k < nST ? k : nST;
+  for (int r = 0; r < kk; ++r) kth = sel.next(k, red, &win);
+  const float mstar = kth.v;
+
+  // 2) the tiles that can hold a top-k entry
+  if (tid == 0) nlist = 0;
+  __syncthreads();
+  for (int j = tid; j < nST; j += TOPK_THREADS) {
+    const float m = part_m[(size_t)j * T + t];
+    if (m >= mstar) {
+      const int at = atomicAdd(&nlist, 1);
+      if (at < TOPK_LIST) list[at] = j;
+    }
+  }
+  __syncthreads();
+  const int n = nlist;
+
+  // 3) top-k of those tiles' entries (or of the whole row)
+  sel.reset();
+  auto offer_v = [&](int v) {
+    float z = row[v] * inv_tau;
+    if (bf16) z = (float)(__bf16)z;
+    sel.offer(z, v, k);
+  };
+  if (n <= TOPK_LIST && mstar == mstar) {
+    for (int i = tid; i < n * STAT_V; i += TOPK_THREADS) {
+      const int v = list[i / STAT_V] * STAT_V + (i % STAT_V);
+      if (v < V) offer_v(v);
+    }
+  } else {
+    for (int v = tid; v < V; v += TOPK_THREADS) offer_v(v);
+  }
+  const float l = lse[t];
+  for (int r = 0; r < k; ++r) {
+    const Cand w = sel.next(k, red, &win);
+    if (tid == 0) {
+      out_lp[(size_t)t * k + r] = w.i == TopK<KC>::NONE ? -INFINITY : w.v - l;
+      out_id[(size_t)t * k + r] = w.i == TopK<KC>::NONE ? -1 : w.i;
+    }
   }
 }
 
-hipError_t launch_topk(const float *logits, int64_t ld, const float *lse, int T, int V, int k,
-                       float inv_tau, int bf16, float *out_lp, int32_t *out_id, hipStream_t s) {
+hipError_t launch_topk(const float *logits, int64_t ld, const float *lse, const float *part_m,
+                       int T, int V, int k, float inv_tau, int bf16, float *out_lp,
+                       int32_t *out_id, hipStream_t s) {
+  const int nST = ceil_div(V, STAT_V);
   if (k <= 8)
-    hipLaunchKernelGGL(topk_kernel<8>, dim3(T), dim3(TOPK_THREADS), 0, s, logits, ld, lse, V, k,
-                       inv_tau, bf16, out_lp, out_id);
+    hipLaunchKernelGGL(topk_kernel<8>, dim3(T), dim3(TOPK_THREADS), 0, s, logits, ld, lse, part_m,
+                       T, V, nST, k, inv_tau, bf16, out_lp, out_id);
   else if (k <= 16)
-    hipLaunchKernelGGL(topk_kernel<16>, dim3(T), dim3(TOPK_THREADS), 0, s, logits, ld, lse, V,
-                       k, inv_tau, bf16, out_lp, out_id);
+    hipLaunchKernelGGL(topk_kernel<16>, dim3(T), dim3(TOPK_THREADS), 0, s, logits, ld, lse,
+                       part_m, T, V, nST, k, inv_tau, bf16, out_lp, out_id);
   else if (k <= 32)
-    hipLaunchKernelGGL(topk_kernel<32>, dim3(T), dim3(TOPK_THREADS), 0, s, logits, ld, lse, V,
-                       k, inv_tau, bf16, out_lp, out_id);
+    hipLaunchKernelGGL(topk_kernel<32>, dim3(T), dim3(TOPK_THREADS), 0, s, logits, ld, lse,
+                       part_m, T, V, nST, k, inv_tau, bf16, out_lp, out_id);
   else
-    hipLaunchKernelGGL(topk_kernel<64>, dim3(T), dim3(TOPK_THREADS), 0, s, logits, ld, lse, V,
-                       k, inv_tau, bf16, out_lp, out_id);
+    hipLaunchKernelGGL(topk_kernel<64>, dim3(T), dim3(TOPK_THREADS), 0, s, logits, ld, lse,
+                       part_m, T, V, nST, k, inv_tau, bf16, out_lp, out_id);
   return hipGetLastError();
 }
 

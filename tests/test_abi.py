@@ -475,12 +475,15 @@ def test_rmsnorm_error_paths(kw, status):
     (dict(out_id=None), rlk.RLK_ERR_NULL_POINTER),
     (dict(logits=FAKE + 2), rlk.RLK_ERR_MISALIGNED),
     (dict(out_id=FAKE + 1), rlk.RLK_ERR_MISALIGNED),
-    (dict(T=0, logits=None, lse=None, out_lp=None, out_id=None), rlk.RLK_OK),
+    (dict(ws=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(ws=WS_FAKE + 4), rlk.RLK_ERR_MISALIGNED),
+    (dict(ws_bytes=64), rlk.RLK_ERR_WORKSPACE_TOO_SMALL),
+    (dict(T=0, logits=None, lse=None, ws=None, out_lp=None, out_id=None), rlk.RLK_OK),
 ])
 def test_topk_error_paths(kw, status):
-    a = dict(logits=FAKE, ld=1000, lse=FAKE, T=4, V=1000, k=5, inv_tau=1.0, flags=0,
-             out_lp=FAKE, out_id=FAKE)
+    a = dict(logits=FAKE, ld=1000, lse=FAKE, ws=WS_FAKE, ws_bytes=1 << 20, T=4, V=1000, k=5,
+             inv_tau=1.0, flags=0, out_lp=FAKE, out_id=FAKE)
     a.update(kw)
-    assert rlk.lib().rlk_topk_logp(a["logits"], a["ld"], a["lse"], a["T"], a["V"], a["k"],
-                                   a["inv_tau"], a["flags"], a["out_lp"], a["out_id"],
-                                   None) == status
+    assert rlk.lib().rlk_topk_logp(a["logits"], a["ld"], a["lse"], a["ws"], a["ws_bytes"],
+                                   a["T"], a["V"], a["k"], a["inv_tau"], a["flags"],
+                                   a["out_lp"], a["out_id"], None) == status
