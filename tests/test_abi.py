@@ -487,3 +487,16 @@ def test_topk_error_paths(kw, status):
     assert rlk.lib().rlk_topk_logp(a["logits"], a["ld"], a["lse"], a["ws"], a["ws_bytes"],
                                    a["T"], a["V"], a["k"], a["inv_tau"], a["flags"],
                                    a["out_lp"], a["out_id"], None) == status
+
+
+def test_binding_type_errors_before_any_device_work():
+    torch = pytest.importorskip("torch")
+    h = torch.zeros((2, 64), dtype=torch.float32)
+    w = torch.zeros((8, 64), dtype=torch.bfloat16)
+    y = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        rlk.rlk_selected_logp(h, w, y)                 # fp32 hidden
+    with pytest.raises(TypeError):
+        rlk.rlk_selected_logp_ex(h, w, y, entropy=True)  # fp32 hidden, option path
+    with pytest.raises(ValueError):
+        rlk.rlk_selected_logp(w[:2], w, y)             # host tensors

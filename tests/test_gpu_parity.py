@@ -280,3 +280,37 @@ def test_maximum_sizes(dev, T, H, V):
     ref_lp, ref_lse = orc.selected_logp(c.hidden, c.weight, y)
     _assert_close(lp, ref_lp, f"logp {T}x{H}x{V}")
     _assert_close(lse, ref_lse, f"lse {T}x{H}x{V}")
+
+
+def test_empty_batches_through_every_entry_point(tiny, dev):
+    """T = 0: every call returns empty results (grad_weight zero-filled)."""
+    h0, y0 = tiny.hidden[:0], tiny.targets[:0]
+    lp, lse = rlk.rlk_selected_logp(h0, tiny.weight, y0)
+    assert lp.shape == (0,) and lse.shape == (0,)
+    lp, lse, ent = rlk.rlk_selected_logp_ex(h0, tiny.weight, y0, inv_temperature=0.5,
+                                            logits_bf16=True, entropy=True)
+    assert ent.shape == (0,)
+    z = rlk.rlk_logits(h0, tiny.weight)
+    assert z.shape == (0, tiny.case.V)
+    e = torch.empty(0, dtype=torch.float32, device=dev)
+    gh, gw = rlk.rlk_selected_logp_backward(h0, tiny.weight, y0, e, e)
+    torch.cuda.synchronize()
+    assert gh.shape == (0, tiny.case.H) and not bool(gw.any())
+    assert rlk.rlk_rmsnorm(h0, tiny.weight[0], 1e-6).shape == (0, tiny.case.H)
+    ws = rlk.workspace_for(1, tiny.case.V, dev)
+    tl, ti = rlk.rlk_topk_logp(z, e, ws, 5)
+    assert tl.shape == (0, 5) and ti.shape == (0, 5)
+
+
+def test_single_entry_vocabulary_with_options(dev):
+    """V = 1: lse = z, logp = 0, entropy = 0, top-1 is that entry."""
+    c = synth.normal_case("v1", 4, 5, 64, 1)
+    h, w = to_dev_bf16(c.hidden, dev), to_dev_bf16(c.weight, dev)
+    y = to_dev_i32(np.zeros(5, np.int32), dev)
+    lp, lse, ent = rlk.rlk_selected_logp_ex(h, w, y, inv_temperature=0.7, entropy=True)
+    torch.cuda.synchronize()
+    assert bool((lp == 0).all()) and bool((ent == 0).all())
+    z = orc.logits(c.hidden, c.weight)[:, 0] * 0.7
+    assert np.abs(lse.cpu().numpy() - z).max() <= 1e-5
+    lp2, lse2, tl, ti = rlk.topk_logprobs(h, w, y, 1, inv_temperature=0.7)
+    assert bool((ti == 0).all()) and bool((tl == 0).all())
