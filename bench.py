@@ -78,7 +78,7 @@ def cpu_baseline(case, seconds: float) -> dict:
                       f"full vocabulary V={case.V}, fp64, {wall:.1f} s wall"}
 
 
-def time_variants(rlk, torch, hidden, weight, targets, T, H, V, steps, flops):
+def time_variants(rlk, torch, np, hidden, weight, targets, T, H, V, steps, flops):
     """The same workload through the other entry points, timed after (never
     inside) the headline region: the contract options (1/tau = 0.7, bf16
     logits, entropy) and the statistics computed as 4 vocabulary slices plus
@@ -162,6 +162,34 @@ def time_variants(rlk, torch, hidden, weight, targets, T, H, V, steps, flops):
     sel = timed(select)
     del z
 
+    # long rollout: 16384 rows (32 responses x 512 tokens) through the same path
+    from invariant_selected_token_amd import synth as _synth
+    lr = _synth.long_rollout_case()
+    to_dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(
+        torch.bfloat16)
+    h_lr, y_lr = to_dev(lr.hidden), torch.from_numpy(lr.targets).to(dev)
+    T_lr = lr.T
+    ws_lr = rlk.workspace_for(T_lr, V, dev)
+    lp_lr = torch.empty(T_lr, dtype=torch.float32, device=dev)
+    lse_lr = torch.empty_like(lp_lr)
+
+    def rollout_stats():
+        rlk.rlk_vocab_stats(h_lr, weight, y_lr, ws_lr)
+
+    def rollout_merge():
+        rlk.rlk_vocab_merge(y_lr, ws_lr, V, logp=lp_lr, lse=lse_lr)
+
+    ro_g = timed(rollout_stats)
+    ro_m = timed(rollout_merge)
+    ro_bytes = 8.0 * ((V + 127) // 128) * T_lr + 16.0 * T_lr
+    rollout = {"T": T_lr, "gemm_stats_ms": ro_g, "merge_ms": ro_m,
+               "tokens/s": T_lr / ((ro_g + ro_m) * 1e-3),
+               "gemm_TFLOP/s": 2.0 * T_lr * H * V / (ro_g * 1e-3) / 1e12,
+               "gemm_frac_of_bf16_peak": 2.0 * T_lr * H * V / (ro_g * 1e-3) / 1e12
+               / PEAK_BF16_TFLOPS,
+               "merge_GB/s": ro_bytes / (ro_m * 1e-3) / 1e9}
+    del h_lr, ws_lr
+
     # decode batches: the whole head is streamed for a handful of rows
     decode = {}
     for B in (1, 16, 64, 256):
@@ -176,6 +204,7 @@ def time_variants(rlk, torch, hidden, weight, targets, T, H, V, steps, flops):
         ms = timed(dec)
         decode[f"B={B}"] = {"ms": ms, "weight_GB/s": 2.0 * V * H / (ms * 1e-3) / 1e9}
     return {
+            "long_rollout": rollout,
             "topk20": {"logits_store_ms": lg, "select_ms": sel,
                        "select_GB/s": 4.0 * T * V / (sel * 1e-3) / 1e9},
             "decode": decode,
@@ -312,7 +341,7 @@ def main() -> int:
         "kernel_source": kernel_source_digest(),
     }
     if args.variant_steps > 0:
-        out["variants"] = time_variants(rlk, torch, hidden, weight, targets, T, H, V,
+        out["variants"] = time_variants(rlk, torch, np, hidden, weight, targets, T, H, V,
                                         args.variant_steps, flops)
     if not args.no_cpu_baseline:
         log("bench: timing the fp64 oracle on the host")
