@@ -292,8 +292,9 @@ int rlk_rmsnorm(const void *x, int64_t ld_x, const void *gamma, float eps, void 
  * section 五: compare intermediate results to find the first divergence).
  * Runs the very same GEMM main loop as rlk_selected_logp and stores the fp32
  * accumulators: logits[t * V + v], row-major [T][V], 4-byte aligned.
- * Argument rules as above; no workspace.  Test and debugging use: it writes
- * 4*T*V bytes. */
+ * Argument rules as above, and V <= 2^24 (RLK_ERR_UNSUPPORTED beyond: 32 rows
+ * of the output must span less than 2^31 bytes); no workspace.  Test,
+ * debugging and top-k use: it writes 4*T*V bytes. */
 int rlk_logits(const void *hidden, int64_t ld_hidden, const void *weight,
                int64_t ld_weight, float *logits, int64_t T, int64_t H,
                int64_t V, void *stream);

@@ -14,6 +14,9 @@ using rlk::ceil_div;
 constexpr int64_t MAX_ROWS = 2147483647;   // T and V fit in a signed int
 constexpr int64_t MAX_H = 65536;
 constexpr int64_t MAX_LD = int64_t(1) << 21;  // 256-row tile bytes < 2^31
+// Columns of a stored fp32 output: the store kernel addresses 32 rows through
+// one buffer resource, whose byte offsets must stay below 2^31.
+constexpr int64_t MAX_STORE_COLS = int64_t(1) << 24;
 constexpr size_t WS_ALIGN = 256;
 
 thread_local hipError_t g_last_hip_error = hipSuccess;
@@ -441,6 +444,7 @@ int rlk_logits(const void *hidden, int64_t ld_hidden, const void *weight,
                int64_t V, void *stream) {
   int st = check_shapes(T, H, V, ld_hidden, ld_weight);
   if (st != RLK_OK) return st;
+  if (V > MAX_STORE_COLS) return RLK_ERR_UNSUPPORTED;
   if (T == 0) return RLK_OK;
   st = check_operands(hidden, ld_hidden, weight, ld_weight);
   if (st != RLK_OK) return st;

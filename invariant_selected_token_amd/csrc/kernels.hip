@@ -10,8 +10,11 @@
 //                       its epilogue (section 四: per-block m_j, s_j of the
 //                       LSE; section 七: local statistics per vocabulary
 //                       tile, here 128 wide).  Logits never leave registers.
-//   gemm_kernel<false,false> the same main loop, storing fp32 logits (the
-//                       stage-by-stage comparison of section 五).
+//   gemm_kernel<false,.> the same main loop, storing fp32 logits (the
+//                       stage-by-stage comparison of section 五; also the two
+//                       gradient products of the backward).  EX 0 stores 16
+//                       bytes per lane, EX 1 one column per store, for rows
+//                       whose length or base is not 16-byte aligned.
 //   merge_kernel        per row, folds the tile statistics in a fixed order
 //                       that depends only on the number of vocabulary tiles,
 //                       then lse = M + log(s) and logp = z_y - lse (and, with
@@ -73,6 +76,8 @@ constexpr int VMCNT0_LGKMCNT0 = 0x0070;
 constexpr int PREFETCH_AHEAD = RLK_PREFETCH_AHEAD;
 // LDS bytes past the two stages that absorb the prefetch loads' data.
 constexpr int PREFETCH_SINK = 256;
+// Then a double buffer of the tiles' targets (2 x 256 int32).
+constexpr int TGT_OFS = 4 * TILE_V * TILE_K * 2 + PREFETCH_SINK;
 
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base,
@@ -184,6 +189,16 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
                                              (uint32_t)kb * (TILE_K * 2), 0, 0);
   };
   // A tile's first K block into stage 0, and its next blocks into L2.
+  // Targets of a tile: one 4-byte direct-to-LDS load per wave (64 rows
+  // each) into the tile's half of a double buffer; rows past T read 0.
+  const __amdgpu_buffer_rsrc_t r_tgt =
+      make_rsrc(a.targets, STATS ? (uint32_t)(a.T * 4) : 0u);
+  auto stage_targets = [&](int tile_m, int par) {
+    if (STATS)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r_tgt, (lds_void *)(smem + TGT_OFS + par * (TILE_T * 4) + wave * 256), 4,
+          (uint32_t)(lane * 4), (uint32_t)((tile_m * TILE_T + 64 * wave) * 4), 0, 0);
+  };
   auto issue_first = [&](__amdgpu_buffer_rsrc_t r_w, __amdgpu_buffer_rsrc_t r_h) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) gload(r_w, r_h, 0, 0, q);
@@ -287,6 +302,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   int m, n;
   coords(L, m, n);
   __amdgpu_buffer_rsrc_t rw = rsrc_w(n), rh = rsrc_h(m);
+  int parity = 0;
+  stage_targets(m, 0);
   issue_first(rw, rh);
 
   for (;;) {
@@ -310,6 +327,15 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     k_block(nk2 - 2, S0{}, std::true_type{}, rw_last, rh_last, rw, rh);
     k_block(nk2 - 1, S1{}, std::false_type{}, rw, rh, rw, rh);
 
+    const int v0 = n * TILE_V;
+    const int t0 = m * TILE_T;
+    // The epilogue's lane values, computed afresh (an asm the compiler cannot
+    // merge with the set-up's) so that nothing from the set-up stays live
+    // across the K loop or is spilled: a reload from scratch here would be
+    // a vector memory op, and waiting for it would also wait for the next
+    // tile's loads issued below.
+    int lane_e;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
     // Stage 0 was last read before the barrier of block nk2 - 2, so the
     // next tile's first block can go there now, under this epilogue.
     const int Ln = PERSIST ? L + (int)gridDim.x : total;
@@ -319,41 +345,69 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
       coords(Ln, mn, nn);
       rwn = rsrc_w(nn);
       rhn = rsrc_h(mn);
+      stage_targets(mn, parity ^ 1);
       issue_first(rwn, rhn);
     }
 
     // acc[i][j][r] holds z[t][v] for
     //   v = v0 + wv*128 + 32 i + 8 (r >> 2) + 4 fk + (r & 3)
     //   t = t0 + wt*128 + 32 j + fr
-    const int v0 = n * TILE_V;
-    const int t0 = m * TILE_T;
     const int vbase = v0 + wv * 128;
+    {
+    const int fr = lane_e & 31;
+    const int fk = lane_e >> 5;
+    auto xor32 = [&](float x) {
+      return __int_as_float(__builtin_amdgcn_ds_bpermute((lane_e ^ 32) << 2, __float_as_int(x)));
+    };
+    // this tile's targets, staged in LDS by issue_first (read with ds_read:
+    // no wait on the vector memory counter)
+    const int *tgt = reinterpret_cast<const int *>(smem + TGT_OFS + parity * (TILE_T * 4));
+    auto target_of = [&](int j, int t) {
+      return (t < a.T) ? tgt[wt * 128 + 32 * j + fr] : -1;
+    };
+    auto xor1i = [&](int x) { return __builtin_amdgcn_ds_bpermute((lane_e ^ 1) << 2, x); };
     if (!STATS) {
-      // Registers 4q .. 4q+3 hold four consecutive columns: one 16-byte
-      // store per lane when rows are 16-byte aligned (the two lane halves
-      // cover 32 contiguous bytes of a row), else element by element.
-      const bool vec = (a.V & 3) == 0 && ((uintptr_t)a.logits & 15) == 0;
+      // Registers 4q .. 4q+3 hold four consecutive columns.  Stores are raw
+      // buffer stores over one resource per 32-row group (at most 32 V
+      // floats: the host keeps V <= 2^24, so the size fits 2^31 bytes).  A
+      // row past T lies past the resource's size, and a column past V is
+      // given offset 2^31, so the hardware's range check drops both stores:
+      // no branch per element, and the accumulators stay in place.  With V a
+      // multiple of 4 and a 16-byte aligned output, each lane writes four
+      // columns per 16-byte store (the two lane halves cover 32 contiguous
+      // bytes of a row); otherwise (EX == 1, chosen by the host) one column
+      // per store.  The two are separate instantiations because the
+      // per-column offsets of the second would otherwise cost the first its
+      // registers; the arithmetic, and so every stored bit, is the same.
+      constexpr uint32_t DROP = 0x80000000u;
+      constexpr bool vec = EX == 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int t = t0 + wt * 128 + 32 * j + fr;
-        if (t >= a.T) continue;
-        float *row = a.logits + (size_t)t * a.V;
+        const int trow = t0 + wt * 128 + 32 * j;
+        const int rows = min(32, a.T - trow);
+        const __amdgpu_buffer_rsrc_t r_out = make_rsrc(
+            a.logits + (size_t)trow * a.V, rows > 0 ? (uint32_t)rows * (uint32_t)a.V * 4u : 0u);
+        const uint32_t rofs = (uint32_t)fr * (uint32_t)a.V * 4u;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int v4 = vbase + 32 * i + 8 * q + 4 * fk;
-            if (vec && v4 + 3 < a.V) {
-              float4 x;
-              x.x = acc[i][j][4 * q];
-              x.y = acc[i][j][4 * q + 1];
-              x.z = acc[i][j][4 * q + 2];
-              x.w = acc[i][j][4 * q + 3];
-              *(float4 *)(row + v4) = x;
+            if constexpr (vec) {
+              const uint32_t off = v4 < a.V ? rofs + 4u * (uint32_t)v4 : DROP;
+              __builtin_amdgcn_raw_buffer_store_b128(
+                  u32x4{__float_as_uint(acc[i][j][4 * q]), __float_as_uint(acc[i][j][4 * q + 1]),
+                        __float_as_uint(acc[i][j][4 * q + 2]),
+                        __float_as_uint(acc[i][j][4 * q + 3])},
+                  r_out, (int)off, 0, 0);
             } else {
 #pragma unroll
-              for (int rr = 0; rr < 4; ++rr)
-                if (v4 + rr < a.V) row[v4 + rr] = acc[i][j][4 * q + rr];
+              for (int rr = 0; rr < 4; ++rr) {
+                const int v = v4 + rr;
+                const uint32_t off = v < a.V ? rofs + 4u * (uint32_t)v : DROP;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][4 * q + rr]),
+                                                      r_out, (int)off, 0, 0);
+              }
             }
           }
       }
@@ -375,7 +429,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
         for (int j = 0; j < 4; ++j) {
           const int t = t0 + wt * 128 + 32 * j + fr;
           const bool trow = t < a.T;
-          const int y = trow ? a.targets[t] : -1;
+          const int y = trow ? target_of(j, t) : -1;
           const bool live = trow && y >= 0 && y < a.V;
           const float lse_t = live ? a.lse[t] : 0.0f;
           const float gs = live ? a.grad[t] * a.inv_tau : 0.0f;
@@ -408,7 +462,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
                 for (int rr = 0; rr < 4; rr += 2) {
                   const uint32_t mine = odd ? b[rr + 1] : b[rr];
                   const uint32_t give = odd ? b[rr] : b[rr + 1];
-                  const uint32_t got = (uint32_t)__shfl_xor((int)give, 1);
+                  const uint32_t got = (uint32_t)xor1i((int)give);
                   const int v = v4 + rr + (odd ? 1 : 0);
                   const int te = t & ~1;
                   const uint32_t pair = odd ? (got | (mine << 16)) : (mine | (got << 16));
@@ -419,27 +473,19 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
             }
         }
       } else {
-      if constexpr (EX == 1 || EX == 2) {
-        // The options, once per logit: one fp32 multiply (exact for
-        // inv_tau == 1), then the fp32 -> bf16 cast (nearest, ties to even)
-        // and back.
-        if (a.bf16_logits) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-              for (int r = 0; r < 16; ++r)
-                acc[i][j][r] = (float)(__bf16)(acc[i][j][r] * a.inv_tau);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) acc[i][j][r] = acc[i][j][r] * a.inv_tau;
+      // The options, applied to each logit where it is read (the same fp32
+      // multiply, exact for inv_tau == 1, then the fp32 -> bf16 cast,
+      // nearest, ties to even): the same values as rewriting the
+      // accumulators once, without the register pressure of writing back.
+      const float itau = a.inv_tau;
+      const bool rb16 = a.bf16_logits != 0;
+      auto xf = [&](float z) {
+        if constexpr (EX == 1 || EX == 2) {
+          z = z * itau;
+          if (rb16) z = (float)(__bf16)z;
         }
-      }
+        return z;
+      };
       auto stats_epilogue = [&](auto masked) {
         constexpr bool MASK = decltype(masked)::value;
         // Columns past the vocabulary end count as -inf: they add nothing to
@@ -457,9 +503,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const bool out = MASK && (32 * i + 8 * (r >> 2) + (r & 3) >= lim);
-              mx = fmaxf(mx, out ? -INFINITY : acc[i][j][r]);
+              mx = fmaxf(mx, out ? -INFINITY : xf(acc[i][j][r]));
             }
-          const float mo = __shfl_xor(mx, 32);
+          const float mo = xor32(mx);
           const float m2 = fk == 0 ? fmaxf(mx, mo) : fmaxf(mo, mx);
           // 2) sum of exp(z - m), same tree; m is taken as 0 when the whole
           //    tile is -inf so that such a tile adds exactly 0.  z == m gives
@@ -471,7 +517,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const bool out = MASK && (32 * i + 8 * (r >> 2) + (r & 3) >= lim);
-              const float z = out ? -INFINITY : acc[i][j][r];
+              const float z = out ? -INFINITY : xf(acc[i][j][r]);
               const float d = z - ms;
               const float e = __builtin_amdgcn_exp2f(d * LOG2E);
               sx = sx + e;
@@ -479,11 +525,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
               // adds -0 (d clamped to the finite range first)
               if constexpr (EX == 2) ux = ux + e * fmaxf(d, -FLT_MAX);
             }
-          const float so = __shfl_xor(sx, 32);
+          const float so = xor32(sx);
           const float s2 = fk == 0 ? sx + so : so + sx;
           float u2 = 0.0f;
           if constexpr (EX == 2) {
-            const float uo = __shfl_xor(ux, 32);
+            const float uo = xor32(ux);
             u2 = fk == 0 ? ux + uo : uo + ux;
           }
           // 3) tile-major [nST][T] statistics (coalesced over rows).
@@ -499,7 +545,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
           // 4) target capture: the one lane holding z[t][y[t]] writes xt[t],
           //    the value picked by a fixed select tree over its 64 values.
           // (targets are global ids; a weight slice starts at y_base)
-          const int y = (t < a.T) ? a.targets[t] - a.y_base : -1;
+          const int yt = target_of(j, t);
+          const int y = yt < 0 ? -1 : yt - a.y_base;
           const int rel = y - vbase;
           const bool hit = rel >= 0 && rel < STAT_V && ((rel >> 2) & 1) == fk;
           if (__any(hit)) {
@@ -522,7 +569,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
               for (int q = 0; q < (8 >> lvl); ++q)
                 sel[q] = bit ? sel[2 * q + 1] : sel[2 * q];
             }
-            if (hit) a.xt[t] = sel[0];
+            if (hit) a.xt[t] = xf(sel[0]);
           }
         }
       };
@@ -535,7 +582,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
       }  // EX != 3
     }
 
+    }  // epilogue scope
     if (Ln >= total) break;
+    parity ^= 1;
     L = Ln;
     m = mn;
     n = nn;
@@ -549,7 +598,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
 // workgroup per tile.
 template <bool STATS, bool PERSIST, int EX>
 __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[4 * STAGE_BYTES + PREFETCH_SINK];
+  __shared__ __attribute__((aligned(16))) char smem[TGT_OFS + 2 * TILE_T * 4];
   gemm_body<STATS, PERSIST, EX>(a, smem);
 }
 
@@ -717,7 +766,10 @@ hipError_t launch_gemm_logits(const GemmArgs &a, int workers, hipStream_t s) {
   const int tiles = a.nMT * a.nVT;
   int grid = workers >= 8 ? workers - workers % 8 : 8;
   if (grid > tiles) grid = tiles;
-  hipLaunchKernelGGL((gemm_kernel<false, true, 0>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
+  if ((a.V & 3) == 0 && ((uintptr_t)a.logits & 15) == 0)
+    hipLaunchKernelGGL((gemm_kernel<false, true, 0>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel<false, true, 1>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
   return hipGetLastError();
 }
 

@@ -119,6 +119,8 @@ def test_workspace_one_byte_short():
     (dict(hidden=None), rlk.RLK_ERR_NULL_POINTER),
     (dict(logits=FAKE + 2), rlk.RLK_ERR_MISALIGNED),
     (dict(T=0, logits=None, hidden=None, weight=None), rlk.RLK_OK),
+    (dict(V=(1 << 24) + 1), rlk.RLK_ERR_UNSUPPORTED),   # 32 output rows past 2^31 bytes
+    (dict(V=(1 << 24) + 1, T=0), rlk.RLK_ERR_UNSUPPORTED),
 ])
 def test_logits_error_paths(kw, status):
     a = dict(hidden=FAKE, ldh=256, weight=FAKE, ldw=256, logits=FAKE, T=4, H=256,

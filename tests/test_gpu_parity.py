@@ -77,6 +77,35 @@ def test_ragged_shapes(dev, T, H, V):
     assert np.all(np.abs(zg - zo) <= bound + 1e-30)
 
 
+@pytest.mark.parametrize("T,V", [(300, 1000), (257, 4133), (70, 3000), (1, 5), (600, 640)])
+def test_logits_store_paths_agree_and_stay_in_bounds(dev, T, V):
+    """The logits land at any 4-byte aligned address: a 16-byte aligned view
+    with V a multiple of 4 takes the 16-byte stores, a view one float further
+    on the one-column stores.  Both hold the same bits, and the floats around
+    each view (rows past T and columns past V are dropped, not redirected)
+    keep their sentinel."""
+    H = 128
+    c = synth.normal_case(f"store_{T}_{V}", 4100 + T + V, T, H, V,
+                          hidden_std=1.0, weight_std=0.1)
+    h, w = to_dev_bf16(c.hidden, dev), to_dev_bf16(c.weight, dev)
+    n = T * V
+    got = []
+    for start in (4, 1):          # 16-byte aligned, then 4-byte aligned
+        buf = torch.full((n + 8 + 64,), -7.25, dtype=torch.float32, device=dev)
+        view = buf[start:start + n].view(T, V)
+        rlk.rlk_logits(h, w, logits=view)
+        torch.cuda.synchronize()
+        b = buf.cpu().numpy()
+        assert np.all(b[:start] == -7.25) and np.all(b[start + n:] == -7.25), start
+        got.append(b[start:start + n].reshape(T, V).copy())
+    assert np.array_equal(got[0].view(np.uint32), got[1].view(np.uint32))
+    zo = orc.logits(c.hidden, c.weight)
+    habs = np.abs(synth.bf16_bits_to_f32(c.hidden).astype(np.float64))
+    wabs = np.abs(synth.bf16_bits_to_f32(c.weight).astype(np.float64))
+    bound = (H + 1) * 2.0 ** -24 * (habs @ wabs.T)
+    assert np.all(np.abs(got[0].astype(np.float64) - zo) <= bound + 1e-30)
+
+
 def test_strided_operands(dev):
     """Row strides larger than H (views into wider buffers)."""
     c = synth.normal_case("strided", 77, 40, 128, 700, weight_std=0.1)
