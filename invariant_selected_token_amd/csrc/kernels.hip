@@ -58,22 +58,20 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int STAGE_BYTES = TILE_V * TILE_K * 2;  // one operand, one stage
-constexpr int GROUP_M = 8;   // token tiles that walk the vocabulary together
+constexpr int GROUP_M = 4;   // token tiles that walk the vocabulary together
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 // Buffer resource word 3 for gfx9-family raw buffers (32-bit data format).
 constexpr int RSRC_WORD3 = 0x00020000;
-// s_waitcnt immediates for "vmcnt(0)" / "vmcnt(2)" only (expcnt and lgkmcnt
-// left at their maxima).
+// s_waitcnt immediate for "vmcnt(0)" only (expcnt and lgkmcnt left at their
+// maxima).
 constexpr int VMCNT0 = 0x0F70;
-// "vmcnt(2) lgkmcnt(0)" and "vmcnt(0) lgkmcnt(0)"
-constexpr int VMCNT2_LGKMCNT0 = 0x0072;
+// "vmcnt(1) lgkmcnt(0)" and "vmcnt(0) lgkmcnt(0)"
+constexpr int VMCNT1_LGKMCNT0 = 0x0071;
 constexpr int VMCNT0_LGKMCNT0 = 0x0070;
-// K blocks between an L2 prefetch and the block's direct-to-LDS load.
-#ifndef RLK_PREFETCH_AHEAD
-#define RLK_PREFETCH_AHEAD 1
-#endif
-constexpr int PREFETCH_AHEAD = RLK_PREFETCH_AHEAD;
+// K blocks between an L2 prefetch of weight rows and the block's
+// direct-to-LDS load.
+constexpr int PREFETCH_AHEAD = 1;
 // LDS bytes past the two stages that absorb the prefetch loads' data.
 constexpr int PREFETCH_SINK = 256;
 // Then a double buffer of the tiles' targets (2 x 256 int32).
@@ -174,19 +172,21 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? r_h : r_w, (lds_void *)dst, 16, gofs[op][i],
                                              (uint32_t)kb * (TILE_K * 2), 0, 0);
   };
-  // L2 prefetch of K block kb: one 4-byte load per 128-byte line, lane l
-  // touching row 32 (l >> 3) + 8 w + (l & 7) -- the 64 rows this wave's own
-  // loads of that block will cover.  The data lands in a scratch slot of LDS
-  // that nothing reads; the point is that the line is in L2 when the real
-  // load comes PREFETCH_AHEAD blocks later.  Past the end of a row or of the
-  // resource the load stays in bounds or reads nothing.
+  // L2 prefetch of the weight's K block kb: one 4-byte load per 128-byte
+  // line, lane l touching row 32 (l >> 3) + 8 w + (l & 7) -- the 64 rows
+  // this wave's own loads of that block will cover.  The data lands in a
+  // scratch slot of LDS that nothing reads; the point is that the line is in
+  // L2 when the real load comes PREFETCH_AHEAD blocks later.  Past the end of
+  // a row or of the resource the load stays in bounds or reads nothing.
+  // Only the weight is prefetched: it is streamed from HBM (far larger than
+  // the last-level cache), while the hidden rows of a few token tiles stay
+  // in the memory-side cache, where a prefetch costs the CU more in line
+  // requests than it saves in latency (measured).
   const int prow = 32 * (lane >> 3) + 8 * (tid >> 6) + (lane & 7);
   const uint32_t pofs_w = (uint32_t)(prow * a.ldw * 2);
-  const uint32_t pofs_h = (uint32_t)(prow * a.ldh * 2);
-  auto prefetch = [&](__amdgpu_buffer_rsrc_t r, int op, int kb) {
+  auto prefetch = [&](__amdgpu_buffer_rsrc_t r, int kb) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(smem + 4 * STAGE_BYTES), 4,
-                                             op ? pofs_h : pofs_w,
-                                             (uint32_t)kb * (TILE_K * 2), 0, 0);
+                                             pofs_w, (uint32_t)kb * (TILE_K * 2), 0, 0);
   };
   // A tile's first K block into stage 0, and its next blocks into L2.
   // Targets of a tile: one 4-byte direct-to-LDS load per wave (64 rows
@@ -203,10 +203,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) gload(r_w, r_h, 0, 0, q);
 #pragma unroll
-    for (int kp = 1; kp <= PREFETCH_AHEAD; ++kp) {
-      prefetch(r_w, 0, kp);
-      prefetch(r_h, 1, kp);
-    }
+    for (int kp = 1; kp <= PREFETCH_AHEAD; ++kp) prefetch(r_w, kp);
   };
 
   // Fragment reads: A (weight) rows wv*128 + 32 i + fr, B (hidden) rows
@@ -241,14 +238,13 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   // (16 per MFMA); the fixed instruction order below only decides what
   // overlaps with what: every MFMA of K step ks is followed by one read of
   // step ks + 1's fragments (first half) or one direct-to-LDS load of the
-  // next K block (second half, steps 0 and 1; step 2: the L2 prefetches).
+  // next K block (second half, steps 0 and 1; step 2: the L2 prefetch).
   // Half-way through step 3 the wave waits for its loads and the workgroup
   // meets at the barrier (the next block has landed; this block is no longer
   // read), then the next block's first fragments are read under the last
   // eight MFMAs.
   auto k_block = [&](int kb, auto stage, auto more, __amdgpu_buffer_rsrc_t r_w,
-                     __amdgpu_buffer_rsrc_t r_h, __amdgpu_buffer_rsrc_t p_w,
-                     __amdgpu_buffer_rsrc_t p_h) {
+                     __amdgpu_buffer_rsrc_t r_h, __amdgpu_buffer_rsrc_t p_w) {
     constexpr int st = decltype(stage)::value;    // == kb & 1
     constexpr bool MORE = decltype(more)::value;  // not the last K block
 #pragma unroll
@@ -259,8 +255,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
         mfma(cur, q);
         if (q < 8) fread(cur ^ 1, st, ks + 1, q);
         else if (MORE && ks < 2) gload(r_w, r_h, st ^ 1, kb + 1, 8 * ks + (q - 8));
-        else if (MORE && ks == 2 && q < 10 && PREFETCH_AHEAD > 0)
-          prefetch(q == 8 ? p_w : p_h, q - 8, kb + 1 + PREFETCH_AHEAD);
+        else if (MORE && ks == 2 && q == 8) prefetch(p_w, kb + 1 + PREFETCH_AHEAD);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -270,14 +265,14 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
       __builtin_amdgcn_sched_barrier(0);
     }
     if (MORE) {
-      // This wave's loads of the next block have landed (only the two
-      // prefetches issued after them may still be in flight) and its reads
-      // of this block are complete; then the workgroup barrier.  A plain
-      // s_barrier, not a fenced __syncthreads(), so that the prefetches are
-      // not waited for; the empty asm statements keep the compiler from
-      // moving memory accesses across it.
+      // This wave's loads of the next block have landed (only the
+      // prefetch issued after them may still be in flight) and its reads of
+      // this block are complete; then the workgroup barrier.  A plain
+      // s_barrier, not a fenced __syncthreads(), so that the prefetch is not
+      // waited for; the empty asm statements keep the compiler from moving
+      // memory accesses across it.
       asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_waitcnt(PREFETCH_AHEAD > 0 ? VMCNT2_LGKMCNT0 : VMCNT0_LGKMCNT0);
+      __builtin_amdgcn_s_waitcnt(VMCNT1_LGKMCNT0);
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
     }
@@ -321,11 +316,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
 #pragma unroll
     for (int w = 0; w < 8; ++w) fread(0, 0, 0, w);
     for (int kb = 0; kb + 2 < nk2; kb += 2) {
-      k_block(kb, S0{}, std::true_type{}, rw, rh, rw, rh);
-      k_block(kb + 1, S1{}, std::true_type{}, rw, rh, rw, rh);
+      k_block(kb, S0{}, std::true_type{}, rw, rh, rw);
+      k_block(kb + 1, S1{}, std::true_type{}, rw, rh, rw);
     }
-    k_block(nk2 - 2, S0{}, std::true_type{}, rw_last, rh_last, rw, rh);
-    k_block(nk2 - 1, S1{}, std::false_type{}, rw, rh, rw, rh);
+    k_block(nk2 - 2, S0{}, std::true_type{}, rw_last, rh_last, rw);
+    k_block(nk2 - 1, S1{}, std::false_type{}, rw, rh, rw);
 
     const int v0 = n * TILE_V;
     const int t0 = m * TILE_T;
