@@ -199,11 +199,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
           r_tgt, (lds_void *)(smem + TGT_OFS + par * (TILE_T * 4) + wave * 256), 4,
           (uint32_t)(lane * 4), (uint32_t)((tile_m * TILE_T + 64 * wave) * 4), 0, 0);
   };
-  auto issue_first = [&](__amdgpu_buffer_rsrc_t r_w, __amdgpu_buffer_rsrc_t r_h) {
+  auto issue_first = [&](__amdgpu_buffer_rsrc_t r_w, __amdgpu_buffer_rsrc_t r_h,
+                         __amdgpu_buffer_rsrc_t p_w) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) gload(r_w, r_h, 0, 0, q);
 #pragma unroll
-    for (int kp = 1; kp <= PREFETCH_AHEAD; ++kp) prefetch(r_w, kp);
+    for (int kp = 1; kp <= PREFETCH_AHEAD; ++kp) prefetch(p_w, kp);
   };
 
   // Fragment reads: A (weight) rows wv*128 + 32 i + fr, B (hidden) rows
@@ -294,12 +295,25 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
 
+  // The GROUP_M = 4 workgroups that share a weight tile run side by side on
+  // one XCD (token tiles 4g .. 4g + 3); each prefetches one quarter of the
+  // tile's rows, the quarter of its wave number m & 3, so every line is
+  // requested once per group instead of four times.  The other waves
+  // prefetch through the zero-size resource (no memory access).  A group
+  // with fewer token tiles (fewer than 4 in all, or the last group) keeps
+  // the whole prefetch in every workgroup.
+  auto pf_rsrc = [&](int mm, __amdgpu_buffer_rsrc_t r) {
+    const bool full_group = (mm & ~(GROUP_M - 1)) + GROUP_M <= a.nMT;
+    return (!full_group || wave == (mm & (GROUP_M - 1))) ? r : zero;
+  };
+  static_assert(GROUP_M == GEMM_THREADS / 64, "one prefetching wave per group member");
   int m, n;
   coords(L, m, n);
   __amdgpu_buffer_rsrc_t rw = rsrc_w(n), rh = rsrc_h(m);
+  __amdgpu_buffer_rsrc_t pw = pf_rsrc(m, rw);
   int parity = 0;
   stage_targets(m, 0);
-  issue_first(rw, rh);
+  issue_first(rw, rh, pw);
 
   for (;;) {
     const __amdgpu_buffer_rsrc_t rw_last = (nk & 1) ? zero : rw;
@@ -316,11 +330,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
 #pragma unroll
     for (int w = 0; w < 8; ++w) fread(0, 0, 0, w);
     for (int kb = 0; kb + 2 < nk2; kb += 2) {
-      k_block(kb, S0{}, std::true_type{}, rw, rh, rw);
-      k_block(kb + 1, S1{}, std::true_type{}, rw, rh, rw);
+      k_block(kb, S0{}, std::true_type{}, rw, rh, pw);
+      k_block(kb + 1, S1{}, std::true_type{}, rw, rh, pw);
     }
-    k_block(nk2 - 2, S0{}, std::true_type{}, rw_last, rh_last, rw);
-    k_block(nk2 - 1, S1{}, std::false_type{}, rw, rh, rw);
+    k_block(nk2 - 2, S0{}, std::true_type{}, rw_last, rh_last, pw);
+    k_block(nk2 - 1, S1{}, std::false_type{}, rw, rh, pw);
 
     const int v0 = n * TILE_V;
     const int t0 = m * TILE_T;
@@ -341,7 +355,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
       rwn = rsrc_w(nn);
       rhn = rsrc_h(mn);
       stage_targets(mn, parity ^ 1);
-      issue_first(rwn, rhn);
+      issue_first(rwn, rhn, pf_rsrc(mn, rwn));
     }
 
     // acc[i][j][r] holds z[t][v] for
@@ -585,6 +599,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     n = nn;
     rw = rwn;
     rh = rhn;
+    pw = pf_rsrc(m, rw);
   }
 }
 
