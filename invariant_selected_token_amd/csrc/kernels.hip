@@ -520,20 +520,30 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
           //    tile is -inf so that such a tile adds exactly 0.  z == m gives
           //    exp(0) = 1 exactly, so the sum is >= 1 when the max is finite.
           const float ms = (m2 == -INFINITY) ? 0.0f : m2;
+          // The 64 differences first, then the exponentials, then the sums
+          // in (i, r) order: the same operations and summation order as one
+          // value at a time, but the exponentials (a separate, quarter-rate
+          // pipe) no longer wait on each other's neighbours, so the
+          // compiler can issue the plain arithmetic under them.
           float sx = 0.0f, ux = 0.0f;
+          float dd[64], ee[64];
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const bool out = MASK && (32 * i + 8 * (r >> 2) + (r & 3) >= lim);
               const float z = out ? -INFINITY : xf(acc[i][j][r]);
-              const float d = z - ms;
-              const float e = __builtin_amdgcn_exp2f(d * LOG2E);
-              sx = sx + e;
-              // entropy partial: e (z - m); a -inf logit has e == 0 and
-              // adds -0 (d clamped to the finite range first)
-              if constexpr (EX == 2) ux = ux + e * fmaxf(d, -FLT_MAX);
+              dd[16 * i + r] = z - ms;
             }
+#pragma unroll
+          for (int k = 0; k < 64; ++k) ee[k] = __builtin_amdgcn_exp2f(dd[k] * LOG2E);
+#pragma unroll
+          for (int k = 0; k < 64; ++k) {
+            sx = sx + ee[k];
+            // entropy partial: e (z - m); a -inf logit has e == 0 and adds
+            // -0 (d clamped to the finite range first)
+            if constexpr (EX == 2) ux = ux + ee[k] * fmaxf(dd[k], -FLT_MAX);
+          }
           const float so = xor32(sx);
           const float s2 = fk == 0 ? sx + so : so + sx;
           float u2 = 0.0f;
