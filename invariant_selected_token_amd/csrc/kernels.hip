@@ -237,9 +237,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
 
   // One K block of the main loop.  Each accumulator advances in increasing k
   // (16 per MFMA); the fixed instruction order below only decides what
-  // overlaps with what: every MFMA of K step ks is followed by one read of
-  // step ks + 1's fragments (first half) or one direct-to-LDS load of the
-  // next K block (second half, steps 0 and 1; step 2: the L2 prefetch).
+  // overlaps with what: each of the first eight MFMAs of K step ks is
+  // followed by one read of step ks + 1's fragments, and every second MFMA
+  // of steps 0 and 1 (the odd ones) by one direct-to-LDS load of the next K
+  // block, so the sixteen loads are issued early but never in bursts (a
+  // burst stalls the wave's in-order issue, and with it the next MFMA, until
+  // the texture path takes the load); step 2 issues the L2 prefetch.
   // Half-way through step 3 the wave waits for its loads and the workgroup
   // meets at the barrier (the next block has landed; this block is no longer
   // read), then the next block's first fragments are read under the last
@@ -255,7 +258,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
       for (int q = 0; q < 16; ++q) {
         mfma(cur, q);
         if (q < 8) fread(cur ^ 1, st, ks + 1, q);
-        else if (MORE && ks < 2) gload(r_w, r_h, st ^ 1, kb + 1, 8 * ks + (q - 8));
+        if (MORE && ks < 2 && (q & 1)) gload(r_w, r_h, st ^ 1, kb + 1, 8 * ks + (q >> 1));
         else if (MORE && ks == 2 && q == 8) prefetch(p_w, kb + 1 + PREFETCH_AHEAD);
         __builtin_amdgcn_sched_barrier(0);
       }
