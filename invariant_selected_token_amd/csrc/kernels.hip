@@ -126,12 +126,12 @@ __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1
 template <bool STATS, bool PERSIST, int EX>
 __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
   const int wv = wave & 1;   // vocabulary half of the tile
   const int wt = wave >> 1;  // token half of the tile
-  const int fr = lane & 31;  // MFMA row / column within a 32-block
-  const int fk = lane >> 5;  // which 8-wide K slice of a 16-wide MFMA step
+  // Lane-dependent values (MFMA row fr = lane & 31, K slice fk = lane >> 5,
+  // load and read offsets) are formed where they are used, from a fresh
+  // lane id, so that none is live across both the K loop and the epilogue.
 
   const int total = a.nMT * a.nVT;
   int L = blockIdx.x;
@@ -155,20 +155,19 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     return make_rsrc(a.hidden + (size_t)t0 * a.ldh,
                      (uint32_t)(min(TILE_T, a.T - t0) * a.ldh * 2));
   };
-  const int lrow = 8 * (tid >> 6) + (lane >> 3);
-  const int lchunk = (lane & 7) ^ (lane >> 3) ^ ((tid >> 6) & 1);
-  uint32_t gofs[2][8];  // [operand][load]
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    gofs[0][i] = (uint32_t)((lrow + 32 * i) * a.ldw * 2 + lchunk * 16);
-    gofs[1][i] = (uint32_t)((lrow + 32 * i) * a.ldh * 2 + lchunk * 16);
-  }
+  uint32_t gofs[2][8];  // [operand][load]; set by set_offsets below
   typedef __attribute__((address_space(3))) void lds_void;
   // Load q (0..15) of K block kb into `stage`: operand q & 1, row group q >> 1.
+  // This wave's LDS slot; each K block makes it opaque to the compiler
+  // (an empty asm), so the 32 destinations below are formed from it by
+  // scalar adds where they are used instead of being held in 32 scalar
+  // registers across the loop.
+  typedef __attribute__((address_space(3))) char lds_char;
+  lds_char *lds_wave = (lds_char *)smem + wave * 1024;
   auto gload = [&](__amdgpu_buffer_rsrc_t r_w, __amdgpu_buffer_rsrc_t r_h, int stage,
                    int kb, int q) {
     const int op = q & 1, i = q >> 1;
-    char *dst = smem + stage * (2 * STAGE_BYTES) + op * STAGE_BYTES + (4 * i + wave) * 1024;
+    lds_char *dst = lds_wave + stage * (2 * STAGE_BYTES) + op * STAGE_BYTES + (4 * i) * 1024;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? r_h : r_w, (lds_void *)dst, 16, gofs[op][i],
                                              (uint32_t)kb * (TILE_K * 2), 0, 0);
   };
@@ -182,8 +181,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   // the last-level cache), while the hidden rows of a few token tiles stay
   // in the memory-side cache, where a prefetch costs the CU more in line
   // requests than it saves in latency (measured).
-  const int prow = 32 * (lane >> 3) + 8 * (tid >> 6) + (lane & 7);
-  const uint32_t pofs_w = (uint32_t)(prow * a.ldw * 2);
+  uint32_t pofs_w;
   auto prefetch = [&](__amdgpu_buffer_rsrc_t r, int kb) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(smem + 4 * STAGE_BYTES), 4,
                                              pofs_w, (uint32_t)kb * (TILE_K * 2), 0, 0);
@@ -193,11 +191,17 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   // each) into the tile's half of a double buffer; rows past T read 0.
   const __amdgpu_buffer_rsrc_t r_tgt =
       make_rsrc(a.targets, STATS ? (uint32_t)(a.T * 4) : 0u);
+  // The lane offset is formed afresh (an asm the compiler cannot merge with
+  // the set-up's): kept across the K loop it would be spilled, and its
+  // reload would wait for every load in flight.
   auto stage_targets = [&](int tile_m, int par) {
-    if (STATS)
+    if (STATS) {
+      int l;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           r_tgt, (lds_void *)(smem + TGT_OFS + par * (TILE_T * 4) + wave * 256), 4,
-          (uint32_t)(lane * 4), (uint32_t)((tile_m * TILE_T + 64 * wave) * 4), 0, 0);
+          (uint32_t)(l * 4), (uint32_t)((tile_m * TILE_T + 64 * wave) * 4), 0, 0);
+    }
   };
   auto issue_first = [&](__amdgpu_buffer_rsrc_t r_w, __amdgpu_buffer_rsrc_t r_h,
                          __amdgpu_buffer_rsrc_t p_w) {
@@ -211,15 +215,33 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   // wt*128 + 32 j + fr, 16-byte chunk 2 ks + fk of the 64-wide K step.  Byte
   // addresses per (stage, ks); the block index i or j adds i * 4096.
   uint32_t ra[2][4], rb[2][4];
+  // The per-lane offsets of the loads, the prefetch and the fragment reads,
+  // formed at the start of every tile from a lane id the compiler cannot
+  // merge with an earlier one: they are then dead during the epilogue
+  // instead of held (or spilled and reloaded) across it.
+  auto set_offsets = [&]() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    const int lrow = 8 * wave + (l >> 3);
+    const int lchunk = (l & 7) ^ (l >> 3) ^ (wave & 1);
 #pragma unroll
-  for (int st = 0; st < 2; ++st)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      // swz(32 i + fr) == swz(fr)
-      const uint32_t x = (uint32_t)(((2 * ks + fk) ^ swz(fr)) << 4);
-      ra[st][ks] = st * (2 * STAGE_BYTES) + (wv * 128 + fr) * 128 + x;
-      rb[st][ks] = st * (2 * STAGE_BYTES) + STAGE_BYTES + (wt * 128 + fr) * 128 + x;
+    for (int i = 0; i < 8; ++i) {
+      gofs[0][i] = (uint32_t)((lrow + 32 * i) * a.ldw * 2 + lchunk * 16);
+      gofs[1][i] = (uint32_t)((lrow + 32 * i) * a.ldh * 2 + lchunk * 16);
     }
+    const int prow = 32 * (l >> 3) + 8 * wave + (l & 7);
+    pofs_w = (uint32_t)(prow * a.ldw * 2);
+    const int lr = l & 31, lk = l >> 5;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        // swz(32 i + fr) == swz(fr)
+        const uint32_t x = (uint32_t)(((2 * ks + lk) ^ swz(lr)) << 4);
+        ra[st][ks] = st * (2 * STAGE_BYTES) + (wv * 128 + lr) * 128 + x;
+        rb[st][ks] = st * (2 * STAGE_BYTES) + STAGE_BYTES + (wt * 128 + lr) * 128 + x;
+      }
+  };
   bf16x8 fa[2][4], fb[2][4];
   // Read number w (0..7) of the fragments of (stage, ks) into set `buf`, in
   // the order the MFMAs consume them: A0, B0, B1, B2, B3, A1, A2, A3.
@@ -246,11 +268,18 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   // Half-way through step 3 the wave waits for its loads and the workgroup
   // meets at the barrier (the next block has landed; this block is no longer
   // read), then the next block's first fragments are read under the last
-  // eight MFMAs.
+  // eight MFMAs.  The tile's last block (MORE false) has no next block of
+  // its own: its load slots carry the next tile's first block into the other
+  // stage (r_w, r_h, p_w then name the next tile), which is free once the
+  // barrier of the block before has passed.  p_w and kp name the weight
+  // block the L2 prefetch fetches: kb + 1 + PREFETCH_AHEAD of this tile, and
+  // in the last two blocks the next tile's blocks 0 and 1.
   auto k_block = [&](int kb, auto stage, auto more, __amdgpu_buffer_rsrc_t r_w,
-                     __amdgpu_buffer_rsrc_t r_h, __amdgpu_buffer_rsrc_t p_w) {
+                     __amdgpu_buffer_rsrc_t r_h, __amdgpu_buffer_rsrc_t p_w, int kp) {
     constexpr int st = decltype(stage)::value;    // == kb & 1
     constexpr bool MORE = decltype(more)::value;  // not the last K block
+    const int kl = MORE ? kb + 1 : 0;             // K block the loads fetch
+    asm volatile("" : "+s"(lds_wave));
 #pragma unroll
     for (int ks = 0; ks < 3; ++ks) {
       const int cur = ks & 1;
@@ -258,8 +287,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
       for (int q = 0; q < 16; ++q) {
         mfma(cur, q);
         if (q < 8) fread(cur ^ 1, st, ks + 1, q);
-        if (MORE && ks < 2 && (q & 1)) gload(r_w, r_h, st ^ 1, kb + 1, 8 * ks + (q >> 1));
-        else if (MORE && ks == 2 && q == 8) prefetch(p_w, kb + 1 + PREFETCH_AHEAD);
+        if (ks < 2 && (q & 1)) gload(r_w, r_h, st ^ 1, kl, 8 * ks + (q >> 1));
+        else if (ks == 2 && q == 8) prefetch(p_w, kp);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -315,6 +344,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   __amdgpu_buffer_rsrc_t rw = rsrc_w(n), rh = rsrc_h(m);
   __amdgpu_buffer_rsrc_t pw = pf_rsrc(m, rw);
   int parity = 0;
+  set_offsets();
   stage_targets(m, 0);
   issue_first(rw, rh, pw);
 
@@ -327,17 +357,31 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-    // The tile's first block (issued before the previous epilogue, or above).
+    set_offsets();
+    // The tile's first block (issued by the previous tile's last K block, or
+    // above).
     __builtin_amdgcn_s_waitcnt(VMCNT0);
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < 8; ++w) fread(0, 0, 0, w);
     for (int kb = 0; kb + 2 < nk2; kb += 2) {
-      k_block(kb, S0{}, std::true_type{}, rw, rh, pw);
-      k_block(kb + 1, S1{}, std::true_type{}, rw, rh, pw);
+      k_block(kb, S0{}, std::true_type{}, rw, rh, pw, kb + 1 + PREFETCH_AHEAD);
+      k_block(kb + 1, S1{}, std::true_type{}, rw, rh, pw, kb + 2 + PREFETCH_AHEAD);
     }
-    k_block(nk2 - 2, S0{}, std::true_type{}, rw_last, rh_last, pw);
-    k_block(nk2 - 1, S1{}, std::false_type{}, rw, rh, pw);
+    // The next tile (its first two weight blocks are prefetched by the last
+    // two blocks of this one) and its targets; the last block loads its
+    // first block into stage 0.  After the last tile those loads and
+    // prefetches go through the zero-size resource and read nothing.
+    const int Ln = PERSIST ? L + (int)gridDim.x : total;
+    const bool more_tiles = Ln < total;
+    int mn = m, nn = n;
+    if (more_tiles) coords(Ln, mn, nn);
+    const __amdgpu_buffer_rsrc_t rwn = more_tiles ? rsrc_w(nn) : zero;
+    const __amdgpu_buffer_rsrc_t rhn = more_tiles ? rsrc_h(mn) : zero;
+    const __amdgpu_buffer_rsrc_t pwn = pf_rsrc(mn, rwn);
+    k_block(nk2 - 2, S0{}, std::true_type{}, rw_last, rh_last, pwn, 0);
+    stage_targets(mn, parity ^ 1);   // after the last tile: its own, unused
+    k_block(nk2 - 1, S1{}, std::false_type{}, rwn, rhn, pwn, 1);
 
     const int v0 = n * TILE_V;
     const int t0 = m * TILE_T;
@@ -345,21 +389,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     // merge with the set-up's) so that nothing from the set-up stays live
     // across the K loop or is spilled: a reload from scratch here would be
     // a vector memory op, and waiting for it would also wait for the next
-    // tile's loads issued below.
+    // tile's loads issued by the last K block.
     int lane_e;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
-    // Stage 0 was last read before the barrier of block nk2 - 2, so the
-    // next tile's first block can go there now, under this epilogue.
-    const int Ln = PERSIST ? L + (int)gridDim.x : total;
-    int mn = 0, nn = 0;
-    __amdgpu_buffer_rsrc_t rwn = rw, rhn = rh;
-    if (Ln < total) {
-      coords(Ln, mn, nn);
-      rwn = rsrc_w(nn);
-      rhn = rsrc_h(mn);
-      stage_targets(mn, parity ^ 1);
-      issue_first(rwn, rhn, pf_rsrc(mn, rwn));
-    }
 
     // acc[i][j][r] holds z[t][v] for
     //   v = v0 + wv*128 + 32 i + 8 (r >> 2) + 4 fk + (r & 3)
@@ -371,8 +403,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     auto xor32 = [&](float x) {
       return __int_as_float(__builtin_amdgcn_ds_bpermute((lane_e ^ 32) << 2, __float_as_int(x)));
     };
-    // this tile's targets, staged in LDS by issue_first (read with ds_read:
-    // no wait on the vector memory counter)
+    // this tile's targets, staged in LDS before its K loop (read with
+    // ds_read: no wait on the vector memory counter)
     const int *tgt = reinterpret_cast<const int *>(smem + TGT_OFS + parity * (TILE_T * 4));
     auto target_of = [&](int j, int t) {
       return (t < a.T) ? tgt[wt * 128 + 32 * j + fr] : -1;
@@ -523,29 +555,30 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
           //    tile is -inf so that such a tile adds exactly 0.  z == m gives
           //    exp(0) = 1 exactly, so the sum is >= 1 when the max is finite.
           const float ms = (m2 == -INFINITY) ? 0.0f : m2;
-          // The 64 differences first, then the exponentials, then the sums
-          // in (i, r) order: the same operations and summation order as one
-          // value at a time, but the exponentials (a separate, quarter-rate
-          // pipe) no longer wait on each other's neighbours, so the
-          // compiler can issue the plain arithmetic under them.
+          // Per block i, the 16 differences first, then the exponentials,
+          // then the sums in r order: the same operations and summation
+          // order as one value at a time, but no exponential waits on the
+          // one before it or feeds the next add directly (that latency, not
+          // the arithmetic, was what the one-at-a-time chain paid).
           float sx = 0.0f, ux = 0.0f;
-          float dd[64], ee[64];
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 4; ++i) {
+            float dd[16], ee[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const bool out = MASK && (32 * i + 8 * (r >> 2) + (r & 3) >= lim);
               const float z = out ? -INFINITY : xf(acc[i][j][r]);
-              dd[16 * i + r] = z - ms;
+              dd[r] = z - ms;
             }
 #pragma unroll
-          for (int k = 0; k < 64; ++k) ee[k] = __builtin_amdgcn_exp2f(dd[k] * LOG2E);
+            for (int r = 0; r < 16; ++r) ee[r] = __builtin_amdgcn_exp2f(dd[r] * LOG2E);
 #pragma unroll
-          for (int k = 0; k < 64; ++k) {
-            sx = sx + ee[k];
-            // entropy partial: e (z - m); a -inf logit has e == 0 and adds
-            // -0 (d clamped to the finite range first)
-            if constexpr (EX == 2) ux = ux + ee[k] * fmaxf(dd[k], -FLT_MAX);
+            for (int r = 0; r < 16; ++r) {
+              sx = sx + ee[r];
+              // entropy partial: e (z - m); a -inf logit has e == 0 and
+              // adds -0 (d clamped to the finite range first)
+              if constexpr (EX == 2) ux = ux + ee[r] * fmaxf(dd[r], -FLT_MAX);
+            }
           }
           const float so = xor32(sx);
           const float s2 = fk == 0 ? sx + so : so + sx;
@@ -605,7 +638,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     }
 
     }  // epilogue scope
-    if (Ln >= total) break;
+    if (!more_tiles) {
+      // nothing of this wave's may still be writing LDS when it ends
+      __builtin_amdgcn_s_waitcnt(VMCNT0);
+      break;
+    }
     parity ^= 1;
     L = Ln;
     m = mn;
