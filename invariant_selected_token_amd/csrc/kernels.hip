@@ -66,8 +66,9 @@ constexpr int RSRC_WORD3 = 0x00020000;
 // s_waitcnt immediate for "vmcnt(0)" only (expcnt and lgkmcnt left at their
 // maxima).
 constexpr int VMCNT0 = 0x0F70;
-// "vmcnt(1) lgkmcnt(0)" and "vmcnt(0) lgkmcnt(0)"
+// "vmcnt(1) lgkmcnt(0)", "vmcnt(2) lgkmcnt(0)" and "vmcnt(0) lgkmcnt(0)"
 constexpr int VMCNT1_LGKMCNT0 = 0x0071;
+constexpr int VMCNT2_LGKMCNT0 = 0x0072;
 constexpr int VMCNT0_LGKMCNT0 = 0x0070;
 // K blocks between an L2 prefetch of weight rows and the block's
 // direct-to-LDS load.
@@ -181,10 +182,18 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   // the last-level cache), while the hidden rows of a few token tiles stay
   // in the memory-side cache, where a prefetch costs the CU more in line
   // requests than it saves in latency (measured).
-  uint32_t pofs_w;
+  uint32_t pofs_w, pofs_h;
   auto prefetch = [&](__amdgpu_buffer_rsrc_t r, int kb) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(smem + 4 * STAGE_BYTES), 4,
                                              pofs_w, (uint32_t)kb * (TILE_K * 2), 0, 0);
+  };
+  // The plain (store) GEMM also prefetches its hidden-role rows, the same
+  // way, when pf_hidden is set (the backward's products, whose hidden-role
+  // operand streams from HBM); otherwise through the zero-size resource.
+  // Two prefetches in flight then, always, so the wait count is fixed.
+  auto prefetch_h = [&](__amdgpu_buffer_rsrc_t r, int kb) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(smem + 4 * STAGE_BYTES), 4,
+                                             pofs_h, (uint32_t)kb * (TILE_K * 2), 0, 0);
   };
   // A tile's first K block into stage 0, and its next blocks into L2.
   // Targets of a tile: one 4-byte direct-to-LDS load per wave (64 rows
@@ -204,11 +213,14 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     }
   };
   auto issue_first = [&](__amdgpu_buffer_rsrc_t r_w, __amdgpu_buffer_rsrc_t r_h,
-                         __amdgpu_buffer_rsrc_t p_w) {
+                         __amdgpu_buffer_rsrc_t p_w, __amdgpu_buffer_rsrc_t p_h) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) gload(r_w, r_h, 0, 0, q);
 #pragma unroll
-    for (int kp = 1; kp <= PREFETCH_AHEAD; ++kp) prefetch(p_w, kp);
+    for (int kp = 1; kp <= PREFETCH_AHEAD; ++kp) {
+      prefetch(p_w, kp);
+      if constexpr (!STATS) prefetch_h(p_h, kp);
+    }
   };
 
   // Fragment reads: A (weight) rows wv*128 + 32 i + fr, B (hidden) rows
@@ -231,6 +243,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     }
     const int prow = 32 * (l >> 3) + 8 * wave + (l & 7);
     pofs_w = (uint32_t)(prow * a.ldw * 2);
+    pofs_h = (uint32_t)(prow * a.ldh * 2);
     const int lr = l & 31, lk = l >> 5;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
@@ -275,7 +288,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   // block the L2 prefetch fetches: kb + 1 + PREFETCH_AHEAD of this tile, and
   // in the last two blocks the next tile's blocks 0 and 1.
   auto k_block = [&](int kb, auto stage, auto more, __amdgpu_buffer_rsrc_t r_w,
-                     __amdgpu_buffer_rsrc_t r_h, __amdgpu_buffer_rsrc_t p_w, int kp) {
+                     __amdgpu_buffer_rsrc_t r_h, __amdgpu_buffer_rsrc_t p_w,
+                     __amdgpu_buffer_rsrc_t p_h, int kp) {
     constexpr int st = decltype(stage)::value;    // == kb & 1
     constexpr bool MORE = decltype(more)::value;  // not the last K block
     const int kl = MORE ? kb + 1 : 0;             // K block the loads fetch
@@ -288,7 +302,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
         mfma(cur, q);
         if (q < 8) fread(cur ^ 1, st, ks + 1, q);
         if (ks < 2 && (q & 1)) gload(r_w, r_h, st ^ 1, kl, 8 * ks + (q >> 1));
-        else if (ks == 2 && q == 8) prefetch(p_w, kp);
+        else if (ks == 2 && q == 8) {
+          prefetch(p_w, kp);
+          if constexpr (!STATS) prefetch_h(p_h, kp);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -305,7 +322,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
       // waited for; the empty asm statements keep the compiler from moving
       // memory accesses across it.
       asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_waitcnt(VMCNT1_LGKMCNT0);
+      __builtin_amdgcn_s_waitcnt(STATS ? VMCNT1_LGKMCNT0 : VMCNT2_LGKMCNT0);
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
     }
@@ -343,10 +360,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   coords(L, m, n);
   __amdgpu_buffer_rsrc_t rw = rsrc_w(n), rh = rsrc_h(m);
   __amdgpu_buffer_rsrc_t pw = pf_rsrc(m, rw);
+  auto pfh_rsrc = [&](__amdgpu_buffer_rsrc_t r) { return a.pf_hidden ? r : zero; };
+  __amdgpu_buffer_rsrc_t ph = pfh_rsrc(rh);
   int parity = 0;
   set_offsets();
   stage_targets(m, 0);
-  issue_first(rw, rh, pw);
+  issue_first(rw, rh, pw, ph);
 
   for (;;) {
     const __amdgpu_buffer_rsrc_t rw_last = (nk & 1) ? zero : rw;
@@ -365,8 +384,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
 #pragma unroll
     for (int w = 0; w < 8; ++w) fread(0, 0, 0, w);
     for (int kb = 0; kb + 2 < nk2; kb += 2) {
-      k_block(kb, S0{}, std::true_type{}, rw, rh, pw, kb + 1 + PREFETCH_AHEAD);
-      k_block(kb + 1, S1{}, std::true_type{}, rw, rh, pw, kb + 2 + PREFETCH_AHEAD);
+      k_block(kb, S0{}, std::true_type{}, rw, rh, pw, ph, kb + 1 + PREFETCH_AHEAD);
+      k_block(kb + 1, S1{}, std::true_type{}, rw, rh, pw, ph, kb + 2 + PREFETCH_AHEAD);
     }
     // The next tile (its first two weight blocks are prefetched by the last
     // two blocks of this one) and its targets; the last block loads its
@@ -379,9 +398,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     const __amdgpu_buffer_rsrc_t rwn = more_tiles ? rsrc_w(nn) : zero;
     const __amdgpu_buffer_rsrc_t rhn = more_tiles ? rsrc_h(mn) : zero;
     const __amdgpu_buffer_rsrc_t pwn = pf_rsrc(mn, rwn);
-    k_block(nk2 - 2, S0{}, std::true_type{}, rw_last, rh_last, pwn, 0);
+    const __amdgpu_buffer_rsrc_t phn = pfh_rsrc(rhn);
+    k_block(nk2 - 2, S0{}, std::true_type{}, rw_last, rh_last, pwn, phn, 0);
     stage_targets(mn, parity ^ 1);   // after the last tile: its own, unused
-    k_block(nk2 - 1, S1{}, std::false_type{}, rwn, rhn, pwn, 1);
+    k_block(nk2 - 1, S1{}, std::false_type{}, rwn, rhn, pwn, phn, 1);
 
     const int v0 = n * TILE_V;
     const int t0 = m * TILE_T;
@@ -650,6 +670,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     rw = rwn;
     rh = rhn;
     pw = pf_rsrc(m, rw);
+    ph = pfh_rsrc(rh);
   }
 }
 
