@@ -383,6 +383,23 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < 8; ++w) fread(0, 0, 0, w);
+    // The logit gradient's per-row inputs (lse, upstream gradient), loaded
+    // now so that their latency hides under the first K block: issued in the
+    // epilogue they would wait behind the next tile's operand loads (vector
+    // memory completes in order).
+    float lse_r[4] = {0.0f, 0.0f, 0.0f, 0.0f}, grad_r[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (EX == 3) {
+      int l;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = m * TILE_T + wt * 128 + 32 * j + (l & 31);
+        if (t < a.T) {
+          lse_r[j] = a.lse[t];
+          grad_r[j] = a.grad[t];
+        }
+      }
+    }
     for (int kb = 0; kb + 2 < nk2; kb += 2) {
       k_block(kb, S0{}, std::true_type{}, rw, rh, pw, ph, kb + 1 + PREFETCH_AHEAD);
       k_block(kb + 1, S1{}, std::true_type{}, rw, rh, pw, ph, kb + 2 + PREFETCH_AHEAD);
@@ -429,7 +446,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     auto target_of = [&](int j, int t) {
       return (t < a.T) ? tgt[wt * 128 + 32 * j + fr] : -1;
     };
-    auto xor1i = [&](int x) { return __builtin_amdgcn_ds_bpermute((lane_e ^ 1) << 2, x); };
+    // neighbouring-lane exchange (lane l gets lane l ^ 1's value): a DPP quad
+    // permutation [1, 0, 3, 2] in the VALU, no LDS round trip
+    auto xor1i = [&](int x) { return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false); };
     if (!STATS) {
       // Registers 4q .. 4q+3 hold four consecutive columns.  Stores are raw
       // buffer stores over one resource per 32-row group (at most 32 V
@@ -495,8 +514,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
           const bool trow = t < a.T;
           const int y = trow ? target_of(j, t) : -1;
           const bool live = trow && y >= 0 && y < a.V;
-          const float lse_t = live ? a.lse[t] : 0.0f;
-          const float gs = live ? a.grad[t] * a.inv_tau : 0.0f;
+          const float lse_t = live ? lse_r[j] : 0.0f;
+          const float gs = live ? grad_r[j] * a.inv_tau : 0.0f;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
