@@ -17,10 +17,12 @@ constexpr int STAT_V = 128;
 constexpr int TILE_T = 256;
 constexpr int TILE_K = 64;
 constexpr int GEMM_THREADS = 256;
-// The vocabulary merge: waves per workgroup, each folding one contiguous
-// group of vocabulary tiles; 64 rows per workgroup (one per lane).
+// The vocabulary merge: MERGE_GROUPS contiguous groups of vocabulary tiles
+// per row (part of the numerical contract), MERGE_ROWS rows per workgroup;
+// groups of up to MERGE_KEEP tiles are held in registers.
 constexpr int MERGE_GROUPS = 16;
-constexpr int MERGE_ROWS = 64;
+constexpr int MERGE_ROWS = 32;
+constexpr int MERGE_KEEP = 80;
 constexpr int MERGE_UNROLL = 16;
 constexpr int COMPARE_THREADS = 256;
 

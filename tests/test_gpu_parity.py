@@ -311,6 +311,32 @@ def test_maximum_sizes(dev, T, H, V):
     _assert_close(lse, ref_lse, f"lse {T}x{H}x{V}")
 
 
+@pytest.mark.parametrize("V", [163_840, 163_841, 200_000])
+def test_merge_register_limit(dev, V):
+    """The merge holds a row's group of statistics tiles in registers while the
+    group has at most 80 tiles (16 groups: V <= 163 840) and reads them in
+    chunks beyond that; both must fold to the oracle's lse, logp and entropy,
+    and the rows with and without the entropy partials must share their bits."""
+    T, H = 40, 64
+    c = synth.normal_case(f"merge_limit_{V}", 771 + V % 1000, T, H, V)
+    y = c.targets.copy()
+    y[0], y[1] = 0, V - 1
+    h, w, yd = to_dev_bf16(c.hidden, dev), to_dev_bf16(c.weight, dev), to_dev_i32(y, dev)
+    lp, lse = _run(h, w, yd)
+    lp2, lse2, ent = rlk.rlk_selected_logp_ex(h, w, yd, inv_temperature=0.9, entropy=True)
+    lp1, lse1, _ = rlk.rlk_selected_logp_ex(h, w, yd, inv_temperature=0.9, entropy=False)
+    torch.cuda.synchronize()
+    ref_lp, ref_lse = orc.selected_logp(c.hidden, c.weight, y)
+    _assert_close(lp, ref_lp, f"V={V} logp")
+    _assert_close(lse, ref_lse, f"V={V} lse")
+    rlp, rlse, rent = orc.selected_logp_ex(c.hidden, c.weight, y, inv_tau=0.9)
+    _assert_close(lp2.cpu().numpy().astype(np.float64), rlp, f"V={V} logp tau")
+    _assert_close(lse2.cpu().numpy().astype(np.float64), rlse, f"V={V} lse tau")
+    _assert_close(ent.cpu().numpy().astype(np.float64), rent, f"V={V} entropy")
+    assert torch.equal(lp1.view(torch.int32), lp2.view(torch.int32))
+    assert torch.equal(lse1.view(torch.int32), lse2.view(torch.int32))
+
+
 def test_empty_batches_through_every_entry_point(tiny, dev):
     """T = 0: every call returns empty results (grad_weight zero-filled)."""
     h0, y0 = tiny.hidden[:0], tiny.targets[:0]
