@@ -508,52 +508,102 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
         // rounded to bf16 (nearest, ties to even) as the operand of the two
         // gradient GEMMs.  Rows past T, columns past V and rows whose target
         // is outside [0, V) hold 0.
+        //
+        // Each wave stages its 128 x 128 block of dz, 64 token rows at a
+        // time, in 16 KiB of the operand buffer's stage 1 (free once every
+        // wave is past the tile's last K block; the next tile's first block
+        // lands in stage 0), then writes dz [T][ld_dz] as 16-byte row pieces
+        // and dz^T [V][ld_dzt] as 16-byte pieces of 8 token rows, read back
+        // with the transposing LDS read: 64 full stores per wave and tile
+        // instead of 192 narrow scattered ones.  Staging row r holds the
+        // 128 columns as 32 chunks of 4 (8 bytes); chunk c sits at slot
+        // c ^ sw(r), sw(r) = 4 (r & 3) + ((r >> 2) & 3), which keeps the
+        // writes (16 rows, one chunk), the row reads (one row, 16 x 16
+        // bytes) and the transposing reads (4 rows x 4 chunks) free of bank
+        // conflicts.
+        typedef __attribute__((address_space(3))) char lds_c;
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) v4s lds_v4s;
+        lds_c *stg = (lds_c *)smem + 2 * STAGE_BYTES + wave * (STAGE_BYTES / 2);
+        auto sw = [](int r) { return ((r & 3) << 2) | ((r >> 2) & 3); };
+        auto slot = [&](int r, int c) { return stg + r * 256 + ((c ^ sw(r)) << 3); };
+        // every wave's fragment reads of stage 1 are done
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int t = t0 + wt * 128 + 32 * j + fr;
-          const bool trow = t < a.T;
-          const int y = trow ? target_of(j, t) : -1;
-          const bool live = trow && y >= 0 && y < a.V;
-          const float lse_t = live ? lse_r[j] : 0.0f;
-          const float gs = live ? grad_r[j] * a.inv_tau : 0.0f;
+        for (int p = 0; p < 2; ++p) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int jj = 0; jj < 2; ++jj) {
+            const int j = 2 * p + jj;
+            const int t = t0 + wt * 128 + 32 * j + fr;
+            const bool trow = t < a.T;
+            const int y = trow ? target_of(j, t) : -1;
+            const bool live = trow && y >= 0 && y < a.V;
+            const float lse_t = live ? lse_r[j] : 0.0f;
+            const float gs = live ? grad_r[j] * a.inv_tau : 0.0f;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int v4 = vbase + 32 * i + 8 * q + 4 * fk;   // 4 consecutive columns
-              uint16_t b[4];
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-              for (int rr = 0; rr < 4; ++rr) {
-                const int v = v4 + rr;
-                const float zs = acc[i][j][4 * q + rr] * a.inv_tau;
-                const float p = __builtin_amdgcn_exp2f((zs - lse_t) * LOG2E);
-                const float d = gs * ((v == y ? 1.0f : 0.0f) - p);
-                b[rr] = __builtin_bit_cast(uint16_t, (__bf16)((live && v < a.V) ? d : 0.0f));
-              }
-              if (a.dz && trow && v4 < a.Vp) {
+              for (int q = 0; q < 4; ++q) {
+                const int v4 = vbase + 32 * i + 8 * q + 4 * fk;   // 4 consecutive columns
+                uint16_t b[4];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                  const int v = v4 + rr;
+                  const float zs = acc[i][j][4 * q + rr] * a.inv_tau;
+                  const float pr = __builtin_amdgcn_exp2f((zs - lse_t) * LOG2E);
+                  const float d = gs * ((v == y ? 1.0f : 0.0f) - pr);
+                  b[rr] = __builtin_bit_cast(uint16_t, (__bf16)((live && v < a.V) ? d : 0.0f));
+                }
                 const uint64_t packed = (uint64_t)b[0] | ((uint64_t)b[1] << 16) |
                                         ((uint64_t)b[2] << 32) | ((uint64_t)b[3] << 48);
-                *(uint64_t *)(a.dz + (size_t)t * a.ld_dz + v4) = packed;
+                *(uint64_t *)slot(32 * jj + fr, 8 * i + 2 * q + fk) = packed;
               }
-              if (a.dzt) {
-                // dz^T rows are contiguous in t, i.e. across lanes.  Lanes
-                // fr and fr ^ 1 swap values so that each writes one aligned
-                // pair (t even, t + 1): the even lane the pair of column
-                // v4 + rr, the odd lane that of v4 + rr + 1.
-                const bool odd = fr & 1;
+          }
+          // The wave reads back only what it wrote, and LDS executes a wave's
+          // accesses in issue order: no wait between the writes and the reads,
+          // nor before the next pass overwrites the rows.
+          const int trow0 = t0 + wt * 128 + 64 * p;   // token of staging row 0
+          if (a.dz) {
+            // row r = 4 e + (lane >> 4), columns 8 u .. 8 u + 7, u = lane & 15:
+            // chunks 2u, 2u + 1 share one 16-byte slot, swapped when sw(r) is odd
 #pragma unroll
-                for (int rr = 0; rr < 4; rr += 2) {
-                  const uint32_t mine = odd ? b[rr + 1] : b[rr];
-                  const uint32_t give = odd ? b[rr] : b[rr + 1];
-                  const uint32_t got = (uint32_t)xor1i((int)give);
-                  const int v = v4 + rr + (odd ? 1 : 0);
-                  const int te = t & ~1;
-                  const uint32_t pair = odd ? (got | (mine << 16)) : (mine | (got << 16));
-                  if (te < a.Tp && v < a.V)
-                    *(uint32_t *)(a.dzt + (size_t)v * a.ld_dzt + te) = pair;
-                }
+            for (int e = 0; e < 16; ++e) {
+              const int r = 4 * e + (lane_e >> 4), u = lane_e & 15;
+              // the even slot of the pair: 16-byte aligned
+              const u32x4 d = *(const u32x4 *)(stg + r * 256 + ((2 * u ^ (sw(r) & ~1)) << 3));
+              const bool swp = sw(r) & 1;
+              const u32x4 o = swp ? u32x4{d[2], d[3], d[0], d[1]} : d;
+              const int t = trow0 + r, v = vbase + 8 * u;
+              if (t < a.T && v < a.Vp) *(u32x4 *)(a.dz + (size_t)t * a.ld_dz + v) = o;
+            }
+          }
+          if (a.dzt) {
+            // lane 16 G + i: column 16 cb + i, token rows 8 tb .. 8 tb + 7 with
+            // tb = 4 h + G; in each 16-lane group lane 4 k + s points the
+            // transposing read at row 8 tb + k (then + 4), chunk 4 cb + s, so
+            // lane i receives rows 8 tb + 0..3 of column 16 cb + i
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int cb = e >> 1, h = e & 1;
+              const int G = lane_e >> 4, i = lane_e & 15;
+              const int tb = 4 * h + G;
+              const int k = i >> 2, sl = i & 3;
+              const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lds_v4s *)slot(8 * tb + k, 4 * cb + sl));
+              const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lds_v4s *)slot(8 * tb + 4 + k, 4 * cb + sl));
+              const int v = vbase + 16 * cb + i, t = trow0 + 8 * tb;
+              if (v < a.V && t < a.Tp) {
+                const u32x4 o = {(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
+                                 (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+                                 (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
+                                 (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
+                *(u32x4 *)(a.dzt + (size_t)v * a.ld_dzt + t) = o;
               }
             }
+          }
         }
       } else {
       // The options, applied to each logit where it is read (the same fp32
