@@ -531,8 +531,15 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
+        // Writing one staging pass.  Every column first gets g inv_tau (0 - p);
+        // a dead row (past T, or target outside [0, V)) is cleared on the
+        // packed bf16 bits, columns past V only in the vocabulary-tail copy
+        // (MASK), and the one column v == y of a live row is then rewritten
+        // with g inv_tau (1 - p) by the lane that holds it.  The values are
+        // those of forming g inv_tau (1[v == y] - p) per column: 0 - p and
+        // 1 - p are the same subtractions, a cleared value is +0.
+        auto stage_pass = [&](int p, auto masked) {
+          constexpr bool MASK = decltype(masked)::value;
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj) {
             const int j = 2 * p + jj;
@@ -542,25 +549,60 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
             const bool live = trow && y >= 0 && y < a.V;
             const float lse_t = live ? lse_r[j] : 0.0f;
             const float gs = live ? grad_r[j] * a.inv_tau : 0.0f;
+            const uint64_t keep = live ? ~0ull : 0ull;
+            const int lim = a.V - vbase - 4 * fk;   // MASK: offsets below lim are valid
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
-                const int v4 = vbase + 32 * i + 8 * q + 4 * fk;   // 4 consecutive columns
                 uint16_t b[4];
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
-                  const int v = v4 + rr;
                   const float zs = acc[i][j][4 * q + rr] * a.inv_tau;
                   const float pr = __builtin_amdgcn_exp2f((zs - lse_t) * LOG2E);
-                  const float d = gs * ((v == y ? 1.0f : 0.0f) - pr);
-                  b[rr] = __builtin_bit_cast(uint16_t, (__bf16)((live && v < a.V) ? d : 0.0f));
+                  float d = gs * (0.0f - pr);
+                  if (MASK && 32 * i + 8 * q + rr >= lim) d = 0.0f;
+                  b[rr] = __builtin_bit_cast(uint16_t, (__bf16)d);
                 }
                 const uint64_t packed = (uint64_t)b[0] | ((uint64_t)b[1] << 16) |
                                         ((uint64_t)b[2] << 32) | ((uint64_t)b[3] << 48);
-                *(uint64_t *)slot(32 * jj + fr, 8 * i + 2 * q + fk) = packed;
+                *(uint64_t *)slot(32 * jj + fr, 8 * i + 2 * q + fk) = packed & keep;
               }
+            // the target column: block i = rel >> 5, register 4 q + rr with
+            // q = (rel >> 3) & 3, rr = rel & 3, picked by a fixed select tree
+            const int rel = y - vbase;
+            const bool hit = live && rel >= 0 && rel < STAT_V && ((rel >> 2) & 1) == fk;
+            if (__any(hit)) {
+              const int bi = (rel >> 5) & 3;
+              const int ri = (((rel & 31) >> 3) << 2) | (rel & 3);
+              float sel[16];
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const float lo = (bi & 1) ? acc[1][j][r] : acc[0][j][r];
+                const float hi = (bi & 1) ? acc[3][j][r] : acc[2][j][r];
+                sel[r] = (bi & 2) ? hi : lo;
+              }
+#pragma unroll
+              for (int lvl = 0; lvl < 4; ++lvl) {
+                const bool bit = (ri >> lvl) & 1;
+#pragma unroll
+                for (int q = 0; q < (8 >> lvl); ++q) sel[q] = bit ? sel[2 * q + 1] : sel[2 * q];
+              }
+              if (hit) {
+                const float zs = sel[0] * a.inv_tau;
+                const float pr = __builtin_amdgcn_exp2f((zs - lse_t) * LOG2E);
+                const float d = gs * (1.0f - pr);
+                *(uint16_t *)(slot(32 * jj + fr, (rel & (STAT_V - 1)) >> 2) + 2 * (rel & 3)) =
+                    __builtin_bit_cast(uint16_t, (__bf16)d);
+              }
+            }
           }
+        };
+        const bool tail = n == a.nVT - 1 && a.V % TILE_V != 0;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          if (tail) stage_pass(p, std::true_type{});
+          else stage_pass(p, std::false_type{});
           // The wave reads back only what it wrote, and LDS executes a wave's
           // accesses in issue order: no wait between the writes and the reads,
           // nor before the next pass overwrites the rows.
