@@ -24,7 +24,8 @@ constexpr int MERGE_GROUPS = 16;
 constexpr int MERGE_ROWS = 32;
 constexpr int MERGE_KEEP = 80;
 constexpr int MERGE_UNROLL = 16;
-constexpr int COMPARE_THREADS = 256;
+constexpr int COMPARE_THREADS = 1024;
+constexpr int COMPARE_UNROLL = 4;
 
 struct GemmArgs {
   const uint16_t *hidden;

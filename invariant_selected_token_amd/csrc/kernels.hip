@@ -907,23 +907,37 @@ __global__ __launch_bounds__(COMPARE_THREADS) void compare_kernel(
   const int tid = threadIdx.x;
   long long mism = 0, kcnt = 0;
   double mx = 0.0, sa = 0.0, sq = 0.0, k3 = 0.0;
-  for (int i = tid; i < n; i += COMPARE_THREADS) {
-    const float a = x[i], b = y[i];
-    if (__float_as_uint(a) != __float_as_uint(b)) {
-      ++mism;
-      double d = fabs((double)a - (double)b);
-      if (isnan(d)) d = INFINITY;
-      mx = fmax(mx, d);
-      sa = sa + d;
-      sq = sq + d * d;
+  // Elements tid, tid + COMPARE_THREADS, ... in increasing order; the loads
+  // of COMPARE_UNROLL of them are issued together (one memory round trip per
+  // 4096 elements instead of one per element a thread visits).
+  for (int base = 0; base < n; base += COMPARE_THREADS * COMPARE_UNROLL) {
+    float xa[COMPARE_UNROLL], ya[COMPARE_UNROLL];
+#pragma unroll
+    for (int u = 0; u < COMPARE_UNROLL; ++u) {
+      const int i = base + u * COMPARE_THREADS + tid;
+      xa[u] = i < n ? x[i] : 0.0f;
+      ya[u] = i < n ? y[i] : 0.0f;
     }
-    if (isfinite(a) && isfinite(b)) {
-      // equal bits give lr = 0 and k3 = exp(0) - 1 - 0 = 0 exactly
+#pragma unroll
+    for (int u = 0; u < COMPARE_UNROLL; ++u) {
+      if (base + u * COMPARE_THREADS + tid >= n) break;
+      const float a = xa[u], b = ya[u];
       if (__float_as_uint(a) != __float_as_uint(b)) {
-        const double lr = (double)a - (double)b;
-        k3 = k3 + ((exp(lr) - 1.0) - lr);
+        ++mism;
+        double d = fabs((double)a - (double)b);
+        if (isnan(d)) d = INFINITY;
+        mx = fmax(mx, d);
+        sa = sa + d;
+        sq = sq + d * d;
       }
-      ++kcnt;
+      if (isfinite(a) && isfinite(b)) {
+        // equal bits give lr = 0 and k3 = exp(0) - 1 - 0 = 0 exactly
+        if (__float_as_uint(a) != __float_as_uint(b)) {
+          const double lr = (double)a - (double)b;
+          k3 = k3 + ((exp(lr) - 1.0) - lr);
+        }
+        ++kcnt;
+      }
     }
   }
   sc[0][tid] = mism;
