@@ -222,7 +222,8 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="untimed steps first (the shader clock settles over ~8 launches)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-time budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
