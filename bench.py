@@ -78,30 +78,19 @@ def cpu_baseline(case, seconds: float) -> dict:
                       f"full vocabulary V={case.V}, fp64, {wall:.1f} s wall"}
 
 
-def time_variants(rlk, torch, np, hidden, weight, targets, T, H, V, steps, flops):
+VARIANTS = ("options", "slices", "backward", "rmsnorm", "topk20", "long_rollout", "decode")
+
+
+def time_variants(rlk, torch, np, hidden, weight, targets, T, H, V, steps, flops,
+                  only=VARIANTS):
     """The same workload through the other entry points, timed after (never
     inside) the headline region: the contract options (1/tau = 0.7, bf16
-    logits, entropy) and the statistics computed as 4 vocabulary slices plus
-    one merge.  Mean milliseconds per call over `steps` calls after 2 warm-up
-    calls, and the GEMM+statistics rate for the options kernel."""
+    logits, entropy), the statistics computed as 4 vocabulary slices plus one
+    merge, the backward, the RMSNorm, top-k, the long rollout and decode
+    batches (`only` names a subset).  Mean milliseconds per call over `steps`
+    calls after 2 warm-up calls."""
     dev = hidden.device
-    flags = rlk.RLK_LOGITS_BF16 | rlk.RLK_ENTROPY
-    ws_ex = torch.empty(rlk.rlk_workspace_bytes_ex(T, V, flags), dtype=torch.uint8, device=dev)
-    ws = rlk.workspace_for(T, V, dev)
-    cols = (V + 255) // 256
-    cuts = [0] + [round(i * cols / 4) * 256 for i in range(1, 4)] + [V]
-
-    def opts_stats():
-        rlk.rlk_vocab_stats_ex(hidden, weight, targets, ws_ex, V, 0, inv_temperature=0.7,
-                               logits_bf16=True, entropy=True)
-
-    def opts_merge():
-        rlk.rlk_vocab_merge_ex(targets, ws_ex, V, logits_bf16=True, entropy=True)
-
-    def slices():
-        for a, b in zip(cuts[:-1], cuts[1:]):
-            rlk.rlk_vocab_stats_shard(hidden, weight[a:b], targets, ws, V, a)
-        rlk.rlk_vocab_merge(targets, ws, V)
+    out = {}
 
     def timed(fn):
         for _ in range(2):
@@ -115,107 +104,137 @@ def time_variants(rlk, torch, np, hidden, weight, targets, T, H, V, steps, flops
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
-    st = timed(opts_stats)
-    mg = timed(opts_merge)
-    sl = timed(slices)
-    del ws_ex
+    if "options" in only:
+        flags = rlk.RLK_LOGITS_BF16 | rlk.RLK_ENTROPY
+        ws_ex = torch.empty(rlk.rlk_workspace_bytes_ex(T, V, flags), dtype=torch.uint8,
+                            device=dev)
 
-    # backward: transposes, dz pass, grad_hidden and grad_weight GEMMs
-    g = torch.linspace(-1.0, 1.0, T, dtype=torch.float32, device=dev)
-    _, lse = rlk.rlk_selected_logp(hidden, weight, targets)
-    gh = torch.empty((T, H), dtype=torch.float32, device=dev)
-    gw = torch.empty((V, H), dtype=torch.float32, device=dev)
-    ws_b = torch.empty(rlk.rlk_selected_logp_backward_workspace_bytes(T, H, V),
-                       dtype=torch.uint8, device=dev)
+        def opts_stats():
+            rlk.rlk_vocab_stats_ex(hidden, weight, targets, ws_ex, V, 0, inv_temperature=0.7,
+                                   logits_bf16=True, entropy=True)
 
-    def backward():
-        rlk.rlk_selected_logp_backward(hidden, weight, targets, lse, g, grad_hidden=gh,
-                                       grad_weight=gw, workspace=ws_b)
+        def opts_merge():
+            rlk.rlk_vocab_merge_ex(targets, ws_ex, V, logits_bf16=True, entropy=True)
 
-    bw = timed(backward)
-    del ws_b, gw
+        st = timed(opts_stats)
+        mg = timed(opts_merge)
+        del ws_ex
+        out["options_tau0.7_bf16_entropy"] = {"gemm_stats_ms": st, "merge_ms": mg,
+                                              "gemm_TFLOP/s": flops / (st * 1e-3) / 1e12}
 
-    # RMSNorm feeding the LM head, on the same [T, H] shape (HBM-bound)
-    gamma = torch.ones(H, dtype=torch.bfloat16, device=dev)
-    xn = torch.empty_like(hidden)
+    if "slices" in only:
+        ws = rlk.workspace_for(T, V, dev)
+        cols = (V + 255) // 256
+        cuts = [0] + [round(i * cols / 4) * 256 for i in range(1, 4)] + [V]
 
-    def rmsnorm():
-        rlk.rlk_rmsnorm(hidden, gamma, 1e-6, y=xn)
+        def slices():
+            for a, b in zip(cuts[:-1], cuts[1:]):
+                rlk.rlk_vocab_stats_shard(hidden, weight[a:b], targets, ws, V, a)
+            rlk.rlk_vocab_merge(targets, ws, V)
 
-    rn = timed(rmsnorm)
-    rn_bytes = 2.0 * T * H * 2 + 2.0 * H
+        out["vocab_slices_4_plus_merge_ms"] = timed(slices)
+        del ws
 
-    # top-k log-probabilities (k = 20): logits stored once, then the selection
-    z = torch.empty((T, V), dtype=torch.float32, device=dev)
-    tl = torch.empty((T, 20), dtype=torch.float32, device=dev)
-    ti = torch.empty((T, 20), dtype=torch.int32, device=dev)
-    ws_t = rlk.workspace_for(T, V, dev)
-    _, lse_t = rlk.rlk_selected_logp(hidden, weight, targets, workspace=ws_t)
+    if "backward" in only:
+        # transposes, dz pass, grad_hidden and grad_weight GEMMs
+        g = torch.linspace(-1.0, 1.0, T, dtype=torch.float32, device=dev)
+        _, lse = rlk.rlk_selected_logp(hidden, weight, targets)
+        gh = torch.empty((T, H), dtype=torch.float32, device=dev)
+        gw = torch.empty((V, H), dtype=torch.float32, device=dev)
+        ws_b = torch.empty(rlk.rlk_selected_logp_backward_workspace_bytes(T, H, V),
+                           dtype=torch.uint8, device=dev)
 
-    def store_logits():
-        rlk.rlk_logits(hidden, weight, logits=z)
+        def backward():
+            rlk.rlk_selected_logp_backward(hidden, weight, targets, lse, g, grad_hidden=gh,
+                                           grad_weight=gw, workspace=ws_b)
 
-    def select():
-        rlk.rlk_topk_logp(z, lse_t, ws_t, 20, topk_logp=tl, topk_ids=ti)
+        bw = timed(backward)
+        del ws_b, gw
+        out["backward"] = {"ms": bw, "TFLOP/s": 3 * flops / (bw * 1e-3) / 1e12,
+                           "frac_of_bf16_peak": 3 * flops / (bw * 1e-3) / 1e12
+                           / PEAK_BF16_TFLOPS}
 
-    lg = timed(store_logits)
-    sel = timed(select)
-    del z
+    if "rmsnorm" in only:
+        # RMSNorm feeding the LM head, on the same [T, H] shape (HBM-bound)
+        gamma = torch.ones(H, dtype=torch.bfloat16, device=dev)
+        xn = torch.empty_like(hidden)
 
-    # long rollout: 16384 rows (32 responses x 512 tokens) through the same path
-    from invariant_selected_token_amd import synth as _synth
-    lr = _synth.long_rollout_case()
-    to_dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(
-        torch.bfloat16)
-    h_lr, y_lr = to_dev(lr.hidden), torch.from_numpy(lr.targets).to(dev)
-    T_lr = lr.T
-    ws_lr = rlk.workspace_for(T_lr, V, dev)
-    lp_lr = torch.empty(T_lr, dtype=torch.float32, device=dev)
-    lse_lr = torch.empty_like(lp_lr)
+        def rmsnorm():
+            rlk.rlk_rmsnorm(hidden, gamma, 1e-6, y=xn)
 
-    def rollout_stats():
-        rlk.rlk_vocab_stats(h_lr, weight, y_lr, ws_lr)
+        rn = timed(rmsnorm)
+        rn_bytes = 2.0 * T * H * 2 + 2.0 * H
+        out["rmsnorm"] = {"ms": rn, "GB/s": rn_bytes / (rn * 1e-3) / 1e9,
+                          "frac_of_hbm_peak": rn_bytes / (rn * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                          "bytes": rn_bytes}
 
-    def rollout_merge():
-        rlk.rlk_vocab_merge(y_lr, ws_lr, V, logp=lp_lr, lse=lse_lr)
+    if "topk20" in only:
+        # top-k log-probabilities (k = 20): logits stored once, then the selection
+        z = torch.empty((T, V), dtype=torch.float32, device=dev)
+        tl = torch.empty((T, 20), dtype=torch.float32, device=dev)
+        ti = torch.empty((T, 20), dtype=torch.int32, device=dev)
+        ws_t = rlk.workspace_for(T, V, dev)
+        _, lse_t = rlk.rlk_selected_logp(hidden, weight, targets, workspace=ws_t)
 
-    ro_g = timed(rollout_stats)
-    ro_m = timed(rollout_merge)
-    ro_bytes = 8.0 * ((V + 127) // 128) * T_lr + 16.0 * T_lr
-    rollout = {"T": T_lr, "gemm_stats_ms": ro_g, "merge_ms": ro_m,
-               "tokens/s": T_lr / ((ro_g + ro_m) * 1e-3),
-               "gemm_TFLOP/s": 2.0 * T_lr * H * V / (ro_g * 1e-3) / 1e12,
-               "gemm_frac_of_bf16_peak": 2.0 * T_lr * H * V / (ro_g * 1e-3) / 1e12
-               / PEAK_BF16_TFLOPS,
-               "merge_GB/s": ro_bytes / (ro_m * 1e-3) / 1e9}
-    del h_lr, ws_lr
+        def store_logits():
+            rlk.rlk_logits(hidden, weight, logits=z)
 
-    # decode batches: the whole head is streamed for a handful of rows
-    decode = {}
-    for B in (1, 16, 64, 256):
-        hb, yb = hidden[:B].contiguous(), targets[:B].contiguous()
-        lpb = torch.empty(B, dtype=torch.float32, device=dev)
-        lseb = torch.empty_like(lpb)
-        wsb = rlk.workspace_for(B, V, dev)
+        def select():
+            rlk.rlk_topk_logp(z, lse_t, ws_t, 20, topk_logp=tl, topk_ids=ti)
 
-        def dec():
-            rlk.rlk_selected_logp(hb, weight, yb, logp=lpb, lse=lseb, workspace=wsb)
+        lg = timed(store_logits)
+        sel = timed(select)
+        del z
+        out["topk20"] = {"logits_store_ms": lg, "select_ms": sel,
+                         "select_GB/s": 4.0 * T * V / (sel * 1e-3) / 1e9}
 
-        ms = timed(dec)
-        decode[f"B={B}"] = {"ms": ms, "weight_GB/s": 2.0 * V * H / (ms * 1e-3) / 1e9}
-    return {
-            "long_rollout": rollout,
-            "topk20": {"logits_store_ms": lg, "select_ms": sel,
-                       "select_GB/s": 4.0 * T * V / (sel * 1e-3) / 1e9},
-            "decode": decode,
-            "rmsnorm": {"ms": rn, "GB/s": rn_bytes / (rn * 1e-3) / 1e9,
-                        "frac_of_hbm_peak": rn_bytes / (rn * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                        "bytes": rn_bytes},"options_tau0.7_bf16_entropy": {"gemm_stats_ms": st, "merge_ms": mg,
-                                            "gemm_TFLOP/s": flops / (st * 1e-3) / 1e12},
-            "vocab_slices_4_plus_merge_ms": sl,
-            "backward": {"ms": bw, "TFLOP/s": 3 * flops / (bw * 1e-3) / 1e12,
-                         "frac_of_bf16_peak": 3 * flops / (bw * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
-            "steps": steps}
+    if "long_rollout" in only:
+        # 16384 rows (32 responses x 512 tokens) through the same path
+        from invariant_selected_token_amd import synth as _synth
+        lr = _synth.long_rollout_case()
+        to_dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(
+            dev).view(torch.bfloat16)
+        h_lr, y_lr = to_dev(lr.hidden), torch.from_numpy(lr.targets).to(dev)
+        T_lr = lr.T
+        ws_lr = rlk.workspace_for(T_lr, V, dev)
+        lp_lr = torch.empty(T_lr, dtype=torch.float32, device=dev)
+        lse_lr = torch.empty_like(lp_lr)
+
+        def rollout_stats():
+            rlk.rlk_vocab_stats(h_lr, weight, y_lr, ws_lr)
+
+        def rollout_merge():
+            rlk.rlk_vocab_merge(y_lr, ws_lr, V, logp=lp_lr, lse=lse_lr)
+
+        ro_g = timed(rollout_stats)
+        ro_m = timed(rollout_merge)
+        ro_bytes = 8.0 * ((V + 127) // 128) * T_lr + 16.0 * T_lr
+        out["long_rollout"] = {
+            "T": T_lr, "gemm_stats_ms": ro_g, "merge_ms": ro_m,
+            "tokens/s": T_lr / ((ro_g + ro_m) * 1e-3),
+            "gemm_TFLOP/s": 2.0 * T_lr * H * V / (ro_g * 1e-3) / 1e12,
+            "gemm_frac_of_bf16_peak": 2.0 * T_lr * H * V / (ro_g * 1e-3) / 1e12
+            / PEAK_BF16_TFLOPS,
+            "merge_GB/s": ro_bytes / (ro_m * 1e-3) / 1e9}
+        del h_lr, ws_lr
+
+    if "decode" in only:
+        # decode batches: the whole head is streamed for a handful of rows
+        decode = {}
+        for B in (1, 16, 64, 256):
+            hb, yb = hidden[:B].contiguous(), targets[:B].contiguous()
+            lpb = torch.empty(B, dtype=torch.float32, device=dev)
+            lseb = torch.empty_like(lpb)
+            wsb = rlk.workspace_for(B, V, dev)
+
+            def dec():
+                rlk.rlk_selected_logp(hb, weight, yb, logp=lpb, lse=lseb, workspace=wsb)
+
+            ms = timed(dec)
+            decode[f"B={B}"] = {"ms": ms, "weight_GB/s": 2.0 * V * H / (ms * 1e-3) / 1e9}
+        out["decode"] = decode
+    out["steps"] = steps
+    return out
 
 
 def main() -> int:
@@ -227,12 +246,19 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-time budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--variants", default=",".join(VARIANTS),
+                    help="comma-separated subset of: " + ", ".join(VARIANTS))
     ap.add_argument("--variant-steps", type=int, default=10,
                     help="timed calls per variant (options, vocabulary slices); 0 skips")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB before the "
                          "timed region (reference kernel for HBM counters)")
     args = ap.parse_args()
+    variants = tuple(x for x in args.variants.split(",") if x)
+    unknown = [x for x in variants if x not in VARIANTS]
+    if unknown:
+        print(f"bench.py: unknown variants {unknown}; choose from {VARIANTS}", file=sys.stderr)
+        return 2
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -343,7 +369,7 @@ def main() -> int:
     }
     if args.variant_steps > 0:
         out["variants"] = time_variants(rlk, torch, np, hidden, weight, targets, T, H, V,
-                                        args.variant_steps, flops)
+                                        args.variant_steps, flops, variants)
     if not args.no_cpu_baseline:
         log("bench: timing the fp64 oracle on the host")
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
