@@ -455,15 +455,53 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
       // floats: the host keeps V <= 2^24, so the size fits 2^31 bytes).  A
       // row past T lies past the resource's size, and a column past V is
       // given offset 2^31, so the hardware's range check drops both stores:
-      // no branch per element, and the accumulators stay in place.  With V a
-      // multiple of 4 and a 16-byte aligned output, each lane writes four
-      // columns per 16-byte store (the two lane halves cover 32 contiguous
-      // bytes of a row); otherwise (EX == 1, chosen by the host) one column
-      // per store.  The two are separate instantiations because the
-      // per-column offsets of the second would otherwise cost the first its
-      // registers; the arithmetic, and so every stored bit, is the same.
+      // no branch per element.  With V a multiple of 4 and a 16-byte aligned
+      // output (EX == 0) the rows go through LDS and leave as whole rows, four
+      // columns per lane; otherwise (EX == 1, chosen by the host) one column
+      // per store straight from the accumulators.  The two are separate
+      // instantiations; the arithmetic, and so every stored bit, is the same.
       constexpr uint32_t DROP = 0x80000000u;
       constexpr bool vec = EX == 0;
+      if constexpr (vec) {
+        // Through LDS: each wave stages its 32-row blocks (32 rows x 128
+        // columns fp32, 16 KiB) in its quarter of the operand buffer's stage 1
+        // (free once every wave is past the tile's last K block), then stores
+        // whole rows, two per instruction: 8 full lines per store instead of
+        // 32 rows x 32 bytes.  16-byte chunk c of staging row r sits at slot
+        // c ^ (r & 15), which keeps the writes (8 rows, one chunk) and the row
+        // reads free of bank conflicts.
+        typedef __attribute__((address_space(3))) char lds_c;
+        lds_c *stg = (lds_c *)smem + 2 * STAGE_BYTES + wave * (STAGE_BYTES / 2);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              *(u32x4 *)(stg + fr * 512 + (((8 * i + 2 * q + fk) ^ (fr & 15)) << 4)) =
+                  u32x4{__float_as_uint(acc[i][j][4 * q]), __float_as_uint(acc[i][j][4 * q + 1]),
+                        __float_as_uint(acc[i][j][4 * q + 2]),
+                        __float_as_uint(acc[i][j][4 * q + 3])};
+          const int trow = t0 + wt * 128 + 32 * j;
+          const int rows = min(32, a.T - trow);
+          const __amdgpu_buffer_rsrc_t r_out = make_rsrc(
+              a.logits + (size_t)trow * a.V, rows > 0 ? (uint32_t)rows * (uint32_t)a.V * 4u : 0u);
+          // row r = 2 e + (lane >> 5), columns 4 u .. 4 u + 3, u = lane & 31
+          const int u = lane_e & 31, rh = lane_e >> 5;
+          const int v4 = vbase + 4 * u;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int r = 2 * e + rh;
+            const u32x4 d = *(const u32x4 *)(stg + r * 512 + ((u ^ (r & 15)) << 4));
+            const uint32_t off =
+                v4 < a.V ? (uint32_t)r * (uint32_t)a.V * 4u + 4u * (uint32_t)v4 : DROP;
+            __builtin_amdgcn_raw_buffer_store_b128(d, r_out, (int)off, 0, 0);
+          }
+        }
+      } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int trow = t0 + wt * 128 + 32 * j;
@@ -476,24 +514,16 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int v4 = vbase + 32 * i + 8 * q + 4 * fk;
-            if constexpr (vec) {
-              const uint32_t off = v4 < a.V ? rofs + 4u * (uint32_t)v4 : DROP;
-              __builtin_amdgcn_raw_buffer_store_b128(
-                  u32x4{__float_as_uint(acc[i][j][4 * q]), __float_as_uint(acc[i][j][4 * q + 1]),
-                        __float_as_uint(acc[i][j][4 * q + 2]),
-                        __float_as_uint(acc[i][j][4 * q + 3])},
-                  r_out, (int)off, 0, 0);
-            } else {
 #pragma unroll
-              for (int rr = 0; rr < 4; ++rr) {
-                const int v = v4 + rr;
-                const uint32_t off = v < a.V ? rofs + 4u * (uint32_t)v : DROP;
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][4 * q + rr]),
-                                                      r_out, (int)off, 0, 0);
-              }
+            for (int rr = 0; rr < 4; ++rr) {
+              const int v = v4 + rr;
+              const uint32_t off = v < a.V ? rofs + 4u * (uint32_t)v : DROP;
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][4 * q + rr]),
+                                                    r_out, (int)off, 0, 0);
             }
           }
       }
+      }  // vec
     } else {
       // Statistics tiles are 128 vocabulary rows wide: wave (wv, wt) owns
       // tile js = 2 n + wv (of this weight slice; js_base + js globally) for
