@@ -1100,6 +1100,11 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+// NC > 0: the row has at most NC chunks per lane (H <= 512 NC); all of them,
+// and gamma's, are loaded at once and the row is kept in registers (one
+// memory round trip).  NC == 0: any H, the row read twice (the second time
+// from L2).  Same arithmetic, same order.
+template <int NC>
 __global__ __launch_bounds__(64 * RMS_ROWS) void rmsnorm_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, const uint16_t *__restrict__ gamma, float eps,
     uint16_t *__restrict__ y, int64_t ldy, int T, int H) {
@@ -1107,10 +1112,9 @@ __global__ __launch_bounds__(64 * RMS_ROWS) void rmsnorm_kernel(
   const int t = blockIdx.x * RMS_ROWS + (threadIdx.x >> 6);
   if (t >= T) return;                      // a whole wave
   const uint16_t *row = x + (size_t)t * ldx;
+  uint16_t *out = y + (size_t)t * ldy;
   const int nch = H >> 3;
-  float ss = 0.0f;
-  for (int c = lane; c < nch; c += 64) {
-    const uint4 v = *(const uint4 *)(row + 8 * c);
+  auto sum_sq = [](float ss, const uint4 &v) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -1118,14 +1122,9 @@ __global__ __launch_bounds__(64 * RMS_ROWS) void rmsnorm_kernel(
       ss = ss + a * a;
       ss = ss + b * b;
     }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) ss = ss + __shfl_xor(ss, o);
-  const float r = 1.0f / sqrtf(ss / (float)H + eps);
-  uint16_t *out = y + (size_t)t * ldy;
-  for (int c = lane; c < nch; c += 64) {
-    const uint4 v = *(const uint4 *)(row + 8 * c);
-    const uint4 g = *(const uint4 *)(gamma + 8 * c);
+    return ss;
+  };
+  auto norm = [](const uint4 &v, const uint4 &g, float r) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
     uint32_t o[4];
@@ -1135,14 +1134,54 @@ __global__ __launch_bounds__(64 * RMS_ROWS) void rmsnorm_kernel(
       const float n1 = bf16_lo(bf16_bits(bf16_hi(w[k]) * r));
       o[k] = bf16_bits(n0 * bf16_lo(gw[k])) | (bf16_bits(n1 * bf16_hi(gw[k])) << 16);
     }
-    *(uint4 *)(out + 8 * c) = make_uint4(o[0], o[1], o[2], o[3]);
+    return make_uint4(o[0], o[1], o[2], o[3]);
+  };
+  float ss = 0.0f;
+  if constexpr (NC > 0) {
+    uint4 v[NC], g[NC];
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+      const int c = lane + 64 * u;
+      v[u] = make_uint4(0, 0, 0, 0);
+      g[u] = make_uint4(0, 0, 0, 0);
+      if (c < nch) {
+        v[u] = *(const uint4 *)(row + 8 * c);
+        g[u] = *(const uint4 *)(gamma + 8 * c);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NC; ++u)
+      if (lane + 64 * u < nch) ss = sum_sq(ss, v[u]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss = ss + __shfl_xor(ss, o);
+    const float r = 1.0f / sqrtf(ss / (float)H + eps);
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+      const int c = lane + 64 * u;
+      if (c < nch) *(uint4 *)(out + 8 * c) = norm(v[u], g[u], r);
+    }
+  } else {
+    for (int c = lane; c < nch; c += 64) ss = sum_sq(ss, *(const uint4 *)(row + 8 * c));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss = ss + __shfl_xor(ss, o);
+    const float r = 1.0f / sqrtf(ss / (float)H + eps);
+    for (int c = lane; c < nch; c += 64)
+      *(uint4 *)(out + 8 * c) =
+          norm(*(const uint4 *)(row + 8 * c), *(const uint4 *)(gamma + 8 * c), r);
   }
 }
 
 hipError_t launch_rmsnorm(const uint16_t *x, int64_t ldx, const uint16_t *gamma, float eps,
                           uint16_t *y, int64_t ldy, int T, int H, hipStream_t s) {
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(ceil_div(T, RMS_ROWS)), dim3(64 * RMS_ROWS), 0, s, x,
-                     ldx, gamma, eps, y, ldy, T, H);
+  const dim3 grid(ceil_div(T, RMS_ROWS)), block(64 * RMS_ROWS);
+  // the smallest register-resident instantiation that holds the row (the
+  // choice depends only on H; all three compute the same bits)
+  if (H <= 512 * 8)
+    hipLaunchKernelGGL(rmsnorm_kernel<8>, grid, block, 0, s, x, ldx, gamma, eps, y, ldy, T, H);
+  else if (H <= 512 * 16)
+    hipLaunchKernelGGL(rmsnorm_kernel<16>, grid, block, 0, s, x, ldx, gamma, eps, y, ldy, T, H);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<0>, grid, block, 0, s, x, ldx, gamma, eps, y, ldy, T, H);
   return hipGetLastError();
 }
 

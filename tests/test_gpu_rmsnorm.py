@@ -52,8 +52,11 @@ def _alternatives(xr, g):
     return mid, y_other
 
 
+# H up to 4096 and up to 8192 keep the row in registers (8 or 16 chunks per
+# lane), larger H reads it twice: all three paths, with ragged chunk counts.
 @pytest.mark.parametrize("T,H,eps", [(1, 64, 1e-6), (300, 4096, 1e-6), (77, 192, 1e-5),
-                                     (513, 2056, 1e-6), (64, 8192, 0.0)])
+                                     (513, 2056, 1e-6), (64, 8192, 0.0), (33, 4104, 1e-6),
+                                     (9, 16392, 1e-6)])
 def test_rmsnorm_parity(dev, T, H, eps):
     x, g = _inputs(T, H, 500 + H)
     got = _gpu(x, g, eps, dev)
