@@ -1002,9 +1002,19 @@ __global__ __launch_bounds__(COMPARE_THREADS) void compare_kernel(
 
 hipError_t launch_gemm_stats(const GemmArgs &a, int workers, hipStream_t s) {
   const int tiles = a.nMT * a.nVT;
-  // A multiple of 8 workgroups keeps each one on a fixed XCD.
+  // A multiple of 8 workgroups keeps each one on a fixed XCD.  As few as
+  // give the same number of rounds: a last round of a few workgroups, each
+  // waiting on its own weight stream, costs as much as a full one, while
+  // fewer concurrent workgroups share the bandwidth of every round (594
+  // tiles of a decode batch: 200 workgroups x 3 rounds instead of 256 and a
+  // third round of 82).
   int grid = workers >= 8 ? workers - workers % 8 : 8;
   if (grid > tiles) grid = tiles;
+  if (grid % 8 == 0) {
+    const int rounds = (tiles + grid - 1) / grid;
+    const int even = (tiles + rounds - 1) / rounds;
+    grid = (even + 7) / 8 * 8;
+  }
   if (a.ex == 3)
     hipLaunchKernelGGL((gemm_kernel<true, true, 3>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
   else if (a.ex == 2)
@@ -1020,6 +1030,11 @@ hipError_t launch_gemm_logits(const GemmArgs &a, int workers, hipStream_t s) {
   const int tiles = a.nMT * a.nVT;
   int grid = workers >= 8 ? workers - workers % 8 : 8;
   if (grid > tiles) grid = tiles;
+  if (grid % 8 == 0) {   // as few workgroups as give the same number of rounds
+    const int rounds = (tiles + grid - 1) / grid;
+    const int even = (tiles + rounds - 1) / rounds;
+    grid = (even + 7) / 8 * 8;
+  }
   if ((a.V & 3) == 0 && ((uintptr_t)a.logits & 15) == 0)
     hipLaunchKernelGGL((gemm_kernel<false, true, 0>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
   else
