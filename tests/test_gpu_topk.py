@@ -113,3 +113,22 @@ def test_topk_ties_nan_and_short_rows(dev):
     # are the short-row filler (id -1, -inf), as in the oracle
     assert np.array_equal(ti_np[1], rids[1]) and np.all(ti_np[1] == -1)
     assert np.all(tl.cpu().numpy()[1] == -np.inf)
+
+
+@pytest.mark.parametrize("k", [17, 25, 33])
+def test_topk_boundary_inside_a_tie_group(dev, k):
+    """Groups of 10 exactly equal logits with the k-th place inside a group:
+    the smaller ids of that group are taken, as in the oracle (k >= 17 takes
+    the bisection path)."""
+    H, V = 64, 40
+    w = np.zeros((V, H), np.float32)
+    w[:, 0] = np.repeat(np.array([1.0, 0.5, -0.5, 0.25], np.float32), 10)
+    h = np.zeros((2, H), np.float32)
+    h[0, 0] = 1.0
+    h[1, 0] = -2.0
+    hb, wb = synth.f32_to_bf16_bits(h), synth.f32_to_bf16_bits(w)
+    y = np.zeros(2, np.int32)
+    lp, lse, tl, ti = _run(to_dev_bf16(hb, dev), to_dev_bf16(wb, dev), to_dev_i32(y, dev), k)
+    rlp, rids = orc.topk_logp(hb, wb, k)
+    assert np.array_equal(ti.cpu().numpy(), rids)
+    np.testing.assert_allclose(tl.cpu().numpy(), rlp, rtol=0, atol=1e-5)
