@@ -107,7 +107,8 @@ int rlk_vocab_tile(void);
  * The contents are opaque to callers. */
 size_t rlk_selected_logp_workspace_bytes(int64_t T, int64_t V);
 /* Layout detail: 2 * ceil(V/128) * T floats of tile statistics, then T floats
- * of target logits, each region rounded up to 256 bytes. */
+ * of target logits, each region rounded up to 256 bytes, then 256 bytes of
+ * tile-claim counters for the GEMM's workgroups (reset by every call). */
 
 /* Selected-token log-probabilities: the hot path.
  *   hidden    bf16 [T][ld_hidden] row-major, only the first H columns read;
@@ -124,9 +125,10 @@ size_t rlk_selected_logp_workspace_bytes(int64_t T, int64_t V);
  *             rlk_selected_logp_workspace_bytes(T, V) bytes, 16-byte
  *             aligned; its contents on entry do not matter.
  *   stream    hipStream_t or NULL.
- * Two kernels run on `stream`: the logit GEMM with the per-tile statistics
- * and target capture fused into its epilogue, then the fixed-order
- * vocabulary merge that writes lse and logp. */
+ * Three kernels run on `stream`: a reset of the workspace's tile-claim
+ * counters, the logit GEMM with the per-tile statistics and target capture
+ * fused into its epilogue, then the fixed-order vocabulary merge that writes
+ * lse and logp.  Which workgroup computes a tile changes no bit. */
 int rlk_selected_logp(const void *hidden, int64_t ld_hidden,
                       const void *weight, int64_t ld_weight,
                       const int32_t *targets, float *logp, float *lse,

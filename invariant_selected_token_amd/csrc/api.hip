@@ -59,10 +59,14 @@ int check_options(float inv_tau, int flags) {
   return RLK_OK;
 }
 
-// Workspace: part_m, part_s, xt, then part_u when the entropy is asked for.
+// Workspace: part_m, part_s, xt, then part_u when the entropy is asked for,
+// then the statistics GEMM's tile-claim counters.
+constexpr size_t QUEUE_BYTES = 256;
+size_t part_u_offset(int64_t T, int64_t V) {
+  return 2 * stats_bytes(T, V) + round_up((size_t)T * sizeof(float));
+}
 size_t ws_bytes_for(int64_t T, int64_t V, int flags) {
-  return 2 * stats_bytes(T, V) + round_up((size_t)T * sizeof(float)) +
-         ((flags & RLK_ENTROPY) ? stats_bytes(T, V) : 0);
+  return part_u_offset(T, V) + ((flags & RLK_ENTROPY) ? stats_bytes(T, V) : 0) + QUEUE_BYTES;
 }
 
 rlk::GemmArgs gemm_args(const void *hidden, int64_t ldh, const void *weight,
@@ -221,7 +225,12 @@ int rlk_vocab_stats_ex(const void *hidden, int64_t ld_hidden, const void *weight
   g.part_m = reinterpret_cast<float *>(ws);
   g.part_s = reinterpret_cast<float *>(ws + stats_bytes(T, V));
   g.xt = reinterpret_cast<float *>(ws + 2 * stats_bytes(T, V));
-  g.part_u = reinterpret_cast<float *>(ws + ws_bytes_for(T, V, 0));
+  g.part_u = reinterpret_cast<float *>(ws + part_u_offset(T, V));
+  // Dynamic tile claims for the whole vocabulary only: slices of one
+  // workspace may run at the same time on several streams.
+  g.queue = (v_begin == 0 && v_count == V)
+                ? reinterpret_cast<int *>(ws + ws_bytes_for(T, V, flags) - QUEUE_BYTES)
+                : nullptr;
   g.js_base = (int)(v_begin / rlk::STAT_V);
   g.y_base = (int)v_begin;
   g.inv_tau = inv_temperature;
@@ -267,7 +276,7 @@ int rlk_vocab_merge_ex(const int32_t *targets, float *logp, float *lse, float *e
   mg.part_m = reinterpret_cast<const float *>(ws);
   mg.part_s = reinterpret_cast<const float *>(ws + stats_bytes(T, V));
   mg.xt = reinterpret_cast<const float *>(ws + 2 * stats_bytes(T, V));
-  mg.part_u = ent ? reinterpret_cast<const float *>(ws + ws_bytes_for(T, V, 0)) : nullptr;
+  mg.part_u = ent ? reinterpret_cast<const float *>(ws + part_u_offset(T, V)) : nullptr;
   mg.entropy = ent ? entropy : nullptr;
   mg.targets = targets;
   mg.logp = logp;

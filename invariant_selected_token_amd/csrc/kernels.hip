@@ -77,6 +77,8 @@ constexpr int PREFETCH_AHEAD = 1;
 constexpr int PREFETCH_SINK = 256;
 // Then a double buffer of the tiles' targets (2 x 256 int32).
 constexpr int TGT_OFS = 4 * TILE_V * TILE_K * 2 + PREFETCH_SINK;
+// Then the two tile-claim slots of the dynamic walk.
+constexpr int CLAIM_OFS = TGT_OFS + 2 * TILE_T * 4;
 
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base,
@@ -97,6 +99,18 @@ __device__ __forceinline__ void tile_of_block(int b, int nMT, int nVT, int &m,
   const int per_xcd = total >> 3;
   int L = b;
   if (b < (per_xcd << 3)) L = (b & 7) * per_xcd + (b >> 3);
+  const int in_group = GROUP_M * nVT;
+  const int g = L / in_group;
+  const int first_m = g * GROUP_M;
+  const int gsm = min(nMT - first_m, GROUP_M);
+  const int r = L - g * in_group;
+  m = first_m + r % gsm;
+  n = r / gsm;
+}
+
+// The same grouping for a logical tile index that is already XCD-ordered
+// (the dynamic claims hand out logical indices directly).
+__device__ __forceinline__ void tile_of_logical(int L, int nMT, int nVT, int &m, int &n) {
   const int in_group = GROUP_M * nVT;
   const int g = L / in_group;
   const int first_m = g * GROUP_M;
@@ -135,9 +149,45 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   // lane id, so that none is live across both the K loop and the epilogue.
 
   const int total = a.nMT * a.nVT;
-  int L = blockIdx.x;
-  if (L >= total) return;
-  auto coords = [&](int l, int &m, int &n) { tile_of_block(l, a.nMT, a.nVT, m, n); };
+  // Dynamic tile claims (statistics kernels, when the host passes a.queue):
+  // the compute units do not run at one speed (per-XCD tile times differ by
+  // several percent), so a fixed share of tiles per workgroup ends with the
+  // slowest one.  Each XCD x claims the logical tiles of its own contiguous
+  // range in order from counter a.queue[x] (the tiles that share weight tiles
+  // in its L2 stay together), and once that range is exhausted takes tiles
+  // from the other XCDs' ranges.  Thread 0 claims the next tile at the start
+  // of the current one, just before the workgroup barrier there, and the
+  // waves read it from LDS.  Which workgroup computes a tile changes no bit.
+  const bool dyn = STATS && PERSIST && a.queue != nullptr;
+  const int per_xcd = total >> 3;
+  // two slots in the kernel's one LDS buffer (a separate __shared__ object
+  // made the compiler wait for every direct-to-LDS load before LDS reads)
+  int *claimed = reinterpret_cast<int *>(smem + CLAIM_OFS);
+  auto claim = [&]() -> int {
+    const int x = (int)(blockIdx.x & 7);
+    for (int d = 0; d < 8; ++d) {
+      const int y = (x + d) & 7;
+      const int lo = y * per_xcd, hi = y == 7 ? total : lo + per_xcd;
+      if (lo >= hi) continue;
+      const int i = atomicAdd(&a.queue[y], 1);
+      if (lo + i < hi) return lo + i;
+    }
+    return -1;
+  };
+  int L;
+  if (dyn) {
+    if (threadIdx.x == 0) claimed[0] = claim();
+    __syncthreads();
+    L = claimed[0];
+    if (L < 0) return;
+  } else {
+    L = blockIdx.x;
+    if (L >= total) return;
+  }
+  auto coords = [&](int l, int &m, int &n) {
+    if (dyn) tile_of_logical(l, a.nMT, a.nVT, m, n);
+    else tile_of_block(l, a.nMT, a.nVT, m, n);
+  };
 
   // Global -> LDS: direct-to-LDS buffer loads (each lane's 16 bytes land in
   // LDS slot base + 16 * lane).  Load i of wave w fills the 1 KiB block
@@ -377,6 +427,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     set_offsets();
+    if (dyn && threadIdx.x == 0) claimed[parity ^ 1] = claim();   // the next tile
     // The tile's first block (issued by the previous tile's last K block, or
     // above).
     __builtin_amdgcn_s_waitcnt(VMCNT0);
@@ -408,8 +459,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     // two blocks of this one) and its targets; the last block loads its
     // first block into stage 0.  After the last tile those loads and
     // prefetches go through the zero-size resource and read nothing.
-    const int Ln = PERSIST ? L + (int)gridDim.x : total;
-    const bool more_tiles = Ln < total;
+    const int Ln = dyn ? claimed[parity ^ 1] : PERSIST ? L + (int)gridDim.x : total;
+    const bool more_tiles = dyn ? Ln >= 0 : Ln < total;
     int mn = m, nn = n;
     if (more_tiles) coords(Ln, mn, nn);
     const __amdgpu_buffer_rsrc_t rwn = more_tiles ? rsrc_w(nn) : zero;
@@ -820,7 +871,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
 // workgroup per tile.
 template <bool STATS, bool PERSIST, int EX>
 __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[TGT_OFS + 2 * TILE_T * 4];
+  __shared__ __attribute__((aligned(16))) char smem[CLAIM_OFS + 16];
   gemm_body<STATS, PERSIST, EX>(a, smem);
 }
 
@@ -1000,6 +1051,8 @@ __global__ __launch_bounds__(COMPARE_THREADS) void compare_kernel(
   }
 }
 
+__global__ __launch_bounds__(256) void zero_kernel(float *x, int64_t n);
+
 hipError_t launch_gemm_stats(const GemmArgs &a, int workers, hipStream_t s) {
   const int tiles = a.nMT * a.nVT;
   // A multiple of 8 workgroups keeps each one on a fixed XCD.  As few as
@@ -1015,6 +1068,8 @@ hipError_t launch_gemm_stats(const GemmArgs &a, int workers, hipStream_t s) {
     const int even = (tiles + rounds - 1) / rounds;
     grid = (even + 7) / 8 * 8;
   }
+  // the claim counters start at zero (a kernel, not a memset: capturable)
+  if (a.queue) hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(64), 0, s, (float *)a.queue, 8);
   if (a.ex == 3)
     hipLaunchKernelGGL((gemm_kernel<true, true, 3>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
   else if (a.ex == 2)

@@ -50,7 +50,7 @@ def test_workspace_size():
 
     def expect(T, V):
         r = lambda x: (x + 255) // 256 * 256
-        return 2 * r(((V + 127) // 128) * T * 4) + r(T * 4)
+        return 2 * r(((V + 127) // 128) * T * 4) + r(T * 4) + 256   # + tile-claim counters
 
     for T, V in [(1, 1), (1, 151936), (64, 4096), (4096, 151936), (16384, 151936),
                  (257, 129)]:
