@@ -106,7 +106,7 @@ int hip_status(hipError_t e) {
 int64_t pad64(int64_t x) { return (x + 63) / 64 * 64; }
 
 struct BwdLayout {
-  size_t dz, dzt, wt, ht, total;  // byte offsets and size
+  size_t dz, dzt, wt, ht, queue, total;  // byte offsets and size
 };
 
 BwdLayout bwd_layout(int64_t T, int64_t H, int64_t V, bool want_h, bool want_w) {
@@ -120,6 +120,8 @@ BwdLayout bwd_layout(int64_t T, int64_t H, int64_t V, bool want_h, bool want_w) 
   if (want_h) o += round_up((size_t)H * pad64(V) * 2);
   L.ht = o;
   if (want_w) o += round_up((size_t)H * pad64(T) * 2);
+  L.queue = o;   // tile-claim counters of the GEMMs, reset before each launch
+  o += QUEUE_BYTES;
   L.total = o;
   return L;
 }
@@ -150,9 +152,11 @@ rlk::GemmArgs dz_args(const void *hidden, int64_t ldh, const void *weight, int64
 
 // out [B rows][A rows] fp32 = A . B^T over depth K (both operands K-contiguous).
 int plain_gemm(const uint16_t *A, int64_t lda, int64_t Arows, const uint16_t *B,
-               int64_t ldb, int64_t Brows, int64_t K, float *out, hipStream_t s) {
+               int64_t ldb, int64_t Brows, int64_t K, float *out, int *queue,
+               hipStream_t s) {
   rlk::GemmArgs g = gemm_args(B, ldb, A, lda, Brows, K, Arows);
   g.logits = out;
+  g.queue = queue;
   // Both backward products stream an operand from HBM in the hidden role
   // (dz, dz^T); prefetching it as well as the weight role measured 3.7 %
   // faster over the whole backward, bitwise identical.
@@ -404,15 +408,17 @@ int rlk_selected_logp_backward(const void *hidden, int64_t ld_hidden, const void
   g.ld_dz = Vp;
   g.dzt = want_w ? dzt : nullptr;
   g.ld_dzt = Tp;
+  int *queue = reinterpret_cast<int *>(ws + L.queue);
+  g.queue = queue;
   st = hip_status(rlk::launch_gemm_stats(g, compute_units(), s));
   if (st != RLK_OK) return st;
   // grad_hidden [T][H] = dz [T][Vp] . wt [H][Vp]^T
   if (want_h) {
-    st = plain_gemm(wt, Vp, H, dz, Vp, T, Vp, grad_hidden, s);
+    st = plain_gemm(wt, Vp, H, dz, Vp, T, Vp, grad_hidden, queue, s);
     if (st != RLK_OK) return st;
   }
   // grad_weight [V][H] = dzt [V][Tp] . ht [H][Tp]^T
-  if (want_w) st = plain_gemm(ht, Tp, H, dzt, Tp, V, Tp, grad_weight, s);
+  if (want_w) st = plain_gemm(ht, Tp, H, dzt, Tp, V, Tp, grad_weight, queue, s);
   return st;
 }
 

@@ -44,8 +44,8 @@ struct GemmArgs {
   // 3: the backward's logit gradient instead of statistics
   int ex;
   int pf_hidden;  // plain GEMM: also prefetch the hidden-role operand into L2
-  // statistics kernels: 8 per-XCD tile-claim counters (zeroed by the launcher
-  // before the kernel), or null for the fixed walk
+  // 8 per-XCD tile-claim counters (zeroed by the launcher before the kernel),
+  // or null for the fixed walk
   int *queue;
   // Logit gradient (ex == 3): dz = g inv_tau (onehot(y) - exp(z inv_tau - lse))
   // rounded to bf16, written to dz [T][ld_dz] (columns V .. Vp-1 zero) and / or

@@ -149,7 +149,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   // lane id, so that none is live across both the K loop and the epilogue.
 
   const int total = a.nMT * a.nVT;
-  // Dynamic tile claims (statistics kernels, when the host passes a.queue):
+  // Dynamic tile claims (when the host passes a.queue):
   // the compute units do not run at one speed (per-XCD tile times differ by
   // several percent), so a fixed share of tiles per workgroup ends with the
   // slowest one.  Each XCD x claims the logical tiles of its own contiguous
@@ -158,7 +158,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   // from the other XCDs' ranges.  Thread 0 claims the next tile at the start
   // of the current one, just before the workgroup barrier there, and the
   // waves read it from LDS.  Which workgroup computes a tile changes no bit.
-  const bool dyn = STATS && PERSIST && a.queue != nullptr;
+  const bool dyn = PERSIST && a.queue != nullptr;
   const int per_xcd = total >> 3;
   // two slots in the kernel's one LDS buffer (a separate __shared__ object
   // made the compiler wait for every direct-to-LDS load before LDS reads)
@@ -1083,6 +1083,7 @@ hipError_t launch_gemm_stats(const GemmArgs &a, int workers, hipStream_t s) {
 
 hipError_t launch_gemm_logits(const GemmArgs &a, int workers, hipStream_t s) {
   const int tiles = a.nMT * a.nVT;
+  if (a.queue) hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(64), 0, s, (float *)a.queue, 8);
   int grid = workers >= 8 ? workers - workers % 8 : 8;
   if (grid > tiles) grid = tiles;
   if (grid % 8 == 0) {   // as few workgroups as give the same number of rounds
