@@ -51,6 +51,12 @@
  *     stream) and never synchronise.  Results are valid once the caller has
  *     synchronised with that stream.  Device faults surface at that sync.
  *   - Outputs must not alias inputs or the workspace.
+ *   - A workspace serves one call at a time: it holds the call's tile
+ *     statistics and the counters its GEMM workgroups claim tiles from, so
+ *     calls that may run at the same time (on different streams) need
+ *     workspaces of their own.  The one exception is vocabulary slices of
+ *     rlk_vocab_stats_shard that are narrower than V: they write disjoint
+ *     statistics and use no counters.
  *   - Validation runs before any HIP call: on an error status nothing was
  *     launched and nothing was written.
  */
