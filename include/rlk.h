@@ -23,7 +23,9 @@
  * Numerical contract (fixed for RLK_ABI_VERSION):
  *   - Inputs are bfloat16 bit patterns; products are exact in fp32, sums are
  *     fp32, accumulated over k = 0 .. H-1 in chunks of 16 in increasing order,
- *     one workgroup per (256 token x 256 vocabulary) tile, no split-K.
+ *     one workgroup per tile of 256 vocabulary rows x 256 token rows (64 or
+ *     128 token rows for batches of at most 64 or 128 rows: the same
+ *     operations per logit), no split-K.
  *   - Logits are never rounded to bf16 and never written to memory.
  *   - Per (row, 128-wide vocabulary tile): tile max m_j and
  *     s_j = sum exp(z - m_j) with a reduction tree that depends only on the

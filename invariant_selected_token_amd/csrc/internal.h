@@ -9,7 +9,8 @@ namespace rlk {
 
 // Workgroup tile of the logit GEMM: TILE_V vocabulary rows x TILE_T token
 // rows, the full hidden dimension per workgroup.  Each wave covers 128 x 128
-// of it; STAT_V = 128 is the width of the vocabulary tiles whose (max, sum of
+// of it (128 vocabulary x 64 or 32 token rows in the lower tiles of batches
+// of at most 128 or 64 rows); STAT_V = 128 is the width of the vocabulary tiles whose (max, sum of
 // exponentials) statistics are merged, so it is part of the numerical
 // contract.
 constexpr int TILE_V = 256;
@@ -65,7 +66,7 @@ struct GemmArgs {
   int V;
   int js_base;  // global index of this weight slice's first statistics tile
   int y_base;   // global vocabulary index of this weight slice's first row
-  int nMT;   // token tiles, ceil(T / TILE_T)
+  int nMT;   // token tiles, ceil(T / TILE_T) (the launcher recounts it for lower tiles)
   int nVT;   // workgroup vocabulary tiles, ceil(V / TILE_V)
   int nST;   // statistics tiles, ceil(V / STAT_V)
 };

@@ -131,15 +131,28 @@ __device__ __forceinline__ void tile_of_logical(int L, int nMT, int nVT, int &m,
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 // The logit GEMM with its epilogue, for a sequence of workgroup tiles of 256
-// vocabulary x 256 token rows.  4 waves; wave w covers vocabulary half
-// wv = w & 1 and token half wt = w >> 1 as 4 x 4 MFMA blocks of 32 x 32.
+// vocabulary x 64 NJ token rows.  4 waves; wave w covers vocabulary half
+// wv = w & 1 and token half wt = w >> 1 as 4 x NJ MFMA blocks of 32 x 32.
+// NJ = 4 is the full tile; the lower tiles (NJ = 2, 1) serve batches of at
+// most 128 and 64 rows, whose full tiles would be mostly padding.  They give
+// every logit, statistic and target capture the same operations in the same
+// order: a logit's accumulator advances through the same K steps, and a
+// token row's 128 vocabulary values of a statistics tile sit in the same
+// (block, register, lane) positions, whatever NJ and the row's block j.
+// Only the number of token blocks per wave changes.
 //
 // PERSIST: the workgroup walks tiles L = blockIdx.x, + gridDim.x, ... and
 // issues the next tile's first K-block loads before the current tile's
 // epilogue, so that their latency hides under the epilogue.  The order of
 // tiles only changes the schedule; every tile's arithmetic is the same.
-template <bool STATS, bool PERSIST, int EX>
+template <bool STATS, bool PERSIST, int EX, int NJ>
 __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
+  static_assert(NJ == 4 || NJ == 2 || NJ == 1, "token blocks of 32 rows per wave");
+  static_assert(NJ == 4 || (STATS && EX != 3), "lower tiles: the statistics epilogue only");
+  constexpr int TT = 64 * NJ;   // token rows of a tile
+  constexpr int WT = 32 * NJ;   // token rows of a wave
+  constexpr int NQ = 4 * NJ;    // MFMAs per wave and K step
+  constexpr int NR = 4 + NJ;    // fragment reads per wave and K step
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
   const int wv = wave & 1;   // vocabulary half of the tile
@@ -202,9 +215,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
                      (uint32_t)(min(TILE_V, a.V - v0) * a.ldw * 2));
   };
   auto rsrc_h = [&](int m) {
-    const int t0 = m * TILE_T;
+    const int t0 = m * TT;
     return make_rsrc(a.hidden + (size_t)t0 * a.ldh,
-                     (uint32_t)(min(TILE_T, a.T - t0) * a.ldh * 2));
+                     (uint32_t)(min(TT, a.T - t0) * a.ldh * 2));
   };
   uint32_t gofs[2][8];  // [operand][load]; set by set_offsets below
   typedef __attribute__((address_space(3))) void lds_void;
@@ -259,7 +272,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
       asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           r_tgt, (lds_void *)(smem + TGT_OFS + par * (TILE_T * 4) + wave * 256), 4,
-          (uint32_t)(l * 4), (uint32_t)((tile_m * TILE_T + 64 * wave) * 4), 0, 0);
+          (uint32_t)(l * 4), (uint32_t)((tile_m * TT + 64 * wave) * 4), 0, 0);
     }
   };
   auto issue_first = [&](__amdgpu_buffer_rsrc_t r_w, __amdgpu_buffer_rsrc_t r_h,
@@ -302,20 +315,20 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
         // swz(32 i + fr) == swz(fr)
         const uint32_t x = (uint32_t)(((2 * ks + lk) ^ swz(lr)) << 4);
         ra[st][ks] = st * (2 * STAGE_BYTES) + (wv * 128 + lr) * 128 + x;
-        rb[st][ks] = st * (2 * STAGE_BYTES) + STAGE_BYTES + (wt * 128 + lr) * 128 + x;
+        rb[st][ks] = st * (2 * STAGE_BYTES) + STAGE_BYTES + (wt * WT + lr) * 128 + x;
       }
   };
-  bf16x8 fa[2][4], fb[2][4];
-  // Read number w (0..7) of the fragments of (stage, ks) into set `buf`, in
-  // the order the MFMAs consume them: A0, B0, B1, B2, B3, A1, A2, A3.
+  bf16x8 fa[2][4], fb[2][NJ];
+  // Read number w (0 .. NR-1) of the fragments of (stage, ks) into set `buf`,
+  // in the order the MFMAs consume them: A0, B0 .. B(NJ-1), A1, A2, A3.
   auto fread = [&](int buf, int st, int ks, int w) {
     if (w == 0) fa[buf][0] = *(const bf16x8 *)(smem + ra[st][ks]);
-    else if (w <= 4) fb[buf][w - 1] = *(const bf16x8 *)(smem + rb[st][ks] + (w - 1) * 4096);
-    else fa[buf][w - 4] = *(const bf16x8 *)(smem + ra[st][ks] + (w - 4) * 4096);
+    else if (w <= NJ) fb[buf][w - 1] = *(const bf16x8 *)(smem + rb[st][ks] + (w - 1) * 4096);
+    else fa[buf][w - NJ] = *(const bf16x8 *)(smem + ra[st][ks] + (w - NJ) * 4096);
   };
-  f32x16 acc[4][4];
+  f32x16 acc[4][NJ];
   auto mfma = [&](int buf, int q) {
-    const int i = q >> 2, j = q & 3;
+    const int i = q / NJ, j = q % NJ;
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j],
                                                        0, 0, 0);
   };
@@ -348,19 +361,30 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     for (int ks = 0; ks < 3; ++ks) {
       const int cur = ks & 1;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
+      for (int q = 0; q < NQ; ++q) {
         mfma(cur, q);
-        if (q < 8) fread(cur ^ 1, st, ks + 1, q);
-        if (ks < 2 && (q & 1)) gload(r_w, r_h, st ^ 1, kl, 8 * ks + (q >> 1));
-        else if (ks == 2 && q == 8) {
+        if (q < NR) fread(cur ^ 1, st, ks + 1, q);
+        if (ks < 2) {
+          // eight loads per step: behind every (NQ / 8)-th MFMA, or 8 / NQ
+          // behind each when the step has fewer than eight
+          if constexpr (NQ >= 8) {
+            if (q % (NQ / 8) == NQ / 8 - 1) gload(r_w, r_h, st ^ 1, kl, 8 * ks + q / (NQ / 8));
+          } else {
+#pragma unroll
+            for (int u = 0; u < 8 / NQ; ++u) gload(r_w, r_h, st ^ 1, kl, 8 * ks + q * (8 / NQ) + u);
+          }
+        } else if (ks == 2 && q == NQ / 2) {
           prefetch(p_w, kp);
           if constexpr (!STATS) prefetch_h(p_h, kp);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      // reads that did not fit behind the step's MFMAs (NJ == 1)
+#pragma unroll
+      for (int w = NQ; w < NR; ++w) fread(cur ^ 1, st, ks + 1, w);
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < NQ / 2; ++q) {
       mfma(1, q);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -377,10 +401,14 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
       asm volatile("" ::: "memory");
     }
 #pragma unroll
-    for (int q = 8; q < 16; ++q) {
+    for (int q = NQ / 2; q < NQ; ++q) {
       mfma(1, q);
-      if (MORE) fread(0, st ^ 1, 0, q - 8);
+      if (MORE && q - NQ / 2 < NR) fread(0, st ^ 1, 0, q - NQ / 2);
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if (MORE) {
+#pragma unroll
+      for (int w = NQ / 2; w < NR; ++w) fread(0, st ^ 1, 0, w);
     }
   };
 
@@ -423,7 +451,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     set_offsets();
@@ -433,7 +461,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     __builtin_amdgcn_s_waitcnt(VMCNT0);
     __syncthreads();
 #pragma unroll
-    for (int w = 0; w < 8; ++w) fread(0, 0, 0, w);
+    for (int w = 0; w < NR; ++w) fread(0, 0, 0, w);
     // The logit gradient's per-row inputs (lse, upstream gradient), loaded
     // now so that their latency hides under the first K block: issued in the
     // epilogue they would wait behind the next tile's operand loads (vector
@@ -444,7 +472,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
       asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int t = m * TILE_T + wt * 128 + 32 * j + (l & 31);
+        const int t = m * TT + wt * WT + 32 * j + (l & 31);
         if (t < a.T) {
           lse_r[j] = a.lse[t];
           grad_r[j] = a.grad[t];
@@ -472,7 +500,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     k_block(nk2 - 1, S1{}, std::false_type{}, rwn, rhn, pwn, phn, 1);
 
     const int v0 = n * TILE_V;
-    const int t0 = m * TILE_T;
+    const int t0 = m * TT;
     // The epilogue's lane values, computed afresh (an asm the compiler cannot
     // merge with the set-up's) so that nothing from the set-up stays live
     // across the K loop or is spilled: a reload from scratch here would be
@@ -483,7 +511,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
 
     // acc[i][j][r] holds z[t][v] for
     //   v = v0 + wv*128 + 32 i + 8 (r >> 2) + 4 fk + (r & 3)
-    //   t = t0 + wt*128 + 32 j + fr
+    //   t = t0 + wt*WT + 32 j + fr
     const int vbase = v0 + wv * 128;
     {
     const int fr = lane_e & 31;
@@ -495,12 +523,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     // ds_read: no wait on the vector memory counter)
     const int *tgt = reinterpret_cast<const int *>(smem + TGT_OFS + parity * (TILE_T * 4));
     auto target_of = [&](int j, int t) {
-      return (t < a.T) ? tgt[wt * 128 + 32 * j + fr] : -1;
+      return (t < a.T) ? tgt[wt * WT + 32 * j + fr] : -1;
     };
     // neighbouring-lane exchange (lane l gets lane l ^ 1's value): a DPP quad
     // permutation [1, 0, 3, 2] in the VALU, no LDS round trip
     auto xor1i = [&](int x) { return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false); };
-    if (!STATS) {
+    if constexpr (!STATS) {
       // Registers 4q .. 4q+3 hold four consecutive columns.  Stores are raw
       // buffer stores over one resource per 32-row group (at most 32 V
       // floats: the host keeps V <= 2^24, so the size fits 2^31 bytes).  A
@@ -749,8 +777,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
         // unmasked instantiations compute the same thing.
         const int lim = a.V - vbase - 4 * fk;  // columns at offset < lim are valid
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int t = t0 + wt * 128 + 32 * j + fr;
+        for (int j = 0; j < NJ; ++j) {
+          const int t = t0 + wt * WT + 32 * j + fr;
           // 1) tile max: this lane's 64 values in (i, r) order, then the
           //    partner lane (fk flipped) holding the other 64 of the tile.
           float mx = -INFINITY;
@@ -869,10 +897,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
 // Launch shapes: the statistics kernel is persistent (one workgroup per
 // compute unit walking the tiles); the logits-stage kernel uses one
 // workgroup per tile.
-template <bool STATS, bool PERSIST, int EX>
+template <bool STATS, bool PERSIST, int EX, int NJ = 4>
 __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[CLAIM_OFS + 16];
-  gemm_body<STATS, PERSIST, EX>(a, smem);
+  gemm_body<STATS, PERSIST, EX, NJ>(a, smem);
 }
 
 // Per row t: M = max_j m_j (exact in any order), then
@@ -1053,14 +1081,14 @@ __global__ __launch_bounds__(COMPARE_THREADS) void compare_kernel(
 
 __global__ __launch_bounds__(256) void zero_kernel(float *x, int64_t n);
 
-hipError_t launch_gemm_stats(const GemmArgs &a, int workers, hipStream_t s) {
-  const int tiles = a.nMT * a.nVT;
-  // A multiple of 8 workgroups keeps each one on a fixed XCD.  As few as
-  // give the same number of rounds: a last round of a few workgroups, each
-  // waiting on its own weight stream, costs as much as a full one, while
-  // fewer concurrent workgroups share the bandwidth of every round (594
-  // tiles of a decode batch: 200 workgroups x 3 rounds instead of 256 and a
-  // third round of 82).
+namespace {
+
+// As few workgroups (a multiple of 8, so each stays on one XCD) as give the
+// same number of rounds: a last round of a few workgroups, each waiting on
+// its own weight stream, costs as much as a full one, while fewer concurrent
+// workgroups share the bandwidth of every round (594 tiles of a decode batch:
+// 200 workgroups x 3 rounds instead of 256 and a third round of 82).
+int balanced_grid(int tiles, int workers) {
   int grid = workers >= 8 ? workers - workers % 8 : 8;
   if (grid > tiles) grid = tiles;
   if (grid % 8 == 0) {
@@ -1068,29 +1096,49 @@ hipError_t launch_gemm_stats(const GemmArgs &a, int workers, hipStream_t s) {
     const int even = (tiles + rounds - 1) / rounds;
     grid = (even + 7) / 8 * 8;
   }
+  return grid;
+}
+
+template <int EX, int NJ>
+void launch_stats_kernel(const GemmArgs &a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_kernel<true, true, EX, NJ>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
+}
+
+template <int NJ>
+void launch_stats_nj(const GemmArgs &a, int grid, hipStream_t s) {
+  if (a.ex == 2) launch_stats_kernel<2, NJ>(a, grid, s);
+  else if (a.ex == 1) launch_stats_kernel<1, NJ>(a, grid, s);
+  else launch_stats_kernel<0, NJ>(a, grid, s);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_stats(const GemmArgs &args, int workers, hipStream_t s) {
+  GemmArgs a = args;
+  // A batch of at most 64 (128) rows runs in tiles of 64 (128) token rows:
+  // a quarter (half) of the MFMAs of full tiles, whose other rows would all
+  // be padding.  (The backward's logit gradient keeps full tiles.)
+  int nj = 4;
+  if (a.ex != 3 && a.T <= 64) nj = 1;
+  else if (a.ex != 3 && a.T <= 128) nj = 2;
+  a.nMT = (a.T + 64 * nj - 1) / (64 * nj);
+  const int grid = balanced_grid(a.nMT * a.nVT, workers);
   // the claim counters start at zero (a kernel, not a memset: capturable)
   if (a.queue) hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(64), 0, s, (float *)a.queue, 8);
   if (a.ex == 3)
     hipLaunchKernelGGL((gemm_kernel<true, true, 3>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
-  else if (a.ex == 2)
-    hipLaunchKernelGGL((gemm_kernel<true, true, 2>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
-  else if (a.ex == 1)
-    hipLaunchKernelGGL((gemm_kernel<true, true, 1>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
+  else if (nj == 1)
+    launch_stats_nj<1>(a, grid, s);
+  else if (nj == 2)
+    launch_stats_nj<2>(a, grid, s);
   else
-    hipLaunchKernelGGL((gemm_kernel<true, true, 0>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
+    launch_stats_nj<4>(a, grid, s);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_logits(const GemmArgs &a, int workers, hipStream_t s) {
-  const int tiles = a.nMT * a.nVT;
   if (a.queue) hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(64), 0, s, (float *)a.queue, 8);
-  int grid = workers >= 8 ? workers - workers % 8 : 8;
-  if (grid > tiles) grid = tiles;
-  if (grid % 8 == 0) {   // as few workgroups as give the same number of rounds
-    const int rounds = (tiles + grid - 1) / grid;
-    const int even = (tiles + rounds - 1) / rounds;
-    grid = (even + 7) / 8 * 8;
-  }
+  const int grid = balanced_grid(a.nMT * a.nVT, workers);
   if ((a.V & 3) == 0 && ((uintptr_t)a.logits & 15) == 0)
     hipLaunchKernelGGL((gemm_kernel<false, true, 0>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
   else

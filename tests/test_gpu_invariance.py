@@ -129,6 +129,32 @@ def test_decode_sweep_matches_batch_one_and_prefill(prefill):
         _assert_bits_equal(b, lse1[s], f"decode B={B} lse")
 
 
+@pytest.mark.parametrize("T,shift", [(1, 4095), (64, 11), (65, 4000), (100, 7), (128, 3000),
+                                     (129, 5), (4000, 1024)])
+def test_lower_tiles_same_bits(prefill, T, shift):
+    """Batches of at most 64 and 128 rows run in tiles of 64 and 128 token
+    rows; every row must carry the bits the same vector gets in the full
+    256-row tiles of the 4096-row call.  Row i holds prefill vector
+    (i + shift) mod 4096.  T = 129 and T = 4000 are full-tile walks whose last
+    token tile is ragged.  The options and the entropy take the same tiles."""
+    dev = prefill.hidden.device
+    lp_pre, lse_pre = rlk.rlk_selected_logp(prefill.hidden, prefill.weight, prefill.targets)
+    idx = (torch.arange(T, device=dev) + shift) % prefill.case.T
+    h = prefill.hidden[idx].contiguous()
+    y = prefill.targets[idx].contiguous()
+    lp, lse = rlk.rlk_selected_logp(h, prefill.weight, y)
+    _assert_bits_equal(lp, lp_pre[idx], f"T={T} logp")
+    _assert_bits_equal(lse, lse_pre[idx], f"T={T} lse")
+    lp2, lse2, ent2 = rlk.rlk_selected_logp_ex(prefill.hidden, prefill.weight, prefill.targets,
+                                              inv_temperature=0.7, logits_bf16=True,
+                                              entropy=True)
+    a, b, e = rlk.rlk_selected_logp_ex(h, prefill.weight, y, inv_temperature=0.7,
+                                       logits_bf16=True, entropy=True)
+    _assert_bits_equal(a, lp2[idx], f"T={T} options logp")
+    _assert_bits_equal(b, lse2[idx], f"T={T} options lse")
+    _assert_bits_equal(e, ent2[idx], f"T={T} entropy")
+
+
 def test_other_rows_do_not_matter(tiny, dev):
     """Replacing every other row's contents and targets leaves a row's bits."""
     lp, lse = rlk.rlk_selected_logp(tiny.hidden, tiny.weight, tiny.targets)
