@@ -93,8 +93,8 @@ extern "C" {
 #define RLK_ENTROPY     2  /* also produce the per-row entropy */
 
 /* Size limits: T <= 2^31 - 1 rows, V <= 2^31 - 1, H <= 65536, row strides
- * ld_hidden, ld_weight <= 2^21 elements, and ceil(T/256) * ceil(V/256) below
- * 2^31 workgroup tiles.  Beyond them: RLK_ERR_UNSUPPORTED. */
+ * ld_hidden, ld_weight <= 2^21 elements, and ceil(T/256) * ceil(V/256) at
+ * most 2^31 - 4097 workgroup tiles.  Beyond them: RLK_ERR_UNSUPPORTED. */
 
 /* Version of this ABI and of the numerical contract above. */
 int rlk_abi_version(void);

@@ -14,6 +14,8 @@ using rlk::ceil_div;
 constexpr int64_t MAX_ROWS = 2147483647;   // T and V fit in a signed int
 constexpr int64_t MAX_H = 65536;
 constexpr int64_t MAX_LD = int64_t(1) << 21;  // 256-row tile bytes < 2^31
+// workgroup tiles: a walk's tile index plus a grid of workgroups stays below 2^31
+constexpr int64_t MAX_TILES = MAX_ROWS - 4096;
 // Columns of a stored fp32 output: the store kernel addresses 32 rows through
 // one buffer resource, whose byte offsets must stay below 2^31.
 constexpr int64_t MAX_STORE_COLS = int64_t(1) << 24;
@@ -39,7 +41,7 @@ int check_shapes(int64_t T, int64_t H, int64_t V, int64_t ldh, int64_t ldw) {
       ldh > MAX_LD || ldw > MAX_LD)
     return RLK_ERR_UNSUPPORTED;
   const int64_t tiles = (int64_t)ceil_div(T, rlk::TILE_T) * ceil_div(V, rlk::TILE_V);
-  if (tiles > MAX_ROWS) return RLK_ERR_UNSUPPORTED;
+  if (tiles > MAX_TILES) return RLK_ERR_UNSUPPORTED;
   return RLK_OK;
 }
 

@@ -335,16 +335,19 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
 
   // One K block of the main loop.  Each accumulator advances in increasing k
   // (16 per MFMA); the fixed instruction order below only decides what
-  // overlaps with what: each of the first eight MFMAs of K step ks is
-  // followed by one read of step ks + 1's fragments, and every second MFMA
-  // of steps 0 and 1 (the odd ones) by one direct-to-LDS load of the next K
-  // block, so the sixteen loads are issued early but never in bursts (a
-  // burst stalls the wave's in-order issue, and with it the next MFMA, until
-  // the texture path takes the load); step 2 issues the L2 prefetch.
-  // Half-way through step 3 the wave waits for its loads and the workgroup
-  // meets at the barrier (the next block has landed; this block is no longer
-  // read), then the next block's first fragments are read under the last
-  // eight MFMAs.  The tile's last block (MORE false) has no next block of
+  // overlaps with what.  In the full tile (NQ = 16 MFMAs per K step) each of
+  // the first eight MFMAs of step ks is followed by one read of step ks + 1's
+  // fragments, and every second MFMA of steps 0 and 1 (the odd ones) by one
+  // direct-to-LDS load of the next K block, so the sixteen loads are issued
+  // early but never in bursts (a burst stalls the wave's in-order issue, and
+  // with it the next MFMA, until the texture path takes the load); step 2
+  // issues the L2 prefetch.  Half-way through step 3 the wave waits for its
+  // loads and the workgroup meets at the barrier (the next block has landed;
+  // this block is no longer read), then the next block's first fragments are
+  // read under the last eight MFMAs.  The lower tiles keep this order with
+  // fewer MFMAs: the sixteen loads go one (NQ = 8) or two (NQ = 4) behind
+  // each MFMA of steps 0 and 1, and reads that find no MFMA left follow the
+  // step's last one.  The tile's last block (MORE false) has no next block of
   // its own: its load slots carry the next tile's first block into the other
   // stage (r_w, r_h, p_w then name the next tile), which is free once the
   // barrier of the block before has passed.  p_w and kp name the weight
@@ -1092,9 +1095,8 @@ int balanced_grid(int tiles, int workers) {
   int grid = workers >= 8 ? workers - workers % 8 : 8;
   if (grid > tiles) grid = tiles;
   if (grid % 8 == 0) {
-    const int rounds = (tiles + grid - 1) / grid;
-    const int even = (tiles + rounds - 1) / rounds;
-    grid = (even + 7) / 8 * 8;
+    const int rounds = ceil_div(tiles, grid);
+    grid = (ceil_div(tiles, rounds) + 7) / 8 * 8;
   }
   return grid;
 }
@@ -1121,7 +1123,7 @@ hipError_t launch_gemm_stats(const GemmArgs &args, int workers, hipStream_t s) {
   int nj = 4;
   if (a.ex != 3 && a.T <= 64) nj = 1;
   else if (a.ex != 3 && a.T <= 128) nj = 2;
-  a.nMT = (a.T + 64 * nj - 1) / (64 * nj);
+  a.nMT = ceil_div(a.T, 64 * nj);   // in int64: T may be 2^31 - 1
   const int grid = balanced_grid(a.nMT * a.nVT, workers);
   // the claim counters start at zero (a kernel, not a memset: capturable)
   if (a.queue) hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(64), 0, s, (float *)a.queue, 8);

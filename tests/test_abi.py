@@ -81,6 +81,9 @@ def _call(hidden=FAKE, ldh=256, weight=FAKE, ldw=256, targets=FAKE, logp=FAKE,
     (dict(ldh=(1 << 21) + 8), rlk.RLK_ERR_UNSUPPORTED),
     (dict(T=1 << 31), rlk.RLK_ERR_UNSUPPORTED),
     (dict(V=1 << 31), rlk.RLK_ERR_UNSUPPORTED),
+    # 8388607 x 256 = 2^31 - 256 workgroup tiles: T and V are in range, but a
+    # tile index plus a grid of workgroups would pass 2^31
+    (dict(T=(2 ** 23 - 1) * 256, V=65536), rlk.RLK_ERR_UNSUPPORTED),
     (dict(hidden=None), rlk.RLK_ERR_NULL_POINTER),
     (dict(weight=None), rlk.RLK_ERR_NULL_POINTER),
     (dict(targets=None), rlk.RLK_ERR_NULL_POINTER),
