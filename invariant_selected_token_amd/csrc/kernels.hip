@@ -236,6 +236,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   auto gload = [&](__amdgpu_buffer_rsrc_t r_w, __amdgpu_buffer_rsrc_t r_h, int stage,
                    int kb, int q) {
     const int op = q < 8 ? 0 : 1, i = q & 7;
+    // a lower tile's hidden rows fill only its first 2 NJ row groups (the
+    // rest would fall outside the tile's resource and read nothing)
+    if (NJ < 4 && op == 1 && i >= 2 * NJ) return;
     lds_char *dst = lds_wave + stage * (2 * STAGE_BYTES) + op * STAGE_BYTES + (4 * i) * 1024;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? r_h : r_w, (lds_void *)dst, 16, gofs[op][i],
                                              (uint32_t)kb * (TILE_K * 2), 0, 0);
