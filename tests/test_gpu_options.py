@@ -110,7 +110,7 @@ def test_temperature_and_entropy_tiny(tiny, inv_tau):
 
 
 @pytest.mark.parametrize("T,H,V", [(1, 64, 5), (255, 256, 129), (300, 192, 1000),
-                                   (513, 128, 4133)])
+                                   (513, 128, 4133), (64, 128, 769), (100, 320, 2000)])
 def test_options_ragged_shapes(dev, T, H, V):
     c = synth.normal_case(f"opt_{T}x{H}x{V}", 900 + T, T, H, V)
     h, w, y = to_dev_bf16(c.hidden, dev), to_dev_bf16(c.weight, dev), to_dev_i32(c.targets, dev)
