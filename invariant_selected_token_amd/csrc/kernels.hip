@@ -148,7 +148,7 @@ __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1
 template <bool STATS, bool PERSIST, int EX, int NJ>
 __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   static_assert(NJ == 4 || NJ == 2 || NJ == 1, "token blocks of 32 rows per wave");
-  static_assert(NJ == 4 || (STATS && EX != 3), "lower tiles: the statistics epilogue only");
+  static_assert(NJ == 4 || EX != 3, "lower tiles: not the logit-gradient epilogue");
   constexpr int TT = 64 * NJ;   // token rows of a tile
   constexpr int WT = 32 * NJ;   // token rows of a wave
   constexpr int NQ = 4 * NJ;    // MFMAs per wave and K step
@@ -566,7 +566,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NJ; ++j) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -575,7 +575,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
                   u32x4{__float_as_uint(acc[i][j][4 * q]), __float_as_uint(acc[i][j][4 * q + 1]),
                         __float_as_uint(acc[i][j][4 * q + 2]),
                         __float_as_uint(acc[i][j][4 * q + 3])};
-          const int trow = t0 + wt * 128 + 32 * j;
+          const int trow = t0 + wt * WT + 32 * j;
           const int rows = min(32, a.T - trow);
           const __amdgpu_buffer_rsrc_t r_out = make_rsrc(
               a.logits + (size_t)trow * a.V, rows > 0 ? (uint32_t)rows * (uint32_t)a.V * 4u : 0u);
@@ -593,8 +593,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
         }
       } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int trow = t0 + wt * 128 + 32 * j;
+      for (int j = 0; j < NJ; ++j) {
+        const int trow = t0 + wt * WT + 32 * j;
         const int rows = min(32, a.T - trow);
         const __amdgpu_buffer_rsrc_t r_out = make_rsrc(
             a.logits + (size_t)trow * a.V, rows > 0 ? (uint32_t)rows * (uint32_t)a.V * 4u : 0u);
@@ -1121,24 +1121,35 @@ void launch_stats_nj(const GemmArgs &a, int grid, hipStream_t s) {
   else launch_stats_kernel<0, NJ>(a, grid, s);
 }
 
-}  // namespace
-
-hipError_t launch_gemm_stats(const GemmArgs &args, int workers, hipStream_t s) {
-  GemmArgs a = args;
-  // A batch of at most 64 (128) rows runs in tiles of 64 (128) token rows:
-  // a quarter (half) of the MFMAs of full tiles, whose other rows would all
-  // be padding.  (The backward's logit gradient keeps full tiles.)
+// A batch of at most 64 (128) rows runs in tiles of 64 (128) token rows: a
+// quarter (half) of the MFMAs of full tiles, whose other rows would all be
+// padding.  Tiles of 128 rows keep one workgroup per compute unit (measured
+// 2-3 % faster than the balanced rounds, 200 workgroups for 594 tiles);
+// tiles of 64 rows, bound by the weight stream, are faster on the balanced
+// grid (8 % at one row) -- as are full tiles.  Sets a.nMT for the tile
+// height; returns NJ, the tile height over 64.
+int pick_tiles(GemmArgs &a, int workers, int &grid) {
   int nj = 4;
   if (a.ex != 3 && a.T <= 64) nj = 1;
   else if (a.ex != 3 && a.T <= 128) nj = 2;
   a.nMT = ceil_div(a.T, 64 * nj);   // in int64: T may be 2^31 - 1
-  // Tiles of 128 rows keep one workgroup per compute unit (measured 2-3 %
-  // faster than the balanced rounds, 200 workgroups for 594 tiles); tiles of
-  // 64 rows, bound by the weight stream, are faster on the balanced grid (8 %
-  // at one row) -- as are full tiles.
   const int tiles = a.nMT * a.nVT;
-  int grid = balanced_grid(tiles, workers);
+  grid = balanced_grid(tiles, workers);
   if (nj == 2) grid = min(workers >= 8 ? workers - workers % 8 : 8, tiles);
+  return nj;
+}
+
+template <int EX, int NJ>
+void launch_store_kernel(const GemmArgs &a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_kernel<false, true, EX, NJ>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_stats(const GemmArgs &args, int workers, hipStream_t s) {
+  GemmArgs a = args;
+  int grid;
+  const int nj = pick_tiles(a, workers, grid);   // (the logit gradient: full tiles)
   // the claim counters start at zero (a kernel, not a memset: capturable)
   if (a.queue) hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(64), 0, s, (float *)a.queue, 8);
   if (a.ex == 3)
@@ -1152,13 +1163,24 @@ hipError_t launch_gemm_stats(const GemmArgs &args, int workers, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_logits(const GemmArgs &a, int workers, hipStream_t s) {
+hipError_t launch_gemm_logits(const GemmArgs &args, int workers, hipStream_t s) {
+  GemmArgs a = args;
+  int grid;
+  const int nj = pick_tiles(a, workers, grid);
   if (a.queue) hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(64), 0, s, (float *)a.queue, 8);
-  const int grid = balanced_grid(a.nMT * a.nVT, workers);
-  if ((a.V & 3) == 0 && ((uintptr_t)a.logits & 15) == 0)
-    hipLaunchKernelGGL((gemm_kernel<false, true, 0>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
-  else
-    hipLaunchKernelGGL((gemm_kernel<false, true, 1>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
+  // whole rows through LDS when V is a multiple of 4 and the output 16-byte
+  // aligned; otherwise one column per store (the same values)
+  const bool vec = (a.V & 3) == 0 && ((uintptr_t)a.logits & 15) == 0;
+  if (nj == 1) {
+    if (vec) launch_store_kernel<0, 1>(a, grid, s);
+    else launch_store_kernel<1, 1>(a, grid, s);
+  } else if (nj == 2) {
+    if (vec) launch_store_kernel<0, 2>(a, grid, s);
+    else launch_store_kernel<1, 2>(a, grid, s);
+  } else {
+    if (vec) launch_store_kernel<0, 4>(a, grid, s);
+    else launch_store_kernel<1, 4>(a, grid, s);
+  }
   return hipGetLastError();
 }
 

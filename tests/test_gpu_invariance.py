@@ -155,6 +155,35 @@ def test_lower_tiles_same_bits(prefill, T, shift):
     _assert_bits_equal(e, ent2[idx], f"T={T} entropy")
 
 
+@pytest.mark.parametrize("V", [151936, 151935])
+def test_logits_and_grad_hidden_lower_tiles_same_bits(prefill, V):
+    """The stored logits (whole-row stores for V a multiple of 4, one column
+    per store otherwise) and the backward's grad_hidden -- a row's gradient
+    depends on that row alone -- carry the same bits in lower tiles (batches
+    of at most 128 rows) as in the full tiles of a 512-row call."""
+    dev = prefill.hidden.device
+    w = prefill.weight[:V]
+    h512 = prefill.hidden[:512].contiguous()
+    y512 = torch.remainder(prefill.targets[:512], V).to(torch.int32).contiguous()
+    z_ref = rlk.rlk_logits(h512, w)
+    for T, shift in ((1, 300), (64, 5), (65, 400), (128, 200)):
+        idx = (torch.arange(T, device=dev) + shift) % 512
+        z = rlk.rlk_logits(h512[idx].contiguous(), w)
+        _assert_bits_equal(z, z_ref[idx].contiguous(), f"T={T} V={V} logits")
+    del z_ref
+    if V != 151936:
+        return
+    g = torch.from_numpy(np.random.default_rng(77).standard_normal(512).astype(np.float32)).to(dev)
+    _, lse512 = rlk.rlk_selected_logp(h512, w, y512)
+    gh_ref, _ = rlk.rlk_selected_logp_backward(h512, w, y512, lse512, g, want_weight=False)
+    for T, shift in ((64, 17), (100, 350)):
+        idx = (torch.arange(T, device=dev) + shift) % 512
+        gh, _ = rlk.rlk_selected_logp_backward(h512[idx].contiguous(), w, y512[idx].contiguous(),
+                                               lse512[idx].contiguous(), g[idx].contiguous(),
+                                               want_weight=False)
+        _assert_bits_equal(gh, gh_ref[idx].contiguous(), f"T={T} grad_hidden")
+
+
 def test_other_rows_do_not_matter(tiny, dev):
     """Replacing every other row's contents and targets leaves a row's bits."""
     lp, lse = rlk.rlk_selected_logp(tiny.hidden, tiny.weight, tiny.targets)
