@@ -12,6 +12,14 @@ whole hot path on one batch, with inputs already resident in HBM:
   3. rlk_compare x2   bitwise consistency of this step's logp and lse against
                       the first call's (mismatch count, max |diff|).
 Prints one JSON line.  Only one GPU is used; --gpus N > 1 exits.
+
+After the timed region (never inside it) the line also gets: per-step median
+and minimum times; the shader clock sampled while the statistics kernel runs
+(amd-smi); the invariance report of every workload (batch 1 vs batch N, row
+positions, packing, decode vs prefill, repeats, and a negative control), as
+mismatch count, max / mean / std of |diff| and the k3 estimator per variant;
+the vendor path (hipBLASLt GEMM + logsumexp + gather) as context; the other
+entry points' timings; and the fp64 oracle timed on the host.
 """
 
 from __future__ import annotations
@@ -21,7 +29,11 @@ import hashlib
 import json
 import os
 import re
+import shutil
+import statistics
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -56,29 +68,265 @@ def measured_traffic():
     return float(b.group(1))
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(case, seconds: float) -> dict:
-    """The fp64 oracle, as it stands, on a bounded sample of the same rows."""
+    """The fp64 oracle, as it stands, on a bounded sample of the same rows;
+    plus the single-thread time of the whole tiny workload."""
     import numpy as np
 
+    from invariant_selected_token_amd import synth
     from oracle import oracle as orc
 
+    # every call names its thread count: a count given to the oracle stays
+    # its OpenMP default for later calls
     cores = orc.max_threads()
+    tiny = synth.tiny_case()
+    t0 = time.perf_counter()
+    orc.selected_logp(tiny.hidden, tiny.weight, tiny.targets, nthreads=1)
+    tiny_s = time.perf_counter() - t0
     probe = max(2, min(cores, 16))
     t0 = time.perf_counter()
-    orc.selected_logp(case.hidden[:probe], case.weight, case.targets[:probe])
+    orc.selected_logp(case.hidden[:probe], case.weight, case.targets[:probe], nthreads=cores)
     per_row = (time.perf_counter() - t0) / probe
     n = int(max(probe, min(case.T, round(seconds / max(per_row, 1e-9)))))
     rng = np.random.Generator(np.random.PCG64(4321))
     rows = np.sort(rng.choice(case.T, size=n, replace=False))
     t0 = time.perf_counter()
-    orc.selected_logp(case.hidden[rows], case.weight, case.targets[rows])
+    orc.selected_logp(case.hidden[rows], case.weight, case.targets[rows], nthreads=cores)
     wall = time.perf_counter() - t0
     return {"value": n / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{n} of {case.T} rows of the same workload (seeded choice), "
-                      f"full vocabulary V={case.V}, fp64, {wall:.1f} s wall"}
+                      f"full vocabulary V={case.V}, fp64, {wall:.1f} s wall",
+            "tiny_T64_H256_V4096_single_thread_s": tiny_s}
+
+
+def sample_sclk(torch, fn, seconds: float = 3.0):
+    """Shader clock (MHz, mean over the XCDs' GFX clocks, median over the
+    samples) read with amd-smi while `fn` keeps the GPU busy; None when the
+    tool is missing or prints no clock."""
+    tool = shutil.which("amd-smi")
+    if tool is None:
+        return None
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                r = subprocess.run([tool, "metric", "-g", "0", "-c"], capture_output=True,
+                                   text=True, timeout=10)
+            except (OSError, subprocess.SubprocessError):
+                return
+            mhz = [int(x) for x in re.findall(r"GFX_\d+:\s*CLK:\s*(\d+)\s*MHz", r.stdout)]
+            if mhz:
+                samples.append(sum(mhz) / len(mhz))
+
+    for _ in range(5):
+        fn()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=15)
+    # the first sample may straddle the start of the load
+    use = samples[1:] if len(samples) > 2 else samples
+    if not use:
+        return None
+    return {"median_MHz": statistics.median(use), "min_MHz": min(use), "max_MHz": max(use),
+            "samples": len(use), "source": "amd-smi metric -c, GFX clocks of the XCDs"}
 
 
 VARIANTS = ("options", "slices", "backward", "rmsnorm", "topk20", "long_rollout", "decode")
+WORKLOADS = ("tiny", "prefill", "decode", "adversarial", "rollout", "negative_control")
+
+
+class Harness:
+    """Collects rlk_compare statistics per (workload, variant, output) on the
+    device and folds them on the host at the end: one synchronisation."""
+
+    def __init__(self, rlk, torch, dev):
+        self.rlk, self.torch, self.dev = rlk, torch, dev
+        self.parts = {}
+
+    def add(self, workload, variant, a, b, what="logp"):
+        st = self.torch.empty(8, dtype=self.torch.float64, device=self.dev)
+        self.rlk.rlk_compare(a.contiguous().view(-1), b.contiguous().view(-1), stats=st)
+        self.parts.setdefault((workload, variant, what), []).append(st)
+
+    def report(self):
+        out = {}
+        for (w, v, what), sts in self.parts.items():
+            s = self.torch.stack(sts).cpu().numpy()
+            n, k3n = s[:, 0].sum(), s[:, 6].sum()
+            mean = s[:, 3].sum() / n if n else 0.0
+            var = max(s[:, 4].sum() / n - mean * mean, 0.0) if n else 0.0
+            out.setdefault(w, {}).setdefault(v, {})[what] = {
+                "compared": int(n), "mismatch_count": int(s[:, 1].sum()),
+                "max_abs_diff": float(s[:, 2].max()), "mean_abs_diff": float(mean),
+                "std_abs_diff": float(var ** 0.5),
+                "k3_mean": float(s[:, 5].sum() / k3n) if k3n else 0.0}
+        return out
+
+
+def invariance_report(rlk, torch, np, prefill_dev, only=WORKLOADS):
+    """Bitwise self-consistency of every workload, per variant (the pages'
+    mismatch count and max |diff|; the vLLM blog summary's mean / std of
+    |diff| and k3).  prefill_dev = (hidden, weight, targets) on the device."""
+    from invariant_selected_token_amd import synth
+
+    hidden, weight, targets = prefill_dev
+    dev = hidden.device
+    H = Harness(rlk, torch, dev)
+
+    def to_dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def both(w, v, got, ref):
+        H.add(w, v, got[0], ref[0], "logp")
+        H.add(w, v, got[1], ref[1], "lse")
+
+    def call(h, W, y):
+        return rlk.rlk_selected_logp(h, W, y)
+
+    rng = np.random.Generator(np.random.PCG64(2468))
+    if "tiny" in only:
+        c = synth.tiny_case()
+        h, W, y = to_dev(c.hidden), to_dev(c.weight), torch.from_numpy(c.targets).to(dev)
+        ref = call(h, W, y)
+        for t in range(c.T):
+            both("tiny_T64", "batch1_vs_batch64", call(h[t:t + 1], W, y[t:t + 1]),
+                 (ref[0][t:t + 1], ref[1][t:t + 1]))
+        for _ in range(100):
+            both("tiny_T64", "repeats_100", call(h, W, y), ref)
+        for _ in range(8):
+            p = torch.from_numpy(rng.permutation(c.T)).to(dev)
+            both("tiny_T64", "permutations_8", call(h[p].contiguous(), W, y[p].contiguous()),
+                 (ref[0][p], ref[1][p]))
+    T = hidden.shape[0]
+    ref_pre = call(hidden, weight, targets)
+    if "prefill" in only:
+        w = "prefill_T4096"
+        for sq in range(T // 512):
+            sl = slice(512 * sq, 512 * (sq + 1))
+            both(w, "per_sequence_vs_packed", call(hidden[sl], weight, targets[sl]),
+                 (ref_pre[0][sl], ref_pre[1][sl]))
+        for _ in range(20):
+            both(w, "repeats_20", call(hidden, weight, targets), ref_pre)
+        p = torch.from_numpy(rng.permutation(T)).to(dev)
+        both(w, "permuted", call(hidden[p].contiguous(), weight, targets[p].contiguous()),
+             (ref_pre[0][p], ref_pre[1][p]))
+        for n in (1, 7, 100, 255, 257, 1000):
+            idx = (torch.arange(n, device=dev) + 13 * n) % T
+            both(w, "sub_batches_at_other_positions",
+                 call(hidden[idx].contiguous(), weight, targets[idx].contiguous()),
+                 (ref_pre[0][idx], ref_pre[1][idx]))
+    if "decode" in only:
+        plan = synth.decode_plan(prefill_T=T)
+        pool = torch.from_numpy(plan["pool"]).to(dev)
+        ph, py = hidden[pool].contiguous(), targets[pool].contiguous()
+        one_lp = torch.empty(pool.numel(), dtype=torch.float32, device=dev)
+        one_lse = torch.empty_like(one_lp)
+        for i in range(pool.numel()):
+            a, b = call(ph[i:i + 1], weight, py[i:i + 1])
+            one_lp[i:i + 1], one_lse[i:i + 1] = a, b
+        both("decode_sweep", "batch1_vs_prefill", (one_lp, one_lse),
+             (ref_pre[0][pool], ref_pre[1][pool]))
+        for B, slots in plan["batches"].items():
+            sl = torch.from_numpy(slots).to(dev)
+            got = call(ph[sl].contiguous(), weight, py[sl].contiguous())
+            both("decode_sweep", f"B={B}_vs_batch1", got, (one_lp[sl], one_lse[sl]))
+            both("decode_sweep", f"B={B}_vs_prefill", got,
+                 (ref_pre[0][pool[sl]], ref_pre[1][pool[sl]]))
+    if "adversarial" in only:
+        c = synth.adversarial_case()
+        h, W, y = to_dev(c.hidden), to_dev(c.weight), torch.from_numpy(c.targets).to(dev)
+        w = "adversarial_T1024"
+        ref = call(h, W, y)
+        for t in list(range(0, 96)) + [500, 1023]:
+            both(w, "batch1_vs_batch", call(h[t:t + 1], W, y[t:t + 1]),
+                 (ref[0][t:t + 1], ref[1][t:t + 1]))
+        for _ in range(100):
+            both(w, "repeats_100", call(h, W, y), ref)
+        for _ in range(3):
+            p = torch.from_numpy(rng.permutation(c.T)).to(dev)
+            both(w, "permutations_3", call(h[p].contiguous(), W, y[p].contiguous()),
+                 (ref[0][p], ref[1][p]))
+        del W
+    if "rollout" in only:
+        c = synth.long_rollout_case()
+        h, y = to_dev(c.hidden), torch.from_numpy(c.targets).to(dev)
+        w = "rollout_T16384"
+        ref = call(h, weight, y)
+        for sq in range(c.T // 512):
+            sl = slice(512 * sq, 512 * (sq + 1))
+            both(w, "per_response_vs_packed", call(h[sl], weight, y[sl]),
+                 (ref[0][sl], ref[1][sl]))
+        for _ in range(5):
+            both(w, "repeats_5", call(h, weight, y), ref)
+        p = torch.from_numpy(rng.permutation(c.T)).to(dev)
+        both(w, "permuted", call(h[p].contiguous(), weight, y[p].contiguous()),
+             (ref[0][p], ref[1][p]))
+        del h
+    if "negative_control" in only:
+        # the same mathematics in another summation order (K reversed in both
+        # operands) must show up as drift: mismatches > 0 (RL-Kernel blog,
+        # section 二: accumulation order changes the last bits)
+        rows = slice(0, 512)
+        got = call(hidden[rows].flip(1).contiguous(), weight.flip(1).contiguous(), targets[rows])
+        both("negative_control", "K_order_reversed_prefill_512_rows", got,
+             (ref_pre[0][rows], ref_pre[1][rows]))
+    return H.report()
+
+
+def vendor_context(torch, hidden, weight, targets, steps):
+    """The vendor path on the same GPU, as context (not a target): the bf16
+    logits GEMM of torch (hipBLASLt), logsumexp in fp32, gather.  Timed, and
+    checked for batch invariance (rows alone and in sub-batches against the
+    full batch)."""
+    import torch.nn.functional as F
+
+    def path(h, y):
+        z = F.linear(h, weight).float()
+        lse = torch.logsumexp(z, dim=1)
+        return z.gather(1, y.long()[:, None])[:, 0] - lse, lse
+
+    for _ in range(2):
+        path(hidden, targets)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        path(hidden, targets)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    lp, _ = path(hidden, targets)
+    mism, maxd, n = 0, 0.0, 0
+    for rows in (slice(0, 1), slice(100, 101), slice(0, 7), slice(0, 64), slice(1000, 1255),
+                 slice(0, 512)):
+        a, _ = path(hidden[rows], targets[rows])
+        d = (a - lp[rows]).abs()
+        mism += int((a.view(torch.int32) != lp[rows].view(torch.int32)).sum())
+        maxd = max(maxd, float(d.max()))
+        n += a.numel()
+    return {"ms": ms, "what": "F.linear bf16 (hipBLASLt) + logsumexp fp32 + gather",
+            "batch_invariance": {"compared": n, "mismatch_count": mism, "max_abs_diff": maxd,
+                                 "variants": "rows 0, 100, 0-6, 0-63, 1000-1254, 0-511 "
+                                             "alone vs in the 4096-row batch"}}
 
 
 def time_variants(rlk, torch, np, hidden, weight, targets, T, H, V, steps, flops,
@@ -250,14 +498,24 @@ def main() -> int:
                     help="comma-separated subset of: " + ", ".join(VARIANTS))
     ap.add_argument("--variant-steps", type=int, default=10,
                     help="timed calls per variant (options, vocabulary slices); 0 skips")
+    ap.add_argument("--no-harness", action="store_true",
+                    help="skip the per-workload invariance report")
+    ap.add_argument("--harness", default=",".join(WORKLOADS),
+                    help="comma-separated subset of: " + ", ".join(WORKLOADS))
+    ap.add_argument("--no-vendor", action="store_true",
+                    help="skip the vendor-path context timing")
+    ap.add_argument("--no-sclk", action="store_true",
+                    help="skip sampling the shader clock under load")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB before the "
                          "timed region (reference kernel for HBM counters)")
     args = ap.parse_args()
     variants = tuple(x for x in args.variants.split(",") if x)
     unknown = [x for x in variants if x not in VARIANTS]
+    unknown += [x for x in args.harness.split(",") if x and x not in WORKLOADS]
     if unknown:
-        print(f"bench.py: unknown variants {unknown}; choose from {VARIANTS}", file=sys.stderr)
+        print(f"bench.py: unknown variants {unknown}; choose from {VARIANTS} "
+              f"and {WORKLOADS}", file=sys.stderr)
         return 2
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -328,9 +586,13 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    gemm_ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(K)) / K
-    merge_ms = sum(ev[i][1].elapsed_time(ev[i][2]) for i in range(K)) / K
-    check_ms = sum(ev[i][2].elapsed_time(ev[i][3]) for i in range(K)) / K
+    g_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
+    m_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
+    c_ms = [ev[i][2].elapsed_time(ev[i][3]) for i in range(K)]
+    s_ms = [ev[i][0].elapsed_time(ev[i][3]) for i in range(K)]
+    gemm_ms = sum(g_ms) / K
+    merge_ms = sum(m_ms) / K
+    check_ms = sum(c_ms) / K
     s_lp = stats_lp.cpu().numpy()
     s_lse = stats_lse.cpu().numpy()
     mismatch = int(s_lp[:, 1].sum() + s_lse[:, 1].sum())
@@ -361,12 +623,34 @@ def main() -> int:
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": traffic},
         "stages_ms": {"gemm_stats": gemm_ms, "merge": merge_ms, "consistency_check": check_ms},
+        "stages_ms_median_min": {
+            "gemm_stats": [statistics.median(g_ms), min(g_ms)],
+            "merge": [statistics.median(m_ms), min(m_ms)],
+            "step_on_device": [statistics.median(s_ms), min(s_ms)]},
         "merge_hbm": {"GB/s": merge_bytes / (merge_ms * 1e-3) / 1e9,
                       "peak": PEAK_HBM_GBS, "bytes": merge_bytes},
         "consistency": {"mismatch_count": mismatch, "max_abs_diff": max_diff,
                         "compared": 2 * T * K},
         "kernel_source": kernel_source_digest(),
     }
+    if not args.no_sclk:
+        log("bench: sampling the shader clock under the statistics kernel")
+        clk = sample_sclk(torch, lambda: rlk.rlk_vocab_stats(hidden, weight, targets, ws))
+        out["sclk"] = clk
+        if clk:
+            # the same achieved rate against the peak at the clock the load sustained
+            peak_at = PEAK_BF16_TFLOPS * clk["median_MHz"] / 2400.0
+            out["roofline"]["frac_at_measured_sclk"] = achieved / peak_at
+            out["roofline"]["peak_at_measured_sclk"] = peak_at
+    if not args.no_harness:
+        log("bench: invariance report")
+        hs = tuple(x for x in args.harness.split(",") if x)
+        out["invariance"] = invariance_report(rlk, torch, np, (hidden, weight, targets), hs)
+        torch.cuda.empty_cache()
+    if not args.no_vendor:
+        log("bench: vendor path (context)")
+        out["vendor_context"] = vendor_context(torch, hidden, weight, targets, 10)
+        torch.cuda.empty_cache()
     if args.variant_steps > 0:
         out["variants"] = time_variants(rlk, torch, np, hidden, weight, targets, T, H, V,
                                         args.variant_steps, flops, variants)

@@ -23,9 +23,9 @@
  * Numerical contract (fixed for RLK_ABI_VERSION):
  *   - Inputs are bfloat16 bit patterns; products are exact in fp32, sums are
  *     fp32, accumulated over k = 0 .. H-1 in chunks of 16 in increasing order,
- *     one workgroup per tile of 256 vocabulary rows x 256 token rows (64 or
- *     128 token rows for batches of at most 64 or 128 rows: the same
- *     operations per logit), no split-K.
+ *     one workgroup per tile of 256 vocabulary rows x 256 token rows -- the
+ *     same tile for every batch size; rows past T are predicated off inside
+ *     it -- and no split-K.
  *   - Logits are never rounded to bf16 and never written to memory.
  *   - Per (row, 128-wide vocabulary tile): tile max m_j and
  *     s_j = sum exp(z - m_j) with a reduction tree that depends only on the
@@ -72,7 +72,12 @@
 extern "C" {
 #endif
 
-#define RLK_ABI_VERSION 2
+/* Version history: 1 the first contract; 2 added the options, backward,
+ * RMSNorm and top-k entry points; 3 gave rlk_selected_logp_workspace_bytes
+ * the (T, H, V) signature, named the logits stage rlk_debug_logits (rlk_logits
+ * stays as an alias), documented the workspace layout (rlk_workspace_layout)
+ * and lowered the T and V limits to 2^31 - 4096. */
+#define RLK_ABI_VERSION 3
 
 /* Status codes returned by every entry point that can fail. */
 #define RLK_OK                      0
@@ -92,9 +97,10 @@ extern "C" {
 #define RLK_LOGITS_BF16 1  /* round every (scaled) logit to bfloat16 */
 #define RLK_ENTROPY     2  /* also produce the per-row entropy */
 
-/* Size limits: T <= 2^31 - 1 rows, V <= 2^31 - 1, H <= 65536, row strides
- * ld_hidden, ld_weight <= 2^21 elements, and ceil(T/256) * ceil(V/256) at
- * most 2^31 - 4097 workgroup tiles.  Beyond them: RLK_ERR_UNSUPPORTED. */
+/* Size limits: T <= 2^31 - 4096 rows, V <= 2^31 - 4096, H <= 65536, row
+ * strides ld_hidden, ld_weight <= 2^21 elements, and ceil(T/256) *
+ * ceil(V/256) at most 2^31 - 8192 workgroup tiles.  Beyond them:
+ * RLK_ERR_UNSUPPORTED. */
 
 /* Version of this ABI and of the numerical contract above. */
 int rlk_abi_version(void);
@@ -110,13 +116,35 @@ int rlk_last_hip_error(void);
  * max and sum of exponentials are merged.  Part of the numerical contract. */
 int rlk_vocab_tile(void);
 
-/* Bytes of device workspace rlk_selected_logp needs for T rows and a
- * vocabulary of V (H does not matter).  Returns 0 when T <= 0 or V <= 0.
- * The contents are opaque to callers. */
-size_t rlk_selected_logp_workspace_bytes(int64_t T, int64_t V);
-/* Layout detail: 2 * ceil(V/128) * T floats of tile statistics, then T floats
- * of target logits, each region rounded up to 256 bytes, then 256 bytes of
- * tile-claim counters for the GEMM's workgroups (reset by every call). */
+/* Bytes of device workspace rlk_selected_logp needs for T rows, hidden size
+ * H and a vocabulary of V (H does not change the size).  Returns 0 when
+ * T <= 0, H <= 0 or V <= 0, or a size is above the limits.  The static-size
+ * workspace the caller allocates once is what lets the hot path run with no
+ * allocation and no host synchronisation (the vLLM blog summary's CUDA Graph
+ * requirements).  The layout is given by rlk_workspace_layout. */
+size_t rlk_selected_logp_workspace_bytes(int64_t T, int64_t H, int64_t V);
+
+/* Byte offsets of the regions of a workspace for (T, V, flags), for callers
+ * that exchange tile statistics between devices that hold different
+ * vocabulary shards (the RL-Kernel blog, section 七: every shard computes
+ * local statistics, merged in a fixed vocabulary-tile order).  With
+ * nST = ceil(V / 128):
+ *   *off_m   part_m, fp32 [nST][T]: part_m[j][t] = max of row t's logits in
+ *            vocabulary tile j (rows 128 j .. 128 j + 127 of w);
+ *   *off_s   part_s, fp32 [nST][T]: sum of exp(z - part_m[j][t]) over tile j;
+ *   *off_xt  xt, fp32 [T]: z[t][y[t]], written by the call (or slice) whose
+ *            vocabulary range holds y[t]; not written otherwise;
+ *   *off_u   part_u, fp32 [nST][T]: sum of exp(z - m_j) (z - m_j) over tile
+ *            j; present with RLK_ENTROPY only (without it nothing of the
+ *            caller's lies at this offset).
+ * The statistics of the tiles [j0, j1) of a slice are the contiguous bytes
+ * [j0 T 4, j1 T 4) after off_m and after off_s (and off_u): a shard's part of
+ * the workspace is one contiguous piece per region.  Anything past the
+ * regions (tile-claim counters) is private to the library.  Any pointer may
+ * be NULL.  Returns RLK_ERR_INVALID_SHAPE / RLK_ERR_UNSUPPORTED /
+ * RLK_ERR_INVALID_VALUE for sizes or flags rlk_workspace_bytes_ex refuses. */
+int rlk_workspace_layout(int64_t T, int64_t V, int flags, size_t *off_m, size_t *off_s,
+                         size_t *off_xt, size_t *off_u);
 
 /* Selected-token log-probabilities: the hot path.
  *   hidden    bf16 [T][ld_hidden] row-major, only the first H columns read;
@@ -130,7 +158,7 @@ size_t rlk_selected_logp_workspace_bytes(int64_t T, int64_t V);
  *   H         hidden size, a multiple of 64.
  *   V         vocabulary size (rows of weight taken into the LSE).
  *   workspace device scratch of at least
- *             rlk_selected_logp_workspace_bytes(T, V) bytes, 16-byte
+ *             rlk_selected_logp_workspace_bytes(T, H, V) bytes, 16-byte
  *             aligned; its contents on entry do not matter.
  *   stream    hipStream_t or NULL.
  * Three kernels run on `stream`: a reset of the workspace's tile-claim
@@ -304,7 +332,11 @@ int rlk_rmsnorm(const void *x, int64_t ld_x, const void *gamma, float eps, void 
  * accumulators: logits[t * V + v], row-major [T][V], 4-byte aligned.
  * Argument rules as above, and V <= 2^24 (RLK_ERR_UNSUPPORTED beyond: 32 rows
  * of the output must span less than 2^31 bytes); no workspace.  Test,
- * debugging and top-k use: it writes 4*T*V bytes. */
+ * debugging and top-k use: it writes 4*T*V bytes.  rlk_logits is the same
+ * call under its earlier name. */
+int rlk_debug_logits(const void *hidden, int64_t ld_hidden, const void *weight,
+                     int64_t ld_weight, float *logits, int64_t T, int64_t H,
+                     int64_t V, void *stream);
 int rlk_logits(const void *hidden, int64_t ld_hidden, const void *weight,
                int64_t ld_weight, float *logits, int64_t T, int64_t H,
                int64_t V, void *stream);
@@ -339,7 +371,7 @@ int rlk_topk_logp(const float *logits, int64_t ld_logits, const float *lse,
  * estimator r - 1 - log r with r = exp(a - b) (vLLM blog summary, "diff = 0"
  * definition).  One workgroup, fixed reduction order, so the statistics are
  * themselves deterministic.
- *   a, b   fp32 [n] device arrays, 4-byte aligned.  n >= 0, n < 2^31.
+ *   a, b   fp32 [n] device arrays, 4-byte aligned.  0 <= n <= 2^31 - 1.
  *   stats  fp64 [8] device array, 8-byte aligned, overwritten with:
  *          [0] n
  *          [1] mismatch count: entries whose 32-bit patterns differ

@@ -32,9 +32,10 @@ RLK_ENTROPY = 2
 
 EXPORTED = (
     "rlk_abi_version", "rlk_status_string", "rlk_last_hip_error",
-    "rlk_vocab_tile", "rlk_selected_logp_workspace_bytes",
+    "rlk_vocab_tile", "rlk_selected_logp_workspace_bytes", "rlk_workspace_layout",
     "rlk_selected_logp", "rlk_vocab_stats", "rlk_vocab_stats_shard",
-    "rlk_vocab_merge", "rlk_logits", "rlk_compare", "rlk_workspace_bytes_ex",
+    "rlk_vocab_merge", "rlk_debug_logits", "rlk_logits", "rlk_compare",
+    "rlk_workspace_bytes_ex",
     "rlk_selected_logp_ex", "rlk_vocab_stats_ex", "rlk_vocab_merge_ex",
     "rlk_selected_logp_backward_workspace_bytes", "rlk_selected_logp_backward",
     "rlk_logp_grad_logits", "rlk_rmsnorm", "rlk_topk_logp",
@@ -73,8 +74,11 @@ def lib() -> ctypes.CDLL:
     L.rlk_status_string.restype = ctypes.c_char_p
     L.rlk_last_hip_error.restype = c_int
     L.rlk_vocab_tile.restype = c_int
-    L.rlk_selected_logp_workspace_bytes.argtypes = [i64, i64]
+    L.rlk_selected_logp_workspace_bytes.argtypes = [i64, i64, i64]
     L.rlk_selected_logp_workspace_bytes.restype = sz
+    psz = ctypes.POINTER(sz)
+    L.rlk_workspace_layout.argtypes = [i64, i64, c_int, psz, psz, psz, psz]
+    L.rlk_workspace_layout.restype = c_int
     L.rlk_selected_logp.argtypes = [vp, i64, vp, i64, vp, vp, vp, i64, i64, i64,
                                     vp, sz, vp]
     L.rlk_selected_logp.restype = c_int
@@ -85,8 +89,9 @@ def lib() -> ctypes.CDLL:
     L.rlk_vocab_stats_shard.restype = c_int
     L.rlk_vocab_merge.argtypes = [vp, vp, vp, i64, i64, vp, sz, vp]
     L.rlk_vocab_merge.restype = c_int
-    L.rlk_logits.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, vp]
-    L.rlk_logits.restype = c_int
+    for name in ("rlk_debug_logits", "rlk_logits"):
+        getattr(L, name).argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, vp]
+        getattr(L, name).restype = c_int
     L.rlk_compare.argtypes = [vp, vp, i64, vp, vp]
     L.rlk_compare.restype = c_int
     f32 = ctypes.c_float
@@ -132,8 +137,17 @@ def rlk_vocab_tile() -> int:
     return int(lib().rlk_vocab_tile())
 
 
-def rlk_selected_logp_workspace_bytes(T: int, V: int) -> int:
-    return int(lib().rlk_selected_logp_workspace_bytes(int(T), int(V)))
+def rlk_selected_logp_workspace_bytes(T: int, H: int, V: int) -> int:
+    return int(lib().rlk_selected_logp_workspace_bytes(int(T), int(H), int(V)))
+
+
+def rlk_workspace_layout(T: int, V: int, flags: int = 0) -> dict:
+    """Byte offsets of the workspace regions for (T, V, flags): part_m and
+    part_s ([ceil(V/128)][T] fp32, tile-major), xt ([T] fp32) and part_u."""
+    offs = [ctypes.c_size_t(0) for _ in range(4)]
+    _call("rlk_workspace_layout", lib().rlk_workspace_layout(
+        int(T), int(V), int(flags), *[ctypes.byref(o) for o in offs]))
+    return dict(zip(("part_m", "part_s", "xt", "part_u"), (int(o.value) for o in offs)))
 
 
 def rlk_workspace_bytes_ex(T: int, V: int, flags: int) -> int:
@@ -162,6 +176,14 @@ def _bf16_operand(name, t, device=None):
         raise ValueError(f"{name} must be 2-D with unit column stride")
     _check_device(name, t, device)
     return t.data_ptr(), t.stride(0)
+
+
+def _on(stream):
+    """Allocations made inside belong to ``stream`` (the side stream the call
+    runs on), so the caching allocator does not hand their memory to other
+    work while that stream's kernels still use it."""
+    import contextlib
+    return _torch().cuda.stream(stream) if stream is not None else contextlib.nullcontext()
 
 
 def _stream_ptr(stream, device):
@@ -193,12 +215,13 @@ def _prepare(hidden, weight, targets, V):
     return dev, hp, ldh, wp, ldw, T, H, V
 
 
-def _outputs(dev, T, logp, lse):
+def _outputs(dev, T, logp, lse, stream=None):
     torch = _torch()
-    if logp is None:
-        logp = torch.empty(T, dtype=torch.float32, device=dev)
-    if lse is None:
-        lse = torch.empty(T, dtype=torch.float32, device=dev)
+    with _on(stream):
+        if logp is None:
+            logp = torch.empty(T, dtype=torch.float32, device=dev)
+        if lse is None:
+            lse = torch.empty(T, dtype=torch.float32, device=dev)
     for name, t in (("logp", logp), ("lse", lse)):
         if t.dtype != torch.float32 or t.shape != (T,) or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous float32 [T] tensor")
@@ -206,16 +229,18 @@ def _outputs(dev, T, logp, lse):
     return logp, lse
 
 
-def workspace_for(T: int, V: int, device):
-    """A device workspace tensor large enough for T rows and vocabulary V."""
+def workspace_for(T: int, V: int, device, flags: int = 0, stream=None):
+    """A device workspace tensor large enough for T rows and vocabulary V
+    (allocated for ``stream`` when one is given)."""
     torch = _torch()
-    need = rlk_selected_logp_workspace_bytes(T, V)
-    return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    need = rlk_workspace_bytes_ex(T, V, flags)
+    with _on(stream):
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
 
 
-def _workspace(dev, T, V, workspace):
+def _workspace(dev, T, V, workspace, stream=None):
     if workspace is None:
-        workspace = workspace_for(T, V, dev)
+        workspace = workspace_for(T, V, dev, stream=stream)
     _check_device("workspace", workspace, dev)
     return workspace, workspace.numel() * workspace.element_size()
 
@@ -230,8 +255,8 @@ def rlk_selected_logp(hidden, weight, targets, logp=None, lse=None,
     current torch stream) without synchronising.
     """
     dev, hp, ldh, wp, ldw, T, H, V = _prepare(hidden, weight, targets, V)
-    logp, lse = _outputs(dev, T, logp, lse)
-    ws, ws_bytes = _workspace(dev, T, V, workspace)
+    logp, lse = _outputs(dev, T, logp, lse, stream)
+    ws, ws_bytes = _workspace(dev, T, V, workspace, stream)
     _call("rlk_selected_logp", lib().rlk_selected_logp(
         hp, ldh, wp, ldw, targets.data_ptr(), logp.data_ptr(), lse.data_ptr(),
         T, H, V, ws.data_ptr(), ws_bytes, _stream_ptr(stream, dev)))
@@ -242,7 +267,7 @@ def rlk_vocab_stats(hidden, weight, targets, workspace, V=None, stream=None):
     """Stage 1: logit GEMM + per-tile statistics + target capture into
     ``workspace`` (see :func:`workspace_for`)."""
     dev, hp, ldh, wp, ldw, T, H, V = _prepare(hidden, weight, targets, V)
-    ws, ws_bytes = _workspace(dev, T, V, workspace)
+    ws, ws_bytes = _workspace(dev, T, V, workspace, stream)
     _call("rlk_vocab_stats", lib().rlk_vocab_stats(
         hp, ldh, wp, ldw, targets.data_ptr(), T, H, V, ws.data_ptr(), ws_bytes,
         _stream_ptr(stream, dev)))
@@ -280,7 +305,7 @@ def rlk_vocab_merge(targets, workspace, V, logp=None, lse=None, stream=None):
     if targets.dtype != torch.int32 or targets.dim() != 1 or not targets.is_contiguous():
         raise ValueError("targets must be a contiguous int32 [T] tensor")
     T = targets.shape[0]
-    logp, lse = _outputs(dev, T, logp, lse)
+    logp, lse = _outputs(dev, T, logp, lse, stream)
     _check_device("workspace", workspace, dev)
     ws_bytes = workspace.numel() * workspace.element_size()
     _call("rlk_vocab_merge", lib().rlk_vocab_merge(
@@ -293,12 +318,13 @@ def _flags(logits_bf16, entropy):
     return (RLK_LOGITS_BF16 if logits_bf16 else 0) | (RLK_ENTROPY if entropy else 0)
 
 
-def _entropy_out(dev, T, entropy, want):
+def _entropy_out(dev, T, entropy, want, stream=None):
     torch = _torch()
     if not want:
         return None
     if entropy is None or entropy is True:
-        entropy = torch.empty(T, dtype=torch.float32, device=dev)
+        with _on(stream):
+            entropy = torch.empty(T, dtype=torch.float32, device=dev)
     if entropy.dtype != torch.float32 or entropy.shape != (T,) or not entropy.is_contiguous():
         raise ValueError("entropy must be a contiguous float32 [T] tensor")
     _check_device("entropy", entropy, dev)
@@ -312,12 +338,11 @@ def rlk_selected_logp_ex(hidden, weight, targets, inv_temperature=1.0, logits_bf
     ``inv_temperature``, optionally rounded to bf16; ``entropy`` True (or an
     output tensor) also returns the per-row entropy, else None."""
     dev, hp, ldh, wp, ldw, T, H, V = _prepare(hidden, weight, targets, V)
-    logp, lse = _outputs(dev, T, logp, lse)
+    logp, lse = _outputs(dev, T, logp, lse, stream)
     flags = _flags(logits_bf16, entropy is not False and entropy is not None)
-    ent = _entropy_out(dev, T, entropy, flags & RLK_ENTROPY)
+    ent = _entropy_out(dev, T, entropy, flags & RLK_ENTROPY, stream)
     if workspace is None:
-        workspace = _torch().empty(max(rlk_workspace_bytes_ex(T, V, flags), 1),
-                                   dtype=_torch().uint8, device=dev)
+        workspace = workspace_for(T, V, dev, flags, stream)
     _check_device("workspace", workspace, dev)
     ws_bytes = workspace.numel() * workspace.element_size()
     _call("rlk_selected_logp_ex", lib().rlk_selected_logp_ex(
@@ -360,9 +385,9 @@ def rlk_vocab_merge_ex(targets, workspace, V, logits_bf16=False, entropy=False, 
     if targets.dtype != torch.int32 or targets.dim() != 1 or not targets.is_contiguous():
         raise ValueError("targets must be a contiguous int32 [T] tensor")
     T = targets.shape[0]
-    logp, lse = _outputs(dev, T, logp, lse)
+    logp, lse = _outputs(dev, T, logp, lse, stream)
     flags = _flags(logits_bf16, entropy is not False and entropy is not None)
-    ent = _entropy_out(dev, T, entropy, flags & RLK_ENTROPY)
+    ent = _entropy_out(dev, T, entropy, flags & RLK_ENTROPY, stream)
     _check_device("workspace", workspace, dev)
     ws_bytes = workspace.numel() * workspace.element_size()
     _call("rlk_vocab_merge_ex", lib().rlk_vocab_merge_ex(
@@ -393,10 +418,11 @@ def rlk_selected_logp_backward(hidden, weight, targets, lse, grad_logp, inv_temp
     dev, hp, ldh, wp, ldw, T, H, V = _prepare(hidden, weight, targets, V)
     lp_ = _f32_vec("lse", lse, T, dev)
     gp_ = _f32_vec("grad_logp", grad_logp, T, dev)
-    if want_hidden and grad_hidden is None:
-        grad_hidden = torch.empty((T, H), dtype=torch.float32, device=dev)
-    if want_weight and grad_weight is None:
-        grad_weight = torch.empty((V, H), dtype=torch.float32, device=dev)
+    with _on(stream):
+        if want_hidden and grad_hidden is None:
+            grad_hidden = torch.empty((T, H), dtype=torch.float32, device=dev)
+        if want_weight and grad_weight is None:
+            grad_weight = torch.empty((V, H), dtype=torch.float32, device=dev)
     for name, t, shape in (("grad_hidden", grad_hidden if want_hidden else None, (T, H)),
                            ("grad_weight", grad_weight if want_weight else None, (V, H))):
         if t is not None:
@@ -406,8 +432,9 @@ def rlk_selected_logp_backward(hidden, weight, targets, lse, grad_logp, inv_temp
     gh = grad_hidden if want_hidden else None
     gw = grad_weight if want_weight else None
     if workspace is None:
-        workspace = torch.empty(max(rlk_selected_logp_backward_workspace_bytes(T, H, V), 1),
-                                dtype=torch.uint8, device=dev)
+        with _on(stream):
+            workspace = torch.empty(max(rlk_selected_logp_backward_workspace_bytes(T, H, V), 1),
+                                    dtype=torch.uint8, device=dev)
     _check_device("workspace", workspace, dev)
     _call("rlk_selected_logp_backward", lib().rlk_selected_logp_backward(
         hp, ldh, wp, ldw, targets.data_ptr(), lp_, gp_,
@@ -424,7 +451,8 @@ def rlk_logp_grad_logits(hidden, weight, targets, lse, grad_logp, inv_temperatur
     dev, hp, ldh, wp, ldw, T, H, V = _prepare(hidden, weight, targets, V)
     Vp = (V + 63) // 64 * 64
     if dz is None:
-        dz = torch.empty((T, Vp), dtype=torch.bfloat16, device=dev)
+        with _on(stream):
+            dz = torch.empty((T, Vp), dtype=torch.bfloat16, device=dev)
     if dz.dim() != 2 or dz.shape[0] != T or dz.stride(1) != 1 or dz.element_size() != 2:
         raise ValueError("dz must be a 2-D 16-bit [T, >= Vp] tensor with unit column stride")
     _check_device("dz", dz, dev)
@@ -445,7 +473,8 @@ def rlk_rmsnorm(x, gamma, eps=1e-6, y=None, stream=None):
         raise ValueError("gamma must be a contiguous [H] tensor")
     gp, _ = _bf16_operand("gamma", gamma.view(1, H), dev)
     if y is None:
-        y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        with _on(stream):
+            y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     yp, ldy = _bf16_operand("y", y, dev)
     if tuple(y.shape) != (T, H):
         raise ValueError("y must have shape [T, H]")
@@ -467,10 +496,11 @@ def rlk_topk_logp(logits, lse, workspace, k, inv_temperature=1.0, logits_bf16=Fa
     V = int(logits.shape[1] if V is None else V)
     lp_ = _f32_vec("lse", lse, T, dev)
     _check_device("workspace", workspace, dev)
-    if topk_logp is None:
-        topk_logp = torch.empty((T, k), dtype=torch.float32, device=dev)
-    if topk_ids is None:
-        topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    with _on(stream):
+        if topk_logp is None:
+            topk_logp = torch.empty((T, k), dtype=torch.float32, device=dev)
+        if topk_ids is None:
+            topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
     _call("rlk_topk_logp", lib().rlk_topk_logp(
         logits.data_ptr(), logits.stride(0), lp_, workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), T, V, int(k), float(inv_temperature),
@@ -485,8 +515,7 @@ def topk_logprobs(hidden, weight, targets, k, inv_temperature=1.0, logits_bf16=F
     row: the statistics pass, the stored logits, then the selection."""
     dev, _, _, _, _, T, _, V = _prepare(hidden, weight, targets, None)
     flags = RLK_LOGITS_BF16 if logits_bf16 else 0
-    ws = _torch().empty(max(rlk_workspace_bytes_ex(T, V, flags), 1), dtype=_torch().uint8,
-                        device=dev)
+    ws = workspace_for(T, V, dev, flags, stream)
     logp, lse, _ = rlk_selected_logp_ex(hidden, weight, targets,
                                         inv_temperature=inv_temperature,
                                         logits_bf16=logits_bf16, workspace=ws, stream=stream)
@@ -495,7 +524,7 @@ def topk_logprobs(hidden, weight, targets, k, inv_temperature=1.0, logits_bf16=F
     return logp, lse, tl, ti
 
 
-def rlk_logits(hidden, weight, logits=None, V=None, stream=None):
+def rlk_debug_logits(hidden, weight, logits=None, V=None, stream=None):
     """fp32 logits [T, V] from the same GEMM main loop (stage comparison)."""
     torch = _torch()
     dev = hidden.device
@@ -504,13 +533,17 @@ def rlk_logits(hidden, weight, logits=None, V=None, stream=None):
     T, H = hidden.shape
     V = int(weight.shape[0] if V is None else V)
     if logits is None:
-        logits = torch.empty((T, V), dtype=torch.float32, device=dev)
+        with _on(stream):
+            logits = torch.empty((T, V), dtype=torch.float32, device=dev)
     if logits.dtype != torch.float32 or logits.shape != (T, V) or not logits.is_contiguous():
         raise ValueError("logits must be a contiguous float32 [T, V] tensor")
     _check_device("logits", logits, dev)
-    _call("rlk_logits", lib().rlk_logits(hp, ldh, wp, ldw, logits.data_ptr(),
-                                         T, H, V, _stream_ptr(stream, dev)))
+    _call("rlk_debug_logits", lib().rlk_debug_logits(hp, ldh, wp, ldw, logits.data_ptr(),
+                                                     T, H, V, _stream_ptr(stream, dev)))
     return logits
+
+
+rlk_logits = rlk_debug_logits
 
 
 def rlk_compare(a, b, stats=None, stream=None):
@@ -521,10 +554,11 @@ def rlk_compare(a, b, stats=None, stream=None):
         raise ValueError("a and b must be float32 tensors of one shape")
     _check_device("a", a, dev)
     _check_device("b", b, dev)
-    a = a.contiguous()
-    b = b.contiguous()
-    if stats is None:
-        stats = torch.empty(8, dtype=torch.float64, device=dev)
+    with _on(stream):
+        a = a.contiguous()
+        b = b.contiguous()
+        if stats is None:
+            stats = torch.empty(8, dtype=torch.float64, device=dev)
     _check_device("stats", stats, dev)
     _call("rlk_compare", lib().rlk_compare(a.data_ptr(), b.data_ptr(), a.numel(),
                                            stats.data_ptr(), _stream_ptr(stream, dev)))

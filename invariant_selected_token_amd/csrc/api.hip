@@ -11,7 +11,11 @@ namespace {
 
 using rlk::ceil_div;
 
-constexpr int64_t MAX_ROWS = 2147483647;   // T and V fit in a signed int
+// T and V: a tile's last row index (up to 255 past the last real row) and
+// every per-row index the kernels form in int stay below 2^31.
+constexpr int64_t MAX_ROWS = 2147483647 - 4095;
+// Elements of rlk_compare (indexed in 64 bits on the device).
+constexpr int64_t MAX_COMPARE = 2147483647;
 constexpr int64_t MAX_H = 65536;
 constexpr int64_t MAX_LD = int64_t(1) << 21;  // 256-row tile bytes < 2^31
 // workgroup tiles: a walk's tile index plus a grid of workgroups stays below 2^31
@@ -184,7 +188,7 @@ const char *rlk_status_string(int status) {
       return "invalid shape (T < 0, H <= 0, V <= 0, n < 0 or ld < H)";
     case RLK_ERR_UNSUPPORTED:
       return "unsupported size (H must be a multiple of 64 and <= 65536; "
-             "T, V < 2^31; ld <= 2^21)";
+             "T, V <= 2^31 - 4096; ld <= 2^21)";
     case RLK_ERR_MISALIGNED:
       return "misaligned pointer or row stride (16-byte operands, ld % 8 == 0, "
              "4-byte vectors)";
@@ -202,7 +206,21 @@ size_t rlk_workspace_bytes_ex(int64_t T, int64_t V, int flags) {
   return ws_bytes_for(T, V, flags);
 }
 
-size_t rlk_selected_logp_workspace_bytes(int64_t T, int64_t V) {
+int rlk_workspace_layout(int64_t T, int64_t V, int flags, size_t *off_m, size_t *off_s,
+                         size_t *off_xt, size_t *off_u) {
+  if (T <= 0 || V <= 0) return RLK_ERR_INVALID_SHAPE;
+  if (T > MAX_ROWS || V > MAX_ROWS) return RLK_ERR_UNSUPPORTED;
+  if (check_options(1.0f, flags) != RLK_OK) return RLK_ERR_INVALID_VALUE;
+  // the carve-up every entry point uses (rlk_vocab_stats_ex, rlk_vocab_merge_ex)
+  if (off_m) *off_m = 0;
+  if (off_s) *off_s = stats_bytes(T, V);
+  if (off_xt) *off_xt = 2 * stats_bytes(T, V);
+  if (off_u) *off_u = part_u_offset(T, V);
+  return RLK_OK;
+}
+
+size_t rlk_selected_logp_workspace_bytes(int64_t T, int64_t H, int64_t V) {
+  if (H <= 0) return 0;   // H does not change the size, but must be a size
   return rlk_workspace_bytes_ex(T, V, 0);
 }
 
@@ -460,9 +478,9 @@ int rlk_topk_logp(const float *logits, int64_t ld_logits, const float *lse,
                                      topk_logp, topk_ids, static_cast<hipStream_t>(stream)));
 }
 
-int rlk_logits(const void *hidden, int64_t ld_hidden, const void *weight,
-               int64_t ld_weight, float *logits, int64_t T, int64_t H,
-               int64_t V, void *stream) {
+int rlk_debug_logits(const void *hidden, int64_t ld_hidden, const void *weight,
+                     int64_t ld_weight, float *logits, int64_t T, int64_t H, int64_t V,
+                     void *stream) {
   int st = check_shapes(T, H, V, ld_hidden, ld_weight);
   if (st != RLK_OK) return st;
   if (V > MAX_STORE_COLS) return RLK_ERR_UNSUPPORTED;
@@ -476,14 +494,20 @@ int rlk_logits(const void *hidden, int64_t ld_hidden, const void *weight,
   return hip_status(rlk::launch_gemm_logits(g, compute_units(), static_cast<hipStream_t>(stream)));
 }
 
+int rlk_logits(const void *hidden, int64_t ld_hidden, const void *weight,
+               int64_t ld_weight, float *logits, int64_t T, int64_t H,
+               int64_t V, void *stream) {
+  return rlk_debug_logits(hidden, ld_hidden, weight, ld_weight, logits, T, H, V, stream);
+}
+
 int rlk_compare(const float *a, const float *b, int64_t n, double *stats,
                 void *stream) {
   if (n < 0) return RLK_ERR_INVALID_SHAPE;
-  if (n > MAX_ROWS) return RLK_ERR_UNSUPPORTED;
+  if (n > MAX_COMPARE) return RLK_ERR_UNSUPPORTED;
   if (!stats || (n > 0 && (!a || !b))) return RLK_ERR_NULL_POINTER;
   if (!aligned(stats, 8) || !aligned(a, 4) || !aligned(b, 4))
     return RLK_ERR_MISALIGNED;
-  return hip_status(rlk::launch_compare(a, b, (int)n, stats,
+  return hip_status(rlk::launch_compare(a, b, n, stats,
                                         static_cast<hipStream_t>(stream)));
 }
 

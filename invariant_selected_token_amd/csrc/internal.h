@@ -8,11 +8,10 @@
 namespace rlk {
 
 // Workgroup tile of the logit GEMM: TILE_V vocabulary rows x TILE_T token
-// rows, the full hidden dimension per workgroup.  Each wave covers 128 x 128
-// of it (128 vocabulary x 64 or 32 token rows in the lower tiles of batches
-// of at most 128 or 64 rows); STAT_V = 128 is the width of the vocabulary tiles whose (max, sum of
-// exponentials) statistics are merged, so it is part of the numerical
-// contract.
+// rows, the full hidden dimension per workgroup, the same for every batch
+// size.  Each wave covers 128 x 128 of it; STAT_V = 128 is the width of the
+// vocabulary tiles whose (max, sum of exponentials) statistics are merged, so
+// it is part of the numerical contract.
 constexpr int TILE_V = 256;
 constexpr int STAT_V = 128;
 constexpr int TILE_T = 256;
@@ -66,7 +65,7 @@ struct GemmArgs {
   int V;
   int js_base;  // global index of this weight slice's first statistics tile
   int y_base;   // global vocabulary index of this weight slice's first row
-  int nMT;   // token tiles, ceil(T / TILE_T) (the launcher recounts it for lower tiles)
+  int nMT;   // token tiles, ceil(T / TILE_T)
   int nVT;   // workgroup vocabulary tiles, ceil(V / TILE_V)
   int nST;   // statistics tiles, ceil(V / STAT_V)
 };
@@ -107,7 +106,7 @@ hipError_t launch_topk(const float *logits, int64_t ld, const float *lse, const 
                        int32_t *out_id, hipStream_t s);
 // x[0 .. n) = 0.0f
 hipError_t launch_zero(float *x, int64_t n, hipStream_t s);
-hipError_t launch_compare(const float *a, const float *b, int n,
+hipError_t launch_compare(const float *a, const float *b, int64_t n,
                           double *stats, hipStream_t s);
 
 }  // namespace rlk

@@ -37,11 +37,14 @@
 //
 // Why rows are batch invariant: every output z[t][v] is produced by the same
 // chain of MFMA instructions over k in increasing order whatever tile or tile
-// position row t lands in; rows beyond T and vocabulary rows beyond V are read
-// as zeros by the buffer unit's range check and never mix into other rows; the
-// epilogue's reduction tree for a row depends only on the tile geometry; the
-// merge's fold depends only on ceil(V / STAT_V).  No split-K, no atomics, no
-// shape-dependent kernel choice.
+// position row t lands in; one 256 x 256 tile serves every batch size, and
+// rows past T only change which loads are issued (their accumulators are
+// never written); vocabulary rows beyond V read as zeros through the buffer
+// unit's range check; the epilogue's reduction tree for a row depends only on
+// the tile geometry; the merge's fold depends only on ceil(V / STAT_V).  No
+// split-K.  The one atomic operation, a workgroup claiming its next tile from
+// a counter, only decides which workgroup computes a tile, never what it
+// computes.
 #include <hip/hip_runtime.h>
 #include <float.h>
 #include <math.h>
@@ -131,25 +134,25 @@ __device__ __forceinline__ void tile_of_logical(int L, int nMT, int nVT, int &m,
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 // The logit GEMM with its epilogue, for a sequence of workgroup tiles of 256
-// vocabulary x 64 NJ token rows.  4 waves; wave w covers vocabulary half
-// wv = w & 1 and token half wt = w >> 1 as 4 x NJ MFMA blocks of 32 x 32.
-// NJ = 4 is the full tile; the lower tiles (NJ = 2, 1) serve batches of at
-// most 128 and 64 rows, whose full tiles would be mostly padding.  They give
-// every logit, statistic and target capture the same operations in the same
-// order: a logit's accumulator advances through the same K steps, and a
-// token row's 128 vocabulary values of a statistics tile sit in the same
-// (block, register, lane) positions, whatever NJ and the row's block j.
-// Only the number of token blocks per wave changes.
+// vocabulary x 256 token rows -- one tile shape for every batch size.  4
+// waves; wave w covers vocabulary half wv = w & 1 and token half wt = w >> 1
+// as 4 x 4 MFMA blocks of 32 x 32.  Every tile runs the same instructions:
+// rows past T (in the last token tile of a batch whose size is not a
+// multiple of 256, e.g. every decode batch) read as zeros through the buffer
+// unit's range check, and no epilogue writes their results.  (Skipping their
+// loads and MFMAs needs either a branch per load or MFMA, which measured 2.5 %
+// slower on full tiles, or copies of the K loop specialised on the number of
+// live rows, which push the option and backward epilogues into scratch
+// spills and amount to a batch-size-dependent code path.)
 //
 // PERSIST: the workgroup walks tiles L = blockIdx.x, + gridDim.x, ... and
 // issues the next tile's first K-block loads before the current tile's
 // epilogue, so that their latency hides under the epilogue.  The order of
 // tiles only changes the schedule; every tile's arithmetic is the same.
-template <bool STATS, bool PERSIST, int EX, int NJ>
+template <bool STATS, bool PERSIST, int EX>
 __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
-  static_assert(NJ == 4 || NJ == 2 || NJ == 1, "token blocks of 32 rows per wave");
-  static_assert(NJ == 4 || EX != 3, "lower tiles: not the logit-gradient epilogue");
-  constexpr int TT = 64 * NJ;   // token rows of a tile
+  constexpr int NJ = 4;         // token blocks of 32 rows per wave
+  constexpr int TT = 64 * NJ;   // token rows of a tile (TILE_T)
   constexpr int WT = 32 * NJ;   // token rows of a wave
   constexpr int NQ = 4 * NJ;    // MFMAs per wave and K step
   constexpr int NR = 4 + NJ;    // fragment reads per wave and K step
@@ -219,6 +222,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     return make_rsrc(a.hidden + (size_t)t0 * a.ldh,
                      (uint32_t)(min(TT, a.T - t0) * a.ldh * 2));
   };
+  // token rows of tile m that lie below T
+  auto rows_of = [&](int m) { return min(TT, a.T - m * TT); };
   uint32_t gofs[2][8];  // [operand][load]; set by set_offsets below
   typedef __attribute__((address_space(3))) void lds_void;
   // Load q (0..15) of K block kb into `stage`: the weight's row group q for
@@ -236,9 +241,6 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   auto gload = [&](__amdgpu_buffer_rsrc_t r_w, __amdgpu_buffer_rsrc_t r_h, int stage,
                    int kb, int q) {
     const int op = q < 8 ? 0 : 1, i = q & 7;
-    // a lower tile's hidden rows fill only its first 2 NJ row groups (the
-    // rest would fall outside the tile's resource and read nothing)
-    if (NJ < 4 && op == 1 && i >= 2 * NJ) return;
     lds_char *dst = lds_wave + stage * (2 * STAGE_BYTES) + op * STAGE_BYTES + (4 * i) * 1024;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? r_h : r_w, (lds_void *)dst, 16, gofs[op][i],
                                              (uint32_t)kb * (TILE_K * 2), 0, 0);
@@ -268,9 +270,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   };
   // A tile's first K block into stage 0, and its next blocks into L2.
   // Targets of a tile: one 4-byte direct-to-LDS load per wave (64 rows
-  // each) into the tile's half of a double buffer; rows past T read 0.
-  const __amdgpu_buffer_rsrc_t r_tgt =
-      make_rsrc(a.targets, STATS ? (uint32_t)(a.T * 4) : 0u);
+  // each) into the tile's half of a double buffer, through a resource based
+  // at the tile's first row and sized to its rows below T (rows past T read
+  // 0; every offset stays below 1 KiB whatever T).
   // The lane offset is formed afresh (an asm the compiler cannot merge with
   // the set-up's): kept across the K loop it would be spilled, and its
   // reload would wait for every load in flight.
@@ -278,9 +280,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     if (STATS) {
       int l;
       asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+      const __amdgpu_buffer_rsrc_t r_tgt =
+          make_rsrc(a.targets + (size_t)tile_m * TT, (uint32_t)(rows_of(tile_m) * 4));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           r_tgt, (lds_void *)(smem + TGT_OFS + par * (TILE_T * 4) + wave * 256), 4,
-          (uint32_t)(l * 4), (uint32_t)((tile_m * TT + 64 * wave) * 4), 0, 0);
+          (uint32_t)(l * 4), (uint32_t)(64 * wave * 4), 0, 0);
     }
   };
   auto issue_first = [&](__amdgpu_buffer_rsrc_t r_w, __amdgpu_buffer_rsrc_t r_h,
@@ -335,6 +339,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     else fa[buf][w - NJ] = *(const bf16x8 *)(smem + ra[st][ks] + (w - NJ) * 4096);
   };
   f32x16 acc[4][NJ];
+  // MFMA q of a K step: A block i = q / NJ, B (token) block j = q % NJ
   auto mfma = [&](int buf, int q) {
     const int i = q / NJ, j = q % NJ;
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j],
@@ -343,20 +348,17 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
 
   // One K block of the main loop.  Each accumulator advances in increasing k
   // (16 per MFMA); the fixed instruction order below only decides what
-  // overlaps with what.  In the full tile (NQ = 16 MFMAs per K step) each of
-  // the first eight MFMAs of step ks is followed by one read of step ks + 1's
-  // fragments, and every second MFMA of steps 0 and 1 (the odd ones) by one
-  // direct-to-LDS load of the next K block, so the sixteen loads are issued
-  // early but never in bursts (a burst stalls the wave's in-order issue, and
-  // with it the next MFMA, until the texture path takes the load); step 2
-  // issues the L2 prefetch.  Half-way through step 3 the wave waits for its
-  // loads and the workgroup meets at the barrier (the next block has landed;
-  // this block is no longer read), then the next block's first fragments are
-  // read under the last eight MFMAs.  The lower tiles keep this order with
-  // fewer MFMAs: the sixteen loads go one (NQ = 8) or two (NQ = 4) behind
-  // each MFMA of steps 0 and 1, and reads that find no MFMA left follow the
-  // step's last one.  The tile's last block (MORE false) has no next block of
-  // its own: its load slots carry the next tile's first block into the other
+  // overlaps with what.  Each of the first eight of the 16 MFMAs of step ks
+  // is followed by one read of step ks + 1's fragments, and every second
+  // MFMA of steps 0 and 1 (the odd ones) by one direct-to-LDS load of the
+  // next K block, so the sixteen loads are issued early but never in bursts
+  // (a burst stalls the wave's in-order issue, and with it the next MFMA,
+  // until the texture path takes the load); step 2 issues the L2 prefetch.
+  // Half-way through step 3 the wave waits for its loads and the workgroup
+  // meets at the barrier (the next block has landed; this block is no longer
+  // read), then the next block's first fragments are read under the last
+  // eight MFMAs.  The tile's last block (MORE false) has no next block of its
+  // own: its load slots carry the next tile's first block into the other
   // stage (r_w, r_h, p_w then name the next tile), which is free once the
   // barrier of the block before has passed.  p_w and kp name the weight
   // block the L2 prefetch fetches: kb + 1 + PREFETCH_AHEAD of this tile, and
@@ -376,23 +378,14 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
         mfma(cur, q);
         if (q < NR) fread(cur ^ 1, st, ks + 1, q);
         if (ks < 2) {
-          // eight loads per step: behind every (NQ / 8)-th MFMA, or 8 / NQ
-          // behind each when the step has fewer than eight
-          if constexpr (NQ >= 8) {
-            if (q % (NQ / 8) == NQ / 8 - 1) gload(r_w, r_h, st ^ 1, kl, 8 * ks + q / (NQ / 8));
-          } else {
-#pragma unroll
-            for (int u = 0; u < 8 / NQ; ++u) gload(r_w, r_h, st ^ 1, kl, 8 * ks + q * (8 / NQ) + u);
-          }
+          // eight loads per step, one behind every odd MFMA
+          if (q & 1) gload(r_w, r_h, st ^ 1, kl, 8 * ks + (q >> 1));
         } else if (ks == 2 && q == NQ / 2) {
           prefetch(p_w, kp);
           if constexpr (!STATS) prefetch_h(p_h, kp);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      // reads that did not fit behind the step's MFMAs (NJ == 1)
-#pragma unroll
-      for (int w = NQ; w < NR; ++w) fread(cur ^ 1, st, ks + 1, w);
     }
 #pragma unroll
     for (int q = 0; q < NQ / 2; ++q) {
@@ -908,10 +901,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
 // Launch shapes: the statistics kernel is persistent (one workgroup per
 // compute unit walking the tiles); the logits-stage kernel uses one
 // workgroup per tile.
-template <bool STATS, bool PERSIST, int EX, int NJ = 4>
+template <bool STATS, bool PERSIST, int EX>
 __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[CLAIM_OFS + 16];
-  gemm_body<STATS, PERSIST, EX, NJ>(a, smem);
+  gemm_body<STATS, PERSIST, EX>(a, smem);
 }
 
 // Per row t: M = max_j m_j (exact in any order), then
@@ -1020,7 +1013,7 @@ __global__ __launch_bounds__(MERGE_GROUPS * MERGE_ROWS) void merge_kernel(
 }
 
 __global__ __launch_bounds__(COMPARE_THREADS) void compare_kernel(
-    const float *__restrict__ x, const float *__restrict__ y, int n,
+    const float *__restrict__ x, const float *__restrict__ y, int64_t n,
     double *__restrict__ stats) {
   __shared__ double sd[4][COMPARE_THREADS];
   __shared__ long long sc[2][COMPARE_THREADS];
@@ -1030,11 +1023,12 @@ __global__ __launch_bounds__(COMPARE_THREADS) void compare_kernel(
   // Elements tid, tid + COMPARE_THREADS, ... in increasing order; the loads
   // of COMPARE_UNROLL of them are issued together (one memory round trip per
   // 4096 elements instead of one per element a thread visits).
-  for (int base = 0; base < n; base += COMPARE_THREADS * COMPARE_UNROLL) {
+  // element indices in 64 bits: n may come within a stride of 2^31
+  for (int64_t base = 0; base < n; base += COMPARE_THREADS * COMPARE_UNROLL) {
     float xa[COMPARE_UNROLL], ya[COMPARE_UNROLL];
 #pragma unroll
     for (int u = 0; u < COMPARE_UNROLL; ++u) {
-      const int i = base + u * COMPARE_THREADS + tid;
+      const int64_t i = base + u * COMPARE_THREADS + tid;
       xa[u] = i < n ? x[i] : 0.0f;
       ya[u] = i < n ? y[i] : 0.0f;
     }
@@ -1109,78 +1103,39 @@ int balanced_grid(int tiles, int workers) {
   return grid;
 }
 
-template <int EX, int NJ>
+template <int EX>
 void launch_stats_kernel(const GemmArgs &a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_kernel<true, true, EX, NJ>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
+  hipLaunchKernelGGL((gemm_kernel<true, true, EX>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
 }
 
-template <int NJ>
-void launch_stats_nj(const GemmArgs &a, int grid, hipStream_t s) {
-  if (a.ex == 2) launch_stats_kernel<2, NJ>(a, grid, s);
-  else if (a.ex == 1) launch_stats_kernel<1, NJ>(a, grid, s);
-  else launch_stats_kernel<0, NJ>(a, grid, s);
-}
-
-// A batch of at most 64 (128) rows runs in tiles of 64 (128) token rows: a
-// quarter (half) of the MFMAs of full tiles, whose other rows would all be
-// padding.  Tiles of 128 rows keep one workgroup per compute unit (measured
-// 2-3 % faster than the balanced rounds, 200 workgroups for 594 tiles);
-// tiles of 64 rows, bound by the weight stream, are faster on the balanced
-// grid (8 % at one row) -- as are full tiles.  Sets a.nMT for the tile
-// height; returns NJ, the tile height over 64.
-int pick_tiles(GemmArgs &a, int workers, int &grid) {
-  int nj = 4;
-  if (a.ex != 3 && a.T <= 64) nj = 1;
-  else if (a.ex != 3 && a.T <= 128) nj = 2;
-  a.nMT = ceil_div(a.T, 64 * nj);   // in int64: T may be 2^31 - 1
-  const int tiles = a.nMT * a.nVT;
-  grid = balanced_grid(tiles, workers);
-  if (nj == 2) grid = min(workers >= 8 ? workers - workers % 8 : 8, tiles);
-  return nj;
-}
-
-template <int EX, int NJ>
+template <int EX>
 void launch_store_kernel(const GemmArgs &a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_kernel<false, true, EX, NJ>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
+  hipLaunchKernelGGL((gemm_kernel<false, true, EX>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
 }
 
 }  // namespace
 
-hipError_t launch_gemm_stats(const GemmArgs &args, int workers, hipStream_t s) {
-  GemmArgs a = args;
-  int grid;
-  const int nj = pick_tiles(a, workers, grid);   // (the logit gradient: full tiles)
+// Every batch size runs the one 256 x 256 tile; only the number of
+// workgroups of the persistent walk (the schedule) depends on the tile count.
+hipError_t launch_gemm_stats(const GemmArgs &a, int workers, hipStream_t s) {
+  const int grid = balanced_grid(a.nMT * a.nVT, workers);
   // the claim counters start at zero (a kernel, not a memset: capturable)
   if (a.queue) hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(64), 0, s, (float *)a.queue, 8);
-  if (a.ex == 3)
-    hipLaunchKernelGGL((gemm_kernel<true, true, 3>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
-  else if (nj == 1)
-    launch_stats_nj<1>(a, grid, s);
-  else if (nj == 2)
-    launch_stats_nj<2>(a, grid, s);
-  else
-    launch_stats_nj<4>(a, grid, s);
+  if (a.ex == 3) launch_stats_kernel<3>(a, grid, s);
+  else if (a.ex == 2) launch_stats_kernel<2>(a, grid, s);
+  else if (a.ex == 1) launch_stats_kernel<1>(a, grid, s);
+  else launch_stats_kernel<0>(a, grid, s);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_logits(const GemmArgs &args, int workers, hipStream_t s) {
-  GemmArgs a = args;
-  int grid;
-  const int nj = pick_tiles(a, workers, grid);
+hipError_t launch_gemm_logits(const GemmArgs &a, int workers, hipStream_t s) {
+  const int grid = balanced_grid(a.nMT * a.nVT, workers);
   if (a.queue) hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(64), 0, s, (float *)a.queue, 8);
   // whole rows through LDS when V is a multiple of 4 and the output 16-byte
   // aligned; otherwise one column per store (the same values)
   const bool vec = (a.V & 3) == 0 && ((uintptr_t)a.logits & 15) == 0;
-  if (nj == 1) {
-    if (vec) launch_store_kernel<0, 1>(a, grid, s);
-    else launch_store_kernel<1, 1>(a, grid, s);
-  } else if (nj == 2) {
-    if (vec) launch_store_kernel<0, 2>(a, grid, s);
-    else launch_store_kernel<1, 2>(a, grid, s);
-  } else {
-    if (vec) launch_store_kernel<0, 4>(a, grid, s);
-    else launch_store_kernel<1, 4>(a, grid, s);
-  }
+  if (vec) launch_store_kernel<0>(a, grid, s);
+  else launch_store_kernel<1>(a, grid, s);
   return hipGetLastError();
 }
 
@@ -1583,7 +1538,9 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(
         if (count([&](int u) { return key[u] >= trial; }) >= kk) K = trial;
       }
       const int need = kk - count([&](int u) { return key[u] > K; });
-      for (int bit = 24; bit >= 0; --bit) {
+      // ids are below V: bits 30 - clz(V - 1) .. 0 cover them (V <= 2^31 - 1)
+      const int top = V > 1 ? 31 - __clz(V - 1) : 0;
+      for (int bit = top; bit >= 0; --bit) {
         const int trial = x | (1 << bit);
         if (count([&](int u) { return key[u] == K && cid[u] < trial; }) < need) x = trial;
       }
@@ -1665,7 +1622,7 @@ hipError_t launch_zero(float *x, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_compare(const float *a, const float *b, int n, double *stats,
+hipError_t launch_compare(const float *a, const float *b, int64_t n, double *stats,
                           hipStream_t s) {
   hipLaunchKernelGGL(compare_kernel, dim3(1), dim3(COMPARE_THREADS), 0, s, a, b,
                      n, stats);

@@ -230,3 +230,19 @@ def long_rollout_case(seed: int = BASE_SEED + 5, T: int = 16384) -> Case:
     c.meta["seq_len"] = 512
     c.meta["n_seqs"] = T // 512
     return c
+
+
+def upstream_grad(T: int, seed: int) -> np.ndarray:
+    """An upstream gradient dL/dlogp for the backward: N(0, 1) as float32."""
+    return np.random.Generator(np.random.PCG64(seed)).normal(size=T).astype(np.float32)
+
+
+def fingerprint(case: Case, targets=None) -> str:
+    """A short digest of a workload's bytes (hidden, weight, targets), so that
+    values stored for it can tell when the generator has changed."""
+    import hashlib
+    h = hashlib.sha256()
+    for a in (case.hidden, case.weight,
+              case.targets if targets is None else np.asarray(targets, np.int32)):
+        h.update(np.ascontiguousarray(a).tobytes())
+    return h.hexdigest()[:24]

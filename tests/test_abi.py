@@ -36,8 +36,55 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, name), name
 
 
+SURVEY_CALLS = {
+    # the boundary's calls and their C signatures, as the hot path's scope
+    # table lists them (argument names may differ; types and order may not)
+    "rlk_abi_version": "int rlk_abi_version(void)",
+    "rlk_status_string": "const char *rlk_status_string(int status)",
+    "rlk_selected_logp_workspace_bytes":
+        "size_t rlk_selected_logp_workspace_bytes(int64_t T, int64_t H, int64_t V)",
+    "rlk_selected_logp":
+        "int rlk_selected_logp(const void *hidden, int64_t ld_hidden, const void *weight, "
+        "int64_t ld_weight, const int32_t *targets, float *logp, float *lse, int64_t T, "
+        "int64_t H, int64_t V, void *workspace, size_t workspace_bytes, void *stream)",
+    "rlk_debug_logits":
+        "int rlk_debug_logits(const void *hidden, int64_t ld_hidden, const void *weight, "
+        "int64_t ld_weight, float *logits, int64_t T, int64_t H, int64_t V, void *stream)",
+}
+
+
+def _types_of(decl):
+    """(return type, [argument types]) of a C declaration, names dropped."""
+    decl = re.sub(r"\s+", " ", decl).strip().rstrip(";")
+    head, args = decl.split("(", 1)
+    args = args.rsplit(")", 1)[0]
+    ret = head.rsplit(" ", 1)[0].replace(" *", "*").strip()
+    if head.rstrip().split(" ")[-1].startswith("*"):
+        ret += "*"
+    out = []
+    for a in ([] if args.strip() == "void" else args.split(",")):
+        a = a.strip()
+        m = re.match(r"(.*?)(\w+)$", a)
+        out.append(re.sub(r"\s+", "", m.group(1)))
+    return ret.replace(" ", ""), out
+
+
+def test_boundary_calls_of_the_scope_table():
+    """Every call of the boundary the hot-path scope table lists is declared
+    with its signature and exported."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    text = "\n".join(l for l in text.splitlines() if not l.lstrip().startswith("#"))
+    decls = [re.sub(r"\s+", " ", d).strip() for d in re.split(r"[;{}]", text)]
+    L = rlk.lib()
+    for name, want in SURVEY_CALLS.items():
+        found = [d for d in decls if re.search(r"\b" + name + r"\s*\(", d)]
+        assert len(found) == 1, (name, found)
+        assert _types_of(found[0]) == _types_of(want), (name, found[0])
+        assert hasattr(L, name), name
+
+
 def test_constants():
-    assert rlk.rlk_abi_version() == 2
+    assert rlk.rlk_abi_version() == 3
     assert rlk.rlk_vocab_tile() == 128
     msgs = {rlk.rlk_status_string(s) for s in range(8)}
     assert len(msgs) == 8 and all(msgs)
@@ -45,8 +92,16 @@ def test_constants():
 
 
 def test_workspace_size():
-    ws = rlk.rlk_selected_logp_workspace_bytes
+    def ws(T, V, H=4096):
+        return rlk.rlk_selected_logp_workspace_bytes(T, H, V)
+
     assert ws(0, 151936) == 0 and ws(-1, 10) == 0 and ws(5, 0) == 0
+    assert ws(5, 10, H=0) == 0 and ws(5, 10, H=-64) == 0
+    # H does not change the size
+    assert ws(64, 4096, H=256) == ws(64, 4096, H=4096) == ws(64, 4096, H=64)
+    # the size limits: T and V up to 2^31 - 4096
+    assert ws(2 ** 31 - 4096, 1) > 0 and ws(2 ** 31 - 4095, 1) == 0
+    assert ws(1, 2 ** 31 - 4096) > 0 and ws(1, 2 ** 31 - 4095) == 0
 
     def expect(T, V):
         r = lambda x: (x + 255) // 256 * 256
@@ -64,7 +119,7 @@ def test_workspace_size():
 def _call(hidden=FAKE, ldh=256, weight=FAKE, ldw=256, targets=FAKE, logp=FAKE,
           lse=FAKE, T=4, H=256, V=1000, ws=WS_FAKE, ws_bytes=None, stream=None):
     if ws_bytes is None:
-        ws_bytes = max(rlk.rlk_selected_logp_workspace_bytes(T, V), 0)
+        ws_bytes = max(rlk.rlk_selected_logp_workspace_bytes(T, 256, V), 0)
     return rlk.lib().rlk_selected_logp(hidden, ldh, weight, ldw, targets, logp, lse,
                                        T, H, V, ws, ws_bytes, stream)
 
@@ -81,6 +136,11 @@ def _call(hidden=FAKE, ldh=256, weight=FAKE, ldw=256, targets=FAKE, logp=FAKE,
     (dict(ldh=(1 << 21) + 8), rlk.RLK_ERR_UNSUPPORTED),
     (dict(T=1 << 31), rlk.RLK_ERR_UNSUPPORTED),
     (dict(V=1 << 31), rlk.RLK_ERR_UNSUPPORTED),
+    # past the last row index every kernel forms in int
+    (dict(T=2 ** 31 - 4095, V=64), rlk.RLK_ERR_UNSUPPORTED),
+    (dict(T=1, V=2 ** 31 - 4095), rlk.RLK_ERR_UNSUPPORTED),
+    # the largest T is accepted (stops at the workspace check)
+    (dict(T=2 ** 31 - 4096, V=64, ws_bytes=100), rlk.RLK_ERR_WORKSPACE_TOO_SMALL),
     # 8388607 x 256 = 2^31 - 256 workgroup tiles: T and V are in range, but a
     # tile index plus a grid of workgroups would pass 2^31
     (dict(T=(2 ** 23 - 1) * 256, V=65536), rlk.RLK_ERR_UNSUPPORTED),
@@ -111,7 +171,7 @@ def test_selected_logp_empty_batch_is_a_no_op():
 
 
 def test_workspace_one_byte_short():
-    need = rlk.rlk_selected_logp_workspace_bytes(4, 1000)
+    need = rlk.rlk_selected_logp_workspace_bytes(4, 256, 1000)
     assert _call(ws_bytes=need - 1) == rlk.RLK_ERR_WORKSPACE_TOO_SMALL
 
 
@@ -125,17 +185,21 @@ def test_workspace_one_byte_short():
     (dict(V=(1 << 24) + 1), rlk.RLK_ERR_UNSUPPORTED),   # 32 output rows past 2^31 bytes
     (dict(V=(1 << 24) + 1, T=0), rlk.RLK_ERR_UNSUPPORTED),
 ])
-def test_logits_error_paths(kw, status):
+@pytest.mark.parametrize("name", ["rlk_debug_logits", "rlk_logits"])
+def test_logits_error_paths(kw, status, name):
     a = dict(hidden=FAKE, ldh=256, weight=FAKE, ldw=256, logits=FAKE, T=4, H=256,
              V=100, stream=None)
     a.update(kw)
-    assert rlk.lib().rlk_logits(a["hidden"], a["ldh"], a["weight"], a["ldw"],
-                                a["logits"], a["T"], a["H"], a["V"], a["stream"]) == status
+    fn = getattr(rlk.lib(), name)
+    assert fn(a["hidden"], a["ldh"], a["weight"], a["ldw"],
+              a["logits"], a["T"], a["H"], a["V"], a["stream"]) == status
 
 
 @pytest.mark.parametrize("a,b,n,stats,status", [
     (FAKE, FAKE, -1, FAKE, rlk.RLK_ERR_INVALID_SHAPE),
     (FAKE, FAKE, 1 << 31, FAKE, rlk.RLK_ERR_UNSUPPORTED),
+    # the largest n is accepted (indices are 64-bit on the device)
+    (FAKE, FAKE, (1 << 31) - 1, None, rlk.RLK_ERR_NULL_POINTER),
     (FAKE, FAKE, 10, None, rlk.RLK_ERR_NULL_POINTER),
     (None, FAKE, 10, FAKE, rlk.RLK_ERR_NULL_POINTER),
     (FAKE, FAKE, 10, FAKE + 4, rlk.RLK_ERR_MISALIGNED),
@@ -164,7 +228,7 @@ def test_status_error_type_carries_the_message():
 def _stats(hidden=FAKE, ldh=256, weight=FAKE, ldw=256, targets=FAKE, T=4, H=256,
            V=1000, ws=WS_FAKE, ws_bytes=None):
     if ws_bytes is None:
-        ws_bytes = rlk.rlk_selected_logp_workspace_bytes(T, V)
+        ws_bytes = rlk.rlk_selected_logp_workspace_bytes(T, 256, V)
     return rlk.lib().rlk_vocab_stats(hidden, ldh, weight, ldw, targets, T, H, V, ws,
                                      ws_bytes, None)
 
@@ -186,7 +250,7 @@ def test_vocab_stats_error_paths(kw, status):
 
 def _merge(targets=FAKE, logp=FAKE, lse=FAKE, T=4, V=1000, ws=WS_FAKE, ws_bytes=None):
     if ws_bytes is None:
-        ws_bytes = rlk.rlk_selected_logp_workspace_bytes(T, V)
+        ws_bytes = rlk.rlk_selected_logp_workspace_bytes(T, 256, V)
     return rlk.lib().rlk_vocab_merge(targets, logp, lse, T, V, ws, ws_bytes, None)
 
 
@@ -210,7 +274,7 @@ def test_vocab_merge_error_paths(kw, status):
 def _shard(hidden=FAKE, ldh=256, weight=FAKE, ldw=256, targets=FAKE, T=4, H=256,
            V=1000, v_begin=256, v_count=256, ws=WS_FAKE, ws_bytes=None):
     if ws_bytes is None:
-        ws_bytes = rlk.rlk_selected_logp_workspace_bytes(T, V)
+        ws_bytes = rlk.rlk_selected_logp_workspace_bytes(T, 256, V)
     return rlk.lib().rlk_vocab_stats_shard(hidden, ldh, weight, ldw, targets, T, H, V,
                                            v_begin, v_count, ws, ws_bytes, None)
 
@@ -235,8 +299,8 @@ def test_vocab_stats_shard_error_paths(kw, status):
     kw = dict(kw)
     if isinstance(kw.get("ws_bytes"), tuple):     # sized in the test, not at collection
         _, t, v = kw["ws_bytes"]
-        kw["ws_bytes"] = rlk.rlk_selected_logp_workspace_bytes(t, v)
-        assert kw["ws_bytes"] < rlk.rlk_selected_logp_workspace_bytes(kw["T"], 1000)
+        kw["ws_bytes"] = rlk.rlk_selected_logp_workspace_bytes(t, 256, v)
+        assert kw["ws_bytes"] < rlk.rlk_selected_logp_workspace_bytes(kw["T"], 256, 1000)
     assert _shard(**kw) == status
     assert rlk.rlk_last_hip_error() == 0
 
@@ -266,7 +330,8 @@ def test_one_hip_runtime_in_the_process():
 # ------------------------------------------------------ contract options --
 
 def test_workspace_size_ex():
-    ws, wx = rlk.rlk_selected_logp_workspace_bytes, rlk.rlk_workspace_bytes_ex
+    wx = rlk.rlk_workspace_bytes_ex
+    ws = lambda T, V: rlk.rlk_selected_logp_workspace_bytes(T, 4096, V)
     r = lambda x: (x + 255) // 256 * 256
     for T, V in [(1, 1), (64, 4096), (4096, 151936), (257, 129)]:
         assert wx(T, V, 0) == ws(T, V)
@@ -506,3 +571,25 @@ def test_binding_type_errors_before_any_device_work():
         rlk.rlk_selected_logp_ex(h, w, y, entropy=True)  # fp32 hidden, option path
     with pytest.raises(ValueError):
         rlk.rlk_selected_logp(w[:2], w, y)             # host tensors
+
+
+def test_workspace_layout():
+    """The documented carve-up: part_m at 0, part_s and xt after whole
+    256-byte-rounded regions, part_u after xt; the entropy workspace is the
+    plain one plus one statistics region."""
+    r = lambda x: (x + 255) // 256 * 256
+    for T, V in [(1, 1), (64, 4096), (4096, 151936), (257, 129)]:
+        st = r(((V + 127) // 128) * T * 4)
+        lay = rlk.rlk_workspace_layout(T, V)
+        assert lay == {"part_m": 0, "part_s": st, "xt": 2 * st, "part_u": 2 * st + r(4 * T)}
+        assert rlk.rlk_workspace_layout(T, V, rlk.RLK_ENTROPY) == lay
+        # the counters after the regions are the library's
+        assert rlk.rlk_workspace_bytes_ex(T, V, 0) >= lay["part_u"]
+        assert rlk.rlk_workspace_bytes_ex(T, V, rlk.RLK_ENTROPY) >= lay["part_u"] + st
+    L = rlk.lib()
+    assert L.rlk_workspace_layout(0, 10, 0, None, None, None, None) == rlk.RLK_ERR_INVALID_SHAPE
+    assert L.rlk_workspace_layout(4, 0, 0, None, None, None, None) == rlk.RLK_ERR_INVALID_SHAPE
+    assert L.rlk_workspace_layout(2 ** 31, 10, 0, None, None, None, None) == \
+        rlk.RLK_ERR_UNSUPPORTED
+    assert L.rlk_workspace_layout(4, 10, 8, None, None, None, None) == rlk.RLK_ERR_INVALID_VALUE
+    assert L.rlk_workspace_layout(4, 10, 0, None, None, None, None) == rlk.RLK_OK

@@ -53,8 +53,8 @@ RAGGED = [
     (1, 64, 1), (1, 64, 5), (3, 128, 127), (7, 64, 128), (255, 256, 129),
     (256, 256, 256), (257, 64, 257), (300, 192, 1000), (513, 128, 4133),
     (70, 4096, 3000), (600, 64, 640),
-    # the edges of the lower tiles: 64 rows (the last 64-row tile), 65 and
-    # 128 (128-row tiles), with odd K-block counts
+    # partly filled tiles whose last live row group is partly (65) or wholly
+    # (64, 128) filled, with odd K-block counts
     (64, 128, 769), (65, 64, 1031), (128, 320, 2000),
 ]
 
