@@ -92,6 +92,9 @@ extern "C" {
 #define RLK_ERR_INVALID_VALUE       7  /* an option out of range: inverse
                                           temperature not finite and > 0, or
                                           unknown flag bits */
+#define RLK_ERR_SCRATCH_LIMIT       8  /* T and V need more workspace than
+                                          rlk_selected_logp_noalloc's static
+                                          scratch */
 
 /* Option flags of the _ex entry points. */
 #define RLK_LOGITS_BF16 1  /* round every (scaled) logit to bfloat16 */
@@ -383,6 +386,26 @@ int rlk_topk_logp(const float *logits, int64_t ld_logits, const float *lse,
  * No workspace; asynchronous on `stream`. */
 int rlk_compare(const float *a, const float *b, int64_t n, double *stats,
                 void *stream);
+
+/* Allocation-free variant of rlk_selected_logp, for callers that cannot
+ * allocate device memory or pass a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  The same kernels
+ * and the same bits as rlk_selected_logp; its workspace is a static device
+ * array of the library, RLK_NOALLOC_SCRATCH_BYTES (64 MiB), of which each GPU
+ * the library runs on holds one copy until the process ends.  It calls no
+ * allocating routine.
+ *   Arguments and errors as for rlk_selected_logp (no workspace), plus
+ *   RLK_ERR_SCRATCH_LIMIT when rlk_selected_logp_workspace_bytes(T, H, V)
+ *   exceeds RLK_NOALLOC_SCRATCH_BYTES (checked before any HIP call; at
+ *   V = 151936 up to about 7000 rows fit).
+ *   Every call on a GPU shares that GPU's array: calls that may overlap on one
+ *   GPU (several streams or threads) race and must be serialised by the
+ *   caller; each call resets the parts it needs (the tile-claim counters by a
+ *   kernel), so a call does not depend on what an earlier one left there. */
+#define RLK_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int rlk_selected_logp_noalloc(const void *hidden, int64_t ld_hidden, const void *weight,
+                              int64_t ld_weight, const int32_t *targets, float *logp,
+                              float *lse, int64_t T, int64_t H, int64_t V, void *stream);
 
 #ifdef __cplusplus
 }

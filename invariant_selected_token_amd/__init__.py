@@ -26,6 +26,8 @@ RLK_ERR_MISALIGNED = 4
 RLK_ERR_WORKSPACE_TOO_SMALL = 5
 RLK_ERR_HIP = 6
 RLK_ERR_INVALID_VALUE = 7
+RLK_ERR_SCRATCH_LIMIT = 8
+RLK_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 
 RLK_LOGITS_BF16 = 1
 RLK_ENTROPY = 2
@@ -38,7 +40,7 @@ EXPORTED = (
     "rlk_workspace_bytes_ex",
     "rlk_selected_logp_ex", "rlk_vocab_stats_ex", "rlk_vocab_merge_ex",
     "rlk_selected_logp_backward_workspace_bytes", "rlk_selected_logp_backward",
-    "rlk_logp_grad_logits", "rlk_rmsnorm", "rlk_topk_logp",
+    "rlk_logp_grad_logits", "rlk_rmsnorm", "rlk_topk_logp", "rlk_selected_logp_noalloc",
 )
 
 _lib = None
@@ -82,6 +84,8 @@ def lib() -> ctypes.CDLL:
     L.rlk_selected_logp.argtypes = [vp, i64, vp, i64, vp, vp, vp, i64, i64, i64,
                                     vp, sz, vp]
     L.rlk_selected_logp.restype = c_int
+    L.rlk_selected_logp_noalloc.argtypes = [vp, i64, vp, i64, vp, vp, vp, i64, i64, i64, vp]
+    L.rlk_selected_logp_noalloc.restype = c_int
     L.rlk_vocab_stats.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, vp, sz, vp]
     L.rlk_vocab_stats.restype = c_int
     L.rlk_vocab_stats_shard.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, i64, i64,
@@ -260,6 +264,18 @@ def rlk_selected_logp(hidden, weight, targets, logp=None, lse=None,
     _call("rlk_selected_logp", lib().rlk_selected_logp(
         hp, ldh, wp, ldw, targets.data_ptr(), logp.data_ptr(), lse.data_ptr(),
         T, H, V, ws.data_ptr(), ws_bytes, _stream_ptr(stream, dev)))
+    return logp, lse
+
+
+def rlk_selected_logp_noalloc(hidden, weight, targets, logp, lse, V=None, stream=None):
+    """rlk_selected_logp with the library's static device scratch as its
+    workspace: the call itself allocates nothing (the caller passes the
+    outputs).  Calls that may overlap on one GPU must be serialised."""
+    dev, hp, ldh, wp, ldw, T, H, V = _prepare(hidden, weight, targets, V)
+    logp, lse = _outputs(dev, T, logp, lse, stream)
+    _call("rlk_selected_logp_noalloc", lib().rlk_selected_logp_noalloc(
+        hp, ldh, wp, ldw, targets.data_ptr(), logp.data_ptr(), lse.data_ptr(),
+        T, H, V, _stream_ptr(stream, dev)))
     return logp, lse
 
 

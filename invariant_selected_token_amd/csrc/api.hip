@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "internal.h"
 #include "rlk.h"
 
@@ -196,6 +198,9 @@ const char *rlk_status_string(int status) {
     case RLK_ERR_HIP: return "HIP launch error (see rlk_last_hip_error)";
     case RLK_ERR_INVALID_VALUE:
       return "invalid option (inverse temperature not finite and > 0, or unknown flag bits)";
+    case RLK_ERR_SCRATCH_LIMIT:
+      return "T and V need more workspace than the allocation-free entry point's static "
+             "scratch (RLK_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -509,6 +514,68 @@ int rlk_compare(const float *a, const float *b, int64_t n, double *stats,
     return RLK_ERR_MISALIGNED;
   return hip_status(rlk::launch_compare(a, b, n, stats,
                                         static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------ allocation-free variant --
+//
+// rlk_selected_logp_noalloc: rlk_selected_logp with its workspace in a
+// file-scope device array instead of a caller's buffer.  Each GPU the
+// library runs on holds its own copy of the array (RLK_NOALLOC_SCRATCH_BYTES)
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not a device address: the device address is looked up once per device,
+// with that device current, and only that address is handed to kernels.
+
+}  // extern "C"
+
+namespace {
+
+__device__ __attribute__((aligned(256))) unsigned char scratch[RLK_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[MAX_DEVICES];   // device address of `scratch` per device
+
+// The device address of the current device's copy of `scratch`.
+int scratch_of_current_device(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= MAX_DEVICES) return RLK_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (!p) return RLK_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return RLK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rlk_selected_logp_noalloc(const void *hidden, int64_t ld_hidden, const void *weight,
+                              int64_t ld_weight, const int32_t *targets, float *logp,
+                              float *lse, int64_t T, int64_t H, int64_t V, void *stream) {
+  // every check of rlk_selected_logp, before any HIP call
+  int st = check_shapes(T, H, V, ld_hidden, ld_weight);
+  if (st != RLK_OK) return st;
+  if (T == 0) return RLK_OK;
+  if (ws_bytes_for(T, V, 0) > RLK_NOALLOC_SCRATCH_BYTES) return RLK_ERR_SCRATCH_LIMIT;
+  st = check_operands(hidden, ld_hidden, weight, ld_weight);
+  if (st != RLK_OK) return st;
+  if (!targets || !logp || !lse) return RLK_ERR_NULL_POINTER;
+  if (!aligned(targets, 4) || !aligned(logp, 4) || !aligned(lse, 4)) return RLK_ERR_MISALIGNED;
+  void *ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != RLK_OK) return st;
+  // the same kernels as rlk_selected_logp; the tile-claim counters in the
+  // scratch are reset by a kernel at the start of every call
+  return rlk_selected_logp(hidden, ld_hidden, weight, ld_weight, targets, logp, lse, T, H, V,
+                           ws, RLK_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

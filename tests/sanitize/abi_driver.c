@@ -60,6 +60,10 @@ int main(void) {
     EXPECT(rlk_selected_logp(F, H, F, H, Y, O, O, T, H, V, F, 100, NULL),
            RLK_ERR_WORKSPACE_TOO_SMALL);
     EXPECT(rlk_selected_logp(NULL, H, NULL, H, NULL, NULL, NULL, 0, H, V, NULL, 0, NULL), RLK_OK);
+    EXPECT(rlk_selected_logp_noalloc(F, H, F, H, Y, O, O, 8000, H, 151936, NULL),
+           RLK_ERR_SCRATCH_LIMIT);
+    EXPECT(rlk_selected_logp_noalloc(F, H, F, H, NULL, O, O, T, H, V, NULL), RLK_ERR_NULL_POINTER);
+    EXPECT(rlk_selected_logp_noalloc(F, 100, F, H, Y, O, O, T, H, V, NULL), RLK_ERR_INVALID_SHAPE);
 
     /* the stages, slices and options */
     EXPECT(rlk_vocab_stats(F, H, F, H, NULL, T, H, V, F, big, NULL), RLK_ERR_NULL_POINTER);

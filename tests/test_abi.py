@@ -86,8 +86,8 @@ def test_boundary_calls_of_the_scope_table():
 def test_constants():
     assert rlk.rlk_abi_version() == 3
     assert rlk.rlk_vocab_tile() == 128
-    msgs = {rlk.rlk_status_string(s) for s in range(8)}
-    assert len(msgs) == 8 and all(msgs)
+    msgs = {rlk.rlk_status_string(s) for s in range(9)}
+    assert len(msgs) == 9 and all(msgs)
     assert rlk.rlk_status_string(99) == "unknown status"
 
 
