@@ -112,8 +112,8 @@ def cpu_baseline(case, seconds: float) -> dict:
 
 def sample_sclk(torch, fn, seconds: float = 3.0):
     """Shader clock (MHz, mean over the XCDs' GFX clocks, median over the
-    samples) read with amd-smi while `fn` keeps the GPU busy; None when the
-    tool is missing or prints no clock."""
+    samples) and socket power (W) read with amd-smi while `fn` keeps the GPU
+    busy; None when the tool is missing or prints no clock."""
     tool = shutil.which("amd-smi")
     if tool is None:
         return None
@@ -122,13 +122,14 @@ def sample_sclk(torch, fn, seconds: float = 3.0):
     def poll():
         while not stop.is_set():
             try:
-                r = subprocess.run([tool, "metric", "-g", "0", "-c"], capture_output=True,
+                r = subprocess.run([tool, "metric", "-g", "0", "-c", "-p"], capture_output=True,
                                    text=True, timeout=10)
             except (OSError, subprocess.SubprocessError):
                 return
             mhz = [int(x) for x in re.findall(r"GFX_\d+:\s*CLK:\s*(\d+)\s*MHz", r.stdout)]
+            pw = re.findall(r"SOCKET_POWER:\s*([\d.]+)\s*W", r.stdout)
             if mhz:
-                samples.append(sum(mhz) / len(mhz))
+                samples.append((sum(mhz) / len(mhz), float(pw[0]) if pw else None))
 
     for _ in range(5):
         fn()
@@ -146,8 +147,12 @@ def sample_sclk(torch, fn, seconds: float = 3.0):
     use = samples[1:] if len(samples) > 2 else samples
     if not use:
         return None
-    return {"median_MHz": statistics.median(use), "min_MHz": min(use), "max_MHz": max(use),
-            "samples": len(use), "source": "amd-smi metric -c, GFX clocks of the XCDs"}
+    mhz = [u[0] for u in use]
+    watts = [u[1] for u in use if u[1] is not None]
+    return {"median_MHz": statistics.median(mhz), "min_MHz": min(mhz), "max_MHz": max(mhz),
+            "socket_power_W_median": statistics.median(watts) if watts else None,
+            "samples": len(use), "source": "amd-smi metric -c -p: GFX clocks of the XCDs "
+                                            "and socket power"}
 
 
 VARIANTS = ("options", "slices", "backward", "rmsnorm", "topk20", "long_rollout", "decode")
