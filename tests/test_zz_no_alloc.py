@@ -103,3 +103,46 @@ def test_noalloc_matches_the_workspace_entry_point():
         assert np.abs(got - ref_lp).max() <= 1e-3
         assert np.abs(lse_n.cpu().numpy()[rows].astype(np.float64) - ref_lse).max() <= 1e-3
         del ws
+
+
+@pytest.mark.gpu
+def test_noalloc_replays_in_a_hip_graph():
+    """The caller it is for: a captured graph.  The capture holds only kernel
+    launches (the scratch's counters are cleared by a kernel); every replay,
+    with an eager call on other rows in between that overwrites the scratch,
+    gives the bits of the workspace entry point."""
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dev = torch.device("cuda:0")
+    c = synth.prefill_case(T=2048)
+    to_dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(
+        torch.bfloat16)
+    h_all, w = to_dev(c.hidden), to_dev(c.weight)
+    y_all = torch.from_numpy(c.targets).to(dev)
+    h, y = h_all[:1024].contiguous(), y_all[:1024].contiguous()
+    h2, y2 = h_all[1024:].contiguous(), y_all[1024:].contiguous()
+    ref_lp, ref_lse = rlk.rlk_selected_logp(h, w, y)
+    torch.cuda.synchronize()
+    lp = torch.empty(1024, dtype=torch.float32, device=dev)
+    lse = torch.empty_like(lp)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):        # warm-up on the capture stream (looks up the scratch)
+        rlk.rlk_selected_logp_noalloc(h, w, y, lp, lse, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        rlk.rlk_selected_logp_noalloc(h, w, y, lp, lse, stream=s)
+    lp2 = torch.empty(1024, dtype=torch.float32, device=dev)
+    lse2 = torch.empty_like(lp2)
+    for rep in range(4):
+        lp.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(lp.view(torch.int32), ref_lp.view(torch.int32)), rep
+        assert torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32)), rep
+        rlk.rlk_selected_logp_noalloc(h2, w, y2, lp2, lse2)     # eager, other rows
+        torch.cuda.synchronize()
