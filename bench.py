@@ -40,7 +40,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+# MI355X's published dense bf16 MFMA peak (2.5 PFLOP/s; 256 CU x 4096 FLOP/clk x 2.4 GHz
+# = 2516.6 TFLOP/s before rounding)
+PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 KERNEL_SRC = os.path.join(ROOT, "invariant_selected_token_amd", "csrc", "kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_stats_prefill_T4096_traffic.md")

@@ -132,3 +132,31 @@ def test_topk_boundary_inside_a_tie_group(dev, k):
     rlp, rids = orc.topk_logp(hb, wb, k)
     assert np.array_equal(ti.cpu().numpy(), rids)
     np.testing.assert_allclose(tl.cpu().numpy(), rlp, rtol=0, atol=1e-5)
+
+
+def test_topk_tie_cut_at_ids_above_2_pow_25(dev):
+    """The tie cut at the k-th value bisects over the token ids; ids of a
+    vocabulary past 2^25 need its 26th bit.  Logits given directly (the
+    store kernel stops at V = 2^24): row t of V = 2^25 + 4096 entries holds 30
+    tied maxima 1.0 at ids 2^25 .. 2^25 + 29 and, in every other 128-wide
+    tile j, the value -1 - j 1e-6; so the candidate tiles are that tile and
+    tiles 0 .. 18 (20 tiles: the bisection path at k = 20) and the answer is
+    ids 2^25 .. 2^25 + 19, each with the value 1.0 - lse."""
+    T, V, k = 2, 2 ** 25 + 4096, 20
+    nst = V // 128
+    tile = torch.arange(nst, device=dev, dtype=torch.float32)
+    z = (-1.0 - tile * 1e-6).repeat_interleave(128).unsqueeze(0).repeat(T, 1).contiguous()
+    a = 2 ** 25
+    z[:, a:a + 128] = -5.0
+    z[:, a:a + 30] = 1.0
+    lse = torch.logsumexp(z, dim=1).contiguous()
+    part_m = z.view(T, nst, 128).amax(dim=2).t().contiguous()     # [nST][T], tile-major
+    ws = torch.zeros((nst * T + 64,), dtype=torch.float32, device=dev)
+    ws[:nst * T] = part_m.view(-1)
+    tl, ti = rlk.rlk_topk_logp(z, lse, ws, k)
+    torch.cuda.synchronize()
+    want_ids = torch.arange(a, a + k, dtype=torch.int32, device=dev).unsqueeze(0).repeat(T, 1)
+    assert torch.equal(ti, want_ids), ti[:, :k].tolist()
+    want_v = (1.0 - lse).unsqueeze(1).expand(T, k)
+    assert torch.equal(tl.view(torch.int32), want_v.contiguous().view(torch.int32))
+    del z
