@@ -398,7 +398,8 @@ def time_variants(rlk, torch, np, hidden, weight, targets, T, H, V, steps, flops
         del ws
 
     if "backward" in only:
-        # transposes, dz pass, grad_hidden and grad_weight GEMMs
+        # hidden-row transpose, dz pass, grad_hidden (weight read K-major) and
+        # grad_weight GEMMs
         g = torch.linspace(-1.0, 1.0, T, dtype=torch.float32, device=dev)
         _, lse = rlk.rlk_selected_logp(hidden, weight, targets)
         gh = torch.empty((T, H), dtype=torch.float32, device=dev)

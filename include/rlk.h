@@ -290,9 +290,10 @@ int rlk_vocab_merge_ex(const int32_t *targets, float *logp, float *lse, float *e
  *                   grad_weight is set to zero.
  *   inv_temperature finite, > 0 (RLK_ERR_INVALID_VALUE otherwise).
  *   workspace       rlk_selected_logp_backward_workspace_bytes(T, H, V)
- *                   bytes, 16-byte aligned: bf16 dz [T][Vp], dz^T [V][Tp],
- *                   w^T [H][Vp] and h^T [H][Tp] with Vp, Tp = V, T rounded up
- *                   to 64 (zero padded); about 3 * 2 V (T + H) bytes.
+ *                   bytes, 16-byte aligned: bf16 dz [T][Vp], dz^T [V][Tp] and
+ *                   h^T [H][Tp] with Vp, Tp = V, T rounded up to 64 (zero
+ *                   padded); about 2 * 2 V T + 2 H T bytes.  (grad_hidden
+ *                   reads the weight as stored, with no copy.)
  * Extra limit: V and T rounded up to 64 must not exceed 2^21
  * (RLK_ERR_UNSUPPORTED). */
 size_t rlk_selected_logp_backward_workspace_bytes(int64_t T, int64_t H, int64_t V);

@@ -113,8 +113,12 @@ int hip_status(hipError_t e) {
 // Backward: workspace layout, limits and launch helpers.
 int64_t pad64(int64_t x) { return (x + 63) / 64 * 64; }
 
+// dz [T][pad64(V)] (grad_hidden's operand), dz^T [V][pad64(T)] and
+// hidden^T [H][pad64(T)] (grad_weight's), then the GEMMs' tile-claim
+// counters (reset before each launch).  The weight needs no copy: grad_hidden
+// reads it as stored (K-major).
 struct BwdLayout {
-  size_t dz, dzt, wt, ht, queue, total;  // byte offsets and size
+  size_t dz, dzt, ht, queue, total;  // byte offsets and size
 };
 
 BwdLayout bwd_layout(int64_t T, int64_t H, int64_t V, bool want_h, bool want_w) {
@@ -124,18 +128,16 @@ BwdLayout bwd_layout(int64_t T, int64_t H, int64_t V, bool want_h, bool want_w) 
   if (want_h) o += round_up((size_t)T * pad64(V) * 2);
   L.dzt = o;
   if (want_w) o += round_up((size_t)V * pad64(T) * 2);
-  L.wt = o;
-  if (want_h) o += round_up((size_t)H * pad64(V) * 2);
   L.ht = o;
   if (want_w) o += round_up((size_t)H * pad64(T) * 2);
-  L.queue = o;   // tile-claim counters of the GEMMs, reset before each launch
+  L.queue = o;
   o += QUEUE_BYTES;
   L.total = o;
   return L;
 }
 
-// The backward's own size limits: V and T become GEMM depths (row strides of
-// the transposed copies), so both must fit the stride limit.
+// The backward's own size limits: pad64(V) and pad64(T) are the row strides
+// of dz and of the transposed copies, so both must fit the stride limit.
 int check_backward(int64_t T, int64_t H, int64_t V, int64_t ldh, int64_t ldw,
                    float inv_tau) {
   int st = check_shapes(T, H, V, ldh, ldw);
@@ -158,11 +160,15 @@ rlk::GemmArgs dz_args(const void *hidden, int64_t ldh, const void *weight, int64
   return g;
 }
 
-// out [B rows][A rows] fp32 = A . B^T over depth K (both operands K-contiguous).
+// out [B rows][A rows] fp32 = A . B^T over depth K: B is [Brows][K]; A is
+// [Arows][K], or with a_kr > 0 K-major, [a_kr][Arows] (rows a_kr .. K-1 of
+// the depth read as zeros; Arows a multiple of 8).
 int plain_gemm(const uint16_t *A, int64_t lda, int64_t Arows, const uint16_t *B,
                int64_t ldb, int64_t Brows, int64_t K, float *out, int *queue,
-               hipStream_t s) {
+               hipStream_t s, int64_t a_kr = 0) {
   rlk::GemmArgs g = gemm_args(B, ldb, A, lda, Brows, K, Arows);
+  g.kmw = a_kr > 0;
+  g.kr = (int)a_kr;
   g.logits = out;
   g.queue = queue;
   // Both backward products stream an operand from HBM in the hidden role
@@ -413,16 +419,14 @@ int rlk_selected_logp_backward(const void *hidden, int64_t ld_hidden, const void
   const int64_t Vp = pad64(V), Tp = pad64(T);
   uint16_t *dz = reinterpret_cast<uint16_t *>(ws + L.dz);
   uint16_t *dzt = reinterpret_cast<uint16_t *>(ws + L.dzt);
-  uint16_t *wt = reinterpret_cast<uint16_t *>(ws + L.wt);
   uint16_t *ht = reinterpret_cast<uint16_t *>(ws + L.ht);
   const uint16_t *h16 = static_cast<const uint16_t *>(hidden);
   const uint16_t *w16 = static_cast<const uint16_t *>(weight);
-  // Transposed operands: the gradient GEMMs contract over V (grad_hidden)
-  // and over T (grad_weight), so those become the contiguous dimension.
-  if (want_h) {
-    st = hip_status(rlk::launch_transpose(w16, ld_weight, (int)V, (int)H, wt, Vp, s));
-    if (st != RLK_OK) return st;
-  }
+  // grad_weight contracts over T: its operands are dz^T (written by the dz
+  // pass) and hidden^T, a copy with the tokens contiguous.  (Reading the
+  // token-major dz and hidden K-major instead measured slower: the
+  // transposing LDS reads deliver about 3/4 of ds_read_b128's bandwidth, and
+  // both operands would need them, 0.56 ms over this copy and dz^T's store.)
   if (want_w) {
     st = hip_status(rlk::launch_transpose(h16, ld_hidden, (int)T, (int)H, ht, Tp, s));
     if (st != RLK_OK) return st;
@@ -437,9 +441,11 @@ int rlk_selected_logp_backward(const void *hidden, int64_t ld_hidden, const void
   g.queue = queue;
   st = hip_status(rlk::launch_gemm_stats(g, compute_units(), s));
   if (st != RLK_OK) return st;
-  // grad_hidden [T][H] = dz [T][Vp] . wt [H][Vp]^T
+  // grad_hidden [T][H] = dz [T][Vp] . W [V][H], the weight read K-major as
+  // stored (its rows are the depth; rows V .. Vp-1 read as zeros): no
+  // transposed copy of the weight (a 2 x V x H byte round trip)
   if (want_h) {
-    st = plain_gemm(wt, Vp, H, dz, Vp, T, Vp, grad_hidden, queue, s);
+    st = plain_gemm(w16, ld_weight, H, dz, Vp, T, Vp, grad_hidden, queue, s, V);
     if (st != RLK_OK) return st;
   }
   // grad_weight [V][H] = dzt [V][Tp] . ht [H][Tp]^T

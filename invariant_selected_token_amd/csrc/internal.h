@@ -58,6 +58,12 @@ struct GemmArgs {
   int64_t ld_dzt;
   int Vp;
   int Tp;
+  // Plain GEMM: the weight-role operand stored K-major, [depth][V columns]
+  // with the depth along its rows (the product over the vocabulary reads
+  // the weight as it is stored); kr is its number of rows along the depth
+  // (rows kr .. H-1 of the depth read as zeros).  V must be a multiple of 8.
+  int kmw;
+  int kr;
   int64_t ldh;
   int64_t ldw;
   int T;

@@ -14,7 +14,11 @@
 //                       stage-by-stage comparison of section 五; also the two
 //                       gradient products of the backward).  EX 0 stores 16
 //                       bytes per lane, EX 1 one column per store, for rows
-//                       whose length or base is not 16-byte aligned.
+//                       whose length or base is not 16-byte aligned.  KMW
+//                       reads the weight-role operand K-major (stored with
+//                       the depth along its rows) through the transposing
+//                       LDS read: the product over the vocabulary takes the
+//                       weight as it is stored.
 //   merge_kernel        per row, folds the tile statistics in a fixed order
 //                       that depends only on the number of vocabulary tiles,
 //                       then lse = M + log(s) and logp = z_y - lse (and, with
@@ -133,6 +137,16 @@ __device__ __forceinline__ void tile_of_logical(int L, int nMT, int nVT, int &m,
 // 8 or 16 lanes per cycle.
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
+// ds_read_b64_tr_b16 through a restrict-qualified pointer: inlined, the
+// call then carries alias-scope information like the kernel's other LDS
+// reads, and the compiler does not make it wait for every direct-to-LDS load
+// in flight (without it, it waits with vmcnt(0) before each one).
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+__device__ __forceinline__ bf16x4 tr_read(const lds_bf16x4 *__restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(const_cast<lds_bf16x4 *>(p));
+}
+
 // The logit GEMM with its epilogue, for a sequence of workgroup tiles of 256
 // vocabulary x 256 token rows -- one tile shape for every batch size.  4
 // waves; wave w covers vocabulary half wv = w & 1 and token half wt = w >> 1
@@ -149,8 +163,9 @@ __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1
 // issues the next tile's first K-block loads before the current tile's
 // epilogue, so that their latency hides under the epilogue.  The order of
 // tiles only changes the schedule; every tile's arithmetic is the same.
-template <bool STATS, bool PERSIST, int EX>
+template <bool STATS, bool PERSIST, int EX, bool KMW>
 __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
+  static_assert(!(STATS && KMW), "the statistics pass reads K-contiguous operands");
   constexpr int NJ = 4;         // token blocks of 32 rows per wave
   constexpr int TT = 64 * NJ;   // token rows of a tile (TILE_T)
   constexpr int WT = 32 * NJ;   // token rows of a wave
@@ -212,15 +227,55 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   // (l & 7) ^ swz(row) = (l & 7) ^ (l >> 3) ^ (w & 1) of that row.  The K
   // offset of the block rides in the scalar offset; rows past T or V fall
   // outside the tile's resource and read 0.
-  auto rsrc_w = [&](int n) {
+  //
+  // A K-major weight-role operand ([depth][columns]; KMW) is handled by tile:
+  // the tile's first column at depth row 0, the operand's rows along the
+  // depth (kr), and the bytes from the tile's first column to the end of the
+  // operand's last row.  Each K block reads through a resource of its own,
+  // based at the block's first row (so no offset reaches 2^32 whatever the
+  // operand's size) and ending at the operand's last element: depth rows
+  // past kr read zeros, and so do the last row's columns past its end (V
+  // columns, a multiple of 8, so that no 16-byte chunk is cut by the range
+  // check, which drops each 4-byte piece on its own).  Columns past the end
+  // in other rows read the next row's values; they only reach outputs of
+  // columns past the end, which are never stored.
+  struct KMajor {
+    const uint16_t *p;
+    int krows;
+    uint32_t cols;
+  };
+  using HW = std::conditional_t<KMW, KMajor, __amdgpu_buffer_rsrc_t>;
+  auto rsrc_w = [&](int n) -> HW {
     const int v0 = n * TILE_V;
-    return make_rsrc(a.weight + (size_t)v0 * a.ldw,
-                     (uint32_t)(min(TILE_V, a.V - v0) * a.ldw * 2));
+    if constexpr (KMW) {
+      return KMajor{a.weight + v0, a.kr, (uint32_t)(a.V - v0) * 2u};
+    } else {
+      return make_rsrc(a.weight + (size_t)v0 * a.ldw,
+                       (uint32_t)(min(TILE_V, a.V - v0) * a.ldw * 2));
+    }
   };
   auto rsrc_h = [&](int m) {
     const int t0 = m * TT;
     return make_rsrc(a.hidden + (size_t)t0 * a.ldh,
                      (uint32_t)(min(TT, a.T - t0) * a.ldh * 2));
+  };
+  const __amdgpu_buffer_rsrc_t zero = make_rsrc(a.weight, 0u);
+  auto zero_w = [&]() -> HW {
+    if constexpr (KMW) return KMajor{a.weight, 0, 0u};
+    else return zero;
+  };
+  // The resource and scalar offset through which K block kb of a tile's
+  // weight-role operand is read.
+  auto src_w = [&](HW h, int kb, uint32_t &so) -> __amdgpu_buffer_rsrc_t {
+    if constexpr (KMW) {
+      const int rows = min(TILE_K, h.krows - kb * TILE_K);
+      so = 0;
+      return make_rsrc(h.p + (size_t)kb * TILE_K * a.ldw,
+                       rows > 0 ? (uint32_t)(rows - 1) * (uint32_t)a.ldw * 2u + h.cols : 0u);
+    } else {
+      so = (uint32_t)kb * (TILE_K * 2);
+      return h;
+    }
   };
   // token rows of tile m that lie below T
   auto rows_of = [&](int m) { return min(TT, a.T - m * TT); };
@@ -238,12 +293,14 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   // registers across the loop.
   typedef __attribute__((address_space(3))) char lds_char;
   lds_char *lds_wave = (lds_char *)smem + wave * 1024;
-  auto gload = [&](__amdgpu_buffer_rsrc_t r_w, __amdgpu_buffer_rsrc_t r_h, int stage,
-                   int kb, int q) {
+  // (r_w, s_w): the weight-role resource and scalar offset of the K block
+  // being loaded (src_w); r_h the hidden-role tile's resource.
+  auto gload = [&](__amdgpu_buffer_rsrc_t r_w, uint32_t s_w, __amdgpu_buffer_rsrc_t r_h,
+                   int stage, int kb, int q) {
     const int op = q < 8 ? 0 : 1, i = q & 7;
     lds_char *dst = lds_wave + stage * (2 * STAGE_BYTES) + op * STAGE_BYTES + (4 * i) * 1024;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? r_h : r_w, (lds_void *)dst, 16, gofs[op][i],
-                                             (uint32_t)kb * (TILE_K * 2), 0, 0);
+                                             op ? (uint32_t)kb * (TILE_K * 2) : s_w, 0, 0);
   };
   // L2 prefetch of the weight's K block kb: one 4-byte load per 128-byte
   // line, lane l touching row 32 (l >> 3) + 8 w + (l & 7) -- the 64 rows
@@ -256,9 +313,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   // in the memory-side cache, where a prefetch costs the CU more in line
   // requests than it saves in latency (measured).
   uint32_t pofs_w, pofs_h;
-  auto prefetch = [&](__amdgpu_buffer_rsrc_t r, int kb) {
+  auto prefetch = [&](HW h, int kb) {
+    uint32_t so;
+    const __amdgpu_buffer_rsrc_t r = src_w(h, kb, so);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(smem + 4 * STAGE_BYTES), 4,
-                                             pofs_w, (uint32_t)kb * (TILE_K * 2), 0, 0);
+                                             pofs_w, so, 0, 0);
   };
   // The plain (store) GEMM also prefetches its hidden-role rows, the same
   // way, when pf_hidden is set (the backward's products, whose hidden-role
@@ -287,10 +346,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
           (uint32_t)(l * 4), (uint32_t)(64 * wave * 4), 0, 0);
     }
   };
-  auto issue_first = [&](__amdgpu_buffer_rsrc_t r_w, __amdgpu_buffer_rsrc_t r_h,
-                         __amdgpu_buffer_rsrc_t p_w, __amdgpu_buffer_rsrc_t p_h) {
+  auto issue_first = [&](HW r_w, __amdgpu_buffer_rsrc_t r_h, HW p_w,
+                         __amdgpu_buffer_rsrc_t p_h) {
+    uint32_t s_w;
+    const __amdgpu_buffer_rsrc_t b_w = src_w(r_w, 0, s_w);
 #pragma unroll
-    for (int q = 0; q < 16; ++q) gload(r_w, r_h, 0, 0, q);
+    for (int q = 0; q < 16; ++q) gload(b_w, s_w, r_h, 0, 0, q);
 #pragma unroll
     for (int kp = 1; kp <= PREFETCH_AHEAD; ++kp) {
       prefetch(p_w, kp);
@@ -301,7 +362,23 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   // Fragment reads: A (weight) rows wv*128 + 32 i + fr, B (hidden) rows
   // wt*128 + 32 j + fr, 16-byte chunk 2 ks + fk of the 64-wide K step.  Byte
   // addresses per (stage, ks); the block index i or j adds i * 4096.
+  //
+  // A K-major weight stage holds 64 depth rows k x 256 columns c (32 chunks
+  // of 8 columns) as 128 lines of 256 bytes: chunk c of row k sits in line
+  // 8 (k >> 2) + (c >> 2), 16-byte slot 2 (k & 3) + (c & 1) +
+  // 8 ((c >> 1) & 1).  The MFMA operand of a 32-column block and a 16-deep
+  // K step is two transposing reads (ds_read_b64_tr_b16: in each group of 16
+  // lanes, lane 4 r + s supplies columns 4 s .. 4 s + 3 of row r, and lane i
+  // receives column i of the 4 rows): lane l = 16 g + L reads row
+  // 16 ks + 8 (g >> 1) + 4 h + (L >> 2) (h = 0, 1), columns 16 (g & 1) +
+  // 4 (L & 3) of the block.  With this layout the 16 lanes of a group meet
+  // 32 distinct banks and any 32 lanes 64, and a read's address is a lane
+  // base plus 8192 ks + 2048 h + 256 block: immediate offsets only.  Load i
+  // of wave w fills lines 4 b .. 4 b + 3, b = 4 i + w (rows 4 (b >> 1) ..
+  // + 3, 256 contiguous bytes of each): lane l fetches row 4 (b >> 1) +
+  // ((l >> 1) & 3), chunk 16 (b & 1) + 4 (l >> 4) + 2 ((l >> 3) & 1) + (l & 1).
   uint32_t ra[2][4], rb[2][4];
+  uint32_t kma[2];   // K-major weight: lane base per stage
   // The per-lane offsets of the loads, the prefetch and the fragment reads,
   // formed at the start of every tile from a lane id the compiler cannot
   // merge with an earlier one: they are then dead during the epilogue
@@ -311,14 +388,24 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
     const int lrow = 8 * wave + (l >> 3);
     const int lchunk = (l & 7) ^ (l >> 3) ^ (wave & 1);
+    // K-major: row 8 i + kmrow, chunk kmchunk of the block (b = 4 i + wave)
+    const int kmrow = 4 * (wave >> 1) + ((l >> 1) & 3);
+    const int kmchunk = 16 * (wave & 1) + 4 * (l >> 4) + 2 * ((l >> 3) & 1) + (l & 1);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      gofs[0][i] = (uint32_t)((lrow + 32 * i) * a.ldw * 2 + lchunk * 16);
+      gofs[0][i] = KMW ? (uint32_t)((8 * i + kmrow) * a.ldw * 2 + kmchunk * 16)
+                       : (uint32_t)((lrow + 32 * i) * a.ldw * 2 + lchunk * 16);
       gofs[1][i] = (uint32_t)((lrow + 32 * i) * a.ldh * 2 + lchunk * 16);
     }
+    // L2 prefetch; K-major: row 16 w + (l >> 2), 128-byte line l & 3
     const int prow = 32 * (l >> 3) + 8 * wave + (l & 7);
-    pofs_w = (uint32_t)(prow * a.ldw * 2);
+    pofs_w = KMW ? (uint32_t)((16 * wave + (l >> 2)) * a.ldw * 2 + (l & 3) * 128)
+                 : (uint32_t)(prow * a.ldw * 2);
     pofs_h = (uint32_t)(prow * a.ldh * 2);
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+      kma[st] = st * (2 * STAGE_BYTES) + 4096 * (l >> 5) + 128 * ((l >> 4) & 1) + 8 * (l & 15) +
+                1024 * wv;
     const int lr = l & 31, lk = l >> 5;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
@@ -331,12 +418,23 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
       }
   };
   bf16x8 fa[2][4], fb[2][NJ];
+  // A fragment, block i of K step ks (K-major: two transposing reads)
+  auto reada = [&](int st, int ks, int i) -> bf16x8 {
+    if constexpr (KMW) {
+      lds_char *p = (lds_char *)smem + kma[st] + 8192 * ks + 256 * i;
+      const bf16x4 lo = tr_read((const lds_bf16x4 *)p);
+      const bf16x4 hi = tr_read((const lds_bf16x4 *)(p + 2048));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+      return *(const bf16x8 *)(smem + ra[st][ks] + i * 4096);
+    }
+  };
   // Read number w (0 .. NR-1) of the fragments of (stage, ks) into set `buf`,
   // in the order the MFMAs consume them: A0, B0 .. B(NJ-1), A1, A2, A3.
   auto fread = [&](int buf, int st, int ks, int w) {
-    if (w == 0) fa[buf][0] = *(const bf16x8 *)(smem + ra[st][ks]);
+    if (w == 0) fa[buf][0] = reada(st, ks, 0);
     else if (w <= NJ) fb[buf][w - 1] = *(const bf16x8 *)(smem + rb[st][ks] + (w - 1) * 4096);
-    else fa[buf][w - NJ] = *(const bf16x8 *)(smem + ra[st][ks] + (w - NJ) * 4096);
+    else fa[buf][w - NJ] = reada(st, ks, w - NJ);
   };
   f32x16 acc[4][NJ];
   // MFMA q of a K step: A block i = q / NJ, B (token) block j = q % NJ
@@ -363,12 +461,13 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   // barrier of the block before has passed.  p_w and kp name the weight
   // block the L2 prefetch fetches: kb + 1 + PREFETCH_AHEAD of this tile, and
   // in the last two blocks the next tile's blocks 0 and 1.
-  auto k_block = [&](int kb, auto stage, auto more, __amdgpu_buffer_rsrc_t r_w,
-                     __amdgpu_buffer_rsrc_t r_h, __amdgpu_buffer_rsrc_t p_w,
-                     __amdgpu_buffer_rsrc_t p_h, int kp) {
+  auto k_block = [&](int kb, auto stage, auto more, HW r_w, __amdgpu_buffer_rsrc_t r_h,
+                     HW p_w, __amdgpu_buffer_rsrc_t p_h, int kp) {
     constexpr int st = decltype(stage)::value;    // == kb & 1
     constexpr bool MORE = decltype(more)::value;  // not the last K block
     const int kl = MORE ? kb + 1 : 0;             // K block the loads fetch
+    uint32_t s_w;
+    const __amdgpu_buffer_rsrc_t b_w = src_w(r_w, kl, s_w);
     asm volatile("" : "+s"(lds_wave));
 #pragma unroll
     for (int ks = 0; ks < 3; ++ks) {
@@ -379,7 +478,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
         if (q < NR) fread(cur ^ 1, st, ks + 1, q);
         if (ks < 2) {
           // eight loads per step, one behind every odd MFMA
-          if (q & 1) gload(r_w, r_h, st ^ 1, kl, 8 * ks + (q >> 1));
+          if (q & 1) gload(b_w, s_w, r_h, st ^ 1, kl, 8 * ks + (q >> 1));
         } else if (ks == 2 && q == NQ / 2) {
           prefetch(p_w, kp);
           if constexpr (!STATS) prefetch_h(p_h, kp);
@@ -422,7 +521,6 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   // of -0 into +0, the same way for every row of a given H).
   const int nk = a.H / TILE_K;
   const int nk2 = nk + (nk & 1);
-  const __amdgpu_buffer_rsrc_t zero = make_rsrc(a.weight, 0u);
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
 
@@ -433,15 +531,16 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   // prefetch through the zero-size resource (no memory access).  A group
   // with fewer token tiles (fewer than 4 in all, or the last group) keeps
   // the whole prefetch in every workgroup.
-  auto pf_rsrc = [&](int mm, __amdgpu_buffer_rsrc_t r) {
+  auto pf_rsrc = [&](int mm, HW r) -> HW {
     const bool full_group = (mm & ~(GROUP_M - 1)) + GROUP_M <= a.nMT;
-    return (!full_group || wave == (mm & (GROUP_M - 1))) ? r : zero;
+    return (!full_group || wave == (mm & (GROUP_M - 1))) ? r : zero_w();
   };
   static_assert(GROUP_M == GEMM_THREADS / 64, "one prefetching wave per group member");
   int m, n;
   coords(L, m, n);
-  __amdgpu_buffer_rsrc_t rw = rsrc_w(n), rh = rsrc_h(m);
-  __amdgpu_buffer_rsrc_t pw = pf_rsrc(m, rw);
+  HW rw = rsrc_w(n);
+  __amdgpu_buffer_rsrc_t rh = rsrc_h(m);
+  HW pw = pf_rsrc(m, rw);
   auto pfh_rsrc = [&](__amdgpu_buffer_rsrc_t r) { return a.pf_hidden ? r : zero; };
   __amdgpu_buffer_rsrc_t ph = pfh_rsrc(rh);
   int parity = 0;
@@ -450,7 +549,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   issue_first(rw, rh, pw, ph);
 
   for (;;) {
-    const __amdgpu_buffer_rsrc_t rw_last = (nk & 1) ? zero : rw;
+    const HW rw_last = (nk & 1) ? zero_w() : rw;
     const __amdgpu_buffer_rsrc_t rh_last = (nk & 1) ? zero : rh;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -495,9 +594,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     const bool more_tiles = dyn ? Ln >= 0 : Ln < total;
     int mn = m, nn = n;
     if (more_tiles) coords(Ln, mn, nn);
-    const __amdgpu_buffer_rsrc_t rwn = more_tiles ? rsrc_w(nn) : zero;
+    const HW rwn = more_tiles ? rsrc_w(nn) : zero_w();
     const __amdgpu_buffer_rsrc_t rhn = more_tiles ? rsrc_h(mn) : zero;
-    const __amdgpu_buffer_rsrc_t pwn = pf_rsrc(mn, rwn);
+    const HW pwn = pf_rsrc(mn, rwn);
     const __amdgpu_buffer_rsrc_t phn = pfh_rsrc(rhn);
     k_block(nk2 - 2, S0{}, std::true_type{}, rw_last, rh_last, pwn, phn, 0);
     stage_targets(mn, parity ^ 1);   // after the last tile: its own, unused
@@ -901,10 +1000,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
 // Launch shapes: the statistics kernel is persistent (one workgroup per
 // compute unit walking the tiles); the logits-stage kernel uses one
 // workgroup per tile.
-template <bool STATS, bool PERSIST, int EX>
+template <bool STATS, bool PERSIST, int EX, bool KMW>
 __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(const GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[CLAIM_OFS + 16];
-  gemm_body<STATS, PERSIST, EX>(a, smem);
+  gemm_body<STATS, PERSIST, EX, KMW>(a, smem);
 }
 
 // Per row t: M = max_j m_j (exact in any order), then
@@ -1105,12 +1204,18 @@ int balanced_grid(int tiles, int workers) {
 
 template <int EX>
 void launch_stats_kernel(const GemmArgs &a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_kernel<true, true, EX>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
+  hipLaunchKernelGGL((gemm_kernel<true, true, EX, false>), dim3(grid), dim3(GEMM_THREADS), 0, s,
+                     a);
 }
 
 template <int EX>
 void launch_store_kernel(const GemmArgs &a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_kernel<false, true, EX>), dim3(grid), dim3(GEMM_THREADS), 0, s, a);
+  if (a.kmw)   // the weight-role operand K-major (the product over the vocabulary)
+    hipLaunchKernelGGL((gemm_kernel<false, true, EX, true>), dim3(grid), dim3(GEMM_THREADS), 0,
+                       s, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel<false, true, EX, false>), dim3(grid), dim3(GEMM_THREADS), 0,
+                       s, a);
 }
 
 }  // namespace
