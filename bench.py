@@ -448,8 +448,20 @@ def time_variants(rlk, torch, np, hidden, weight, targets, T, H, V, steps, flops
         lg = timed(store_logits)
         sel = timed(select)
         del z
+        # the same top-k without the stored logits: the candidate tiles'
+        # logits recomputed (bitwise the same entries)
+        ws_d = torch.empty(rlk.rlk_topk_logp_direct_workspace_bytes(T, V, 20),
+                           dtype=torch.uint8, device=dev)
+
+        def direct():
+            rlk.rlk_topk_logp_direct(hidden, weight, lse_t, ws_t, 20, workspace=ws_d,
+                                     topk_logp=tl, topk_ids=ti)
+
+        dr = timed(direct)
+        del ws_d
         out["topk20"] = {"logits_store_ms": lg, "select_ms": sel,
-                         "select_GB/s": 4.0 * T * V / (sel * 1e-3) / 1e9}
+                         "select_GB/s": 4.0 * T * V / (sel * 1e-3) / 1e9,
+                         "direct_ms": dr, "direct_vs_stored": (lg + sel) / dr}
 
     if "long_rollout" in only:
         # 16384 rows (32 responses x 512 tokens) through the same path

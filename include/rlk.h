@@ -76,8 +76,10 @@ extern "C" {
  * RMSNorm and top-k entry points; 3 gave rlk_selected_logp_workspace_bytes
  * the (T, H, V) signature, named the logits stage rlk_debug_logits (rlk_logits
  * stays as an alias), documented the workspace layout (rlk_workspace_layout)
- * and lowered the T and V limits to 2^31 - 4096. */
-#define RLK_ABI_VERSION 3
+ * and lowered the T and V limits to 2^31 - 4096; 4 added the top-k entry point
+ * without stored logits (rlk_topk_logp_direct) and shrank the backward's
+ * workspace (the weight is read as stored, with no transposed copy). */
+#define RLK_ABI_VERSION 4
 
 /* Status codes returned by every entry point that can fail. */
 #define RLK_OK                      0
@@ -367,6 +369,42 @@ int rlk_topk_logp(const float *logits, int64_t ld_logits, const float *lse,
                   const void *workspace, size_t workspace_bytes, int64_t T, int64_t V, int k,
                   float inv_temperature, int flags, float *topk_logp, int32_t *topk_ids,
                   void *stream);
+
+/* The same top-k log-probabilities without stored logits: the logits of the
+ * candidate tiles only are recomputed from hidden and weight, by the same
+ * MFMA instruction over the same operands in the same K order as the logit
+ * GEMM, so every output is bitwise that of rlk_topk_logp on the logits
+ * rlk_debug_logits stores.  A row's candidate tiles (m* its k-th largest tile
+ * maximum): those whose maximum exceeds m*, and the first of those whose
+ * maximum equals m* by tile index, k tiles in all; no other tile can hold a
+ * top-k entry under the order (value descending, id ascending).  A row whose
+ * m* is -inf (fewer than k tiles hold a value above -inf: rows of NaN or
+ * infinities) needs all ceil(V / 128) tiles: when that is more than k, the
+ * first max_degenerate_rows such rows (in row order) get room in the
+ * workspace, and any further one gets id -2 and NaN in all k places.
+ *   hidden, weight, T, H, V  as for rlk_selected_logp.
+ *   lse, stats_workspace  the lse and workspace of rlk_selected_logp(_ex) or
+ *                   rlk_vocab_stats(_ex) with the same T, V and options (the
+ *                   tile maxima); only read.
+ *   k, flags, inv_temperature, topk_logp, topk_ids  as for rlk_topk_logp.
+ *   max_degenerate_rows  >= 0 (RLK_ERR_INVALID_VALUE otherwise).
+ *   workspace       rlk_topk_logp_direct_workspace_bytes(T, V, k,
+ *                   max_degenerate_rows) bytes, 16-byte aligned: 512 bytes per
+ *                   (row, candidate tile) pair, T k + max_degenerate_rows *
+ *                   ceil(V / 128) pairs (the second term only when
+ *                   ceil(V / 128) > k), plus small tables.  The pair count
+ *                   must not exceed 2^30 (RLK_ERR_UNSUPPORTED; the size query
+ *                   returns 0).
+ * Six launches on the stream (candidates, plan, buckets, tile logits,
+ * selection, and a counter reset); no host synchronisation. */
+size_t rlk_topk_logp_direct_workspace_bytes(int64_t T, int64_t V, int k,
+                                            int64_t max_degenerate_rows);
+int rlk_topk_logp_direct(const void *hidden, int64_t ld_hidden, const void *weight,
+                         int64_t ld_weight, const float *lse, const void *stats_workspace,
+                         size_t stats_workspace_bytes, int64_t T, int64_t H, int64_t V, int k,
+                         float inv_temperature, int flags, int64_t max_degenerate_rows,
+                         void *workspace, size_t workspace_bytes, float *topk_logp,
+                         int32_t *topk_ids, void *stream);
 
 /* Consistency statistics of two fp32 arrays a (the side under test, e.g.
  * training) and b (the reference, e.g. rollout), as the pages measure them:

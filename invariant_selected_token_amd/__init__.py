@@ -41,6 +41,7 @@ EXPORTED = (
     "rlk_selected_logp_ex", "rlk_vocab_stats_ex", "rlk_vocab_merge_ex",
     "rlk_selected_logp_backward_workspace_bytes", "rlk_selected_logp_backward",
     "rlk_logp_grad_logits", "rlk_rmsnorm", "rlk_topk_logp", "rlk_selected_logp_noalloc",
+    "rlk_topk_logp_direct_workspace_bytes", "rlk_topk_logp_direct",
 )
 
 _lib = None
@@ -121,6 +122,11 @@ def lib() -> ctypes.CDLL:
     L.rlk_rmsnorm.restype = c_int
     L.rlk_topk_logp.argtypes = [vp, i64, vp, vp, sz, i64, i64, c_int, f32, c_int, vp, vp, vp]
     L.rlk_topk_logp.restype = c_int
+    L.rlk_topk_logp_direct_workspace_bytes.argtypes = [i64, i64, c_int, i64]
+    L.rlk_topk_logp_direct_workspace_bytes.restype = sz
+    L.rlk_topk_logp_direct.argtypes = [vp, i64, vp, i64, vp, vp, sz, i64, i64, i64, c_int, f32,
+                                       c_int, i64, vp, sz, vp, vp, vp]
+    L.rlk_topk_logp_direct.restype = c_int
     _lib = L
     return L
 
@@ -525,18 +531,61 @@ def rlk_topk_logp(logits, lse, workspace, k, inv_temperature=1.0, logits_bf16=Fa
     return topk_logp, topk_ids
 
 
+def rlk_topk_logp_direct_workspace_bytes(T, V, k, max_degenerate_rows=16) -> int:
+    return int(lib().rlk_topk_logp_direct_workspace_bytes(int(T), int(V), int(k),
+                                                          int(max_degenerate_rows)))
+
+
+def rlk_topk_logp_direct(hidden, weight, lse, stats_workspace, k, inv_temperature=1.0,
+                         logits_bf16=False, max_degenerate_rows=16, workspace=None,
+                         topk_logp=None, topk_ids=None, V=None, stream=None):
+    """(topk_logp [T, k] fp32, topk_ids [T, k] int32) without stored logits:
+    the candidate tiles' logits are recomputed from hidden and weight; the
+    statistics pass's lse and workspace (same options) select them."""
+    torch = _torch()
+    dev = hidden.device
+    hp, ldh = _bf16_operand("hidden", hidden, dev)
+    wp, ldw = _bf16_operand("weight", weight, dev)
+    T, H = hidden.shape
+    V = int(weight.shape[0] if V is None else V)
+    lp_ = _f32_vec("lse", lse, T, dev)
+    _check_device("stats_workspace", stats_workspace, dev)
+    need = rlk_topk_logp_direct_workspace_bytes(T, V, k, max_degenerate_rows) if T > 0 else 0
+    with _on(stream):
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        if topk_logp is None:
+            topk_logp = torch.empty((T, k), dtype=torch.float32, device=dev)
+        if topk_ids is None:
+            topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    _check_device("workspace", workspace, dev)
+    _call("rlk_topk_logp_direct", lib().rlk_topk_logp_direct(
+        hp, ldh, wp, ldw, lp_, stats_workspace.data_ptr(),
+        stats_workspace.numel() * stats_workspace.element_size(), T, H, V, int(k),
+        float(inv_temperature), RLK_LOGITS_BF16 if logits_bf16 else 0, int(max_degenerate_rows),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        topk_logp.data_ptr(), topk_ids.data_ptr(), _stream_ptr(stream, dev)))
+    return topk_logp, topk_ids
+
+
 def topk_logprobs(hidden, weight, targets, k, inv_temperature=1.0, logits_bf16=False,
-                  stream=None):
+                  stored_logits=False, stream=None):
     """Selected-token logp and lse plus the top-k log-probabilities of every
-    row: the statistics pass, the stored logits, then the selection."""
+    row: the statistics pass, then the selection over the candidate tiles'
+    recomputed logits (or, with stored_logits, over the logits stored whole:
+    the same bits, at the cost of a [T, V] fp32 array)."""
     dev, _, _, _, _, T, _, V = _prepare(hidden, weight, targets, None)
     flags = RLK_LOGITS_BF16 if logits_bf16 else 0
     ws = workspace_for(T, V, dev, flags, stream)
     logp, lse, _ = rlk_selected_logp_ex(hidden, weight, targets,
                                         inv_temperature=inv_temperature,
                                         logits_bf16=logits_bf16, workspace=ws, stream=stream)
-    z = rlk_logits(hidden, weight, stream=stream)
-    tl, ti = rlk_topk_logp(z, lse, ws, k, inv_temperature, logits_bf16, stream=stream)
+    if stored_logits:
+        z = rlk_logits(hidden, weight, stream=stream)
+        tl, ti = rlk_topk_logp(z, lse, ws, k, inv_temperature, logits_bf16, stream=stream)
+    else:
+        tl, ti = rlk_topk_logp_direct(hidden, weight, lse, ws, k, inv_temperature, logits_bf16,
+                                      V=V, stream=stream)
     return logp, lse, tl, ti
 
 

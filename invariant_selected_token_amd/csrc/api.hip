@@ -489,6 +489,127 @@ int rlk_topk_logp(const float *logits, int64_t ld_logits, const float *lse,
                                      topk_logp, topk_ids, static_cast<hipStream_t>(stream)));
 }
 
+// ------------------------------------------------ top-k from the operands
+}  // extern "C"
+
+namespace {
+
+struct TopkLayout {
+  size_t pair_z, bucket, cand_tile, cand_n, deg_rank, deg_row, tile_count, tile_off, tile_fill,
+      item_off, item_tile, totals, total;
+  int64_t P, items_max;
+};
+
+// The direct top-k's workspace: k pair slots per row (128 fp32 logits each),
+// then room for dcap rows with m* = -inf (all nST tiles each) when nST > k;
+// the pair buckets, the per-row candidate lists, and the plan's tile tables.
+TopkLayout topk_layout(int64_t T, int64_t V, int64_t k, int64_t dcap) {
+  TopkLayout L{};
+  const int64_t nST = ceil_div(V, rlk::STAT_V);
+  if (nST <= k) dcap = 0;   // such rows use their own k slots
+  L.P = T * k + dcap * nST;
+  L.items_max = (L.P + 127) / 128 + nST;   // work items of up to 128 pairs per tile
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += round_up(bytes);
+    return at;
+  };
+  L.pair_z = take((size_t)L.P * rlk::STAT_V * 4);
+  L.bucket = take((size_t)L.P * 4);
+  L.cand_tile = take((size_t)T * k * 4);
+  L.cand_n = take((size_t)T * 4);
+  L.deg_rank = take((size_t)T * 4);
+  L.deg_row = take((size_t)(dcap > 0 ? dcap : 1) * 4);
+  L.tile_count = take((size_t)nST * 4);
+  L.tile_off = take((size_t)nST * 4);
+  L.tile_fill = take((size_t)nST * 4);
+  L.item_off = take((size_t)(nST + 1) * 4);
+  L.item_tile = take((size_t)L.items_max * 4);
+  L.totals = take(16);
+  L.total = o;
+  return L;
+}
+
+// Pair and item indices are int on the device.
+constexpr int64_t MAX_PAIRS = int64_t(1) << 30;
+
+int check_topk_direct(int64_t T, int64_t V, int k, int64_t dcap) {
+  if (dcap < 0) return RLK_ERR_INVALID_VALUE;
+  if (k < 1 || k > 64 || k > V) return RLK_ERR_INVALID_VALUE;
+  const int64_t nST = ceil_div(V, rlk::STAT_V);
+  if (T * k + (nST > k ? dcap * nST : 0) > MAX_PAIRS) return RLK_ERR_UNSUPPORTED;
+  return RLK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t rlk_topk_logp_direct_workspace_bytes(int64_t T, int64_t V, int k,
+                                            int64_t max_degenerate_rows) {
+  if (T <= 0 || V <= 0 || T > MAX_ROWS || V > MAX_ROWS) return 0;
+  if (check_topk_direct(T, V, k, max_degenerate_rows) != RLK_OK) return 0;
+  return topk_layout(T, V, k, max_degenerate_rows).total;
+}
+
+int rlk_topk_logp_direct(const void *hidden, int64_t ld_hidden, const void *weight,
+                         int64_t ld_weight, const float *lse, const void *stats_workspace,
+                         size_t stats_workspace_bytes, int64_t T, int64_t H, int64_t V, int k,
+                         float inv_temperature, int flags, int64_t max_degenerate_rows,
+                         void *workspace, size_t workspace_bytes, float *topk_logp,
+                         int32_t *topk_ids, void *stream) {
+  int st = check_shapes(T, H, V, ld_hidden, ld_weight);
+  if (st != RLK_OK) return st;
+  if (check_options(inv_temperature, flags) != RLK_OK) return RLK_ERR_INVALID_VALUE;
+  st = check_topk_direct(T, V, k, max_degenerate_rows);
+  if (st != RLK_OK) return st;
+  if (T == 0) return RLK_OK;
+  st = check_operands(hidden, ld_hidden, weight, ld_weight);
+  if (st != RLK_OK) return st;
+  if (!lse || !stats_workspace || !workspace || !topk_logp || !topk_ids)
+    return RLK_ERR_NULL_POINTER;
+  if (!aligned(lse, 4) || !aligned(stats_workspace, 16) || !aligned(workspace, 16) ||
+      !aligned(topk_logp, 4) || !aligned(topk_ids, 4))
+    return RLK_ERR_MISALIGNED;
+  if (stats_workspace_bytes < stats_bytes(T, V)) return RLK_ERR_WORKSPACE_TOO_SMALL;
+  const TopkLayout L = topk_layout(T, V, k, max_degenerate_rows);
+  if (workspace_bytes < L.total) return RLK_ERR_WORKSPACE_TOO_SMALL;
+  char *ws = static_cast<char *>(workspace);
+  rlk::TopkDirectArgs a{};
+  a.hidden = static_cast<const uint16_t *>(hidden);
+  a.weight = static_cast<const uint16_t *>(weight);
+  a.ldh = ld_hidden;
+  a.ldw = ld_weight;
+  a.lse = lse;
+  a.part_m = static_cast<const float *>(stats_workspace);
+  a.out_lp = topk_logp;
+  a.out_id = topk_ids;
+  a.pair_z = reinterpret_cast<float *>(ws + L.pair_z);
+  a.bucket = reinterpret_cast<int *>(ws + L.bucket);
+  a.cand_tile = reinterpret_cast<int *>(ws + L.cand_tile);
+  a.cand_n = reinterpret_cast<int *>(ws + L.cand_n);
+  a.deg_rank = reinterpret_cast<int *>(ws + L.deg_rank);
+  a.deg_row = reinterpret_cast<int *>(ws + L.deg_row);
+  a.tile_count = reinterpret_cast<int *>(ws + L.tile_count);
+  a.tile_off = reinterpret_cast<int *>(ws + L.tile_off);
+  a.tile_fill = reinterpret_cast<int *>(ws + L.tile_fill);
+  a.item_off = reinterpret_cast<int *>(ws + L.item_off);
+  a.item_tile = reinterpret_cast<int *>(ws + L.item_tile);
+  a.totals = reinterpret_cast<int *>(ws + L.totals);
+  a.inv_tau = inv_temperature;
+  a.bf16 = (flags & RLK_LOGITS_BF16) ? 1 : 0;
+  a.T = (int)T;
+  a.H = (int)H;
+  a.V = (int)V;
+  a.nST = ceil_div(V, rlk::STAT_V);
+  a.k = k;
+  a.C = k;
+  a.dcap = (int)max_degenerate_rows;
+  a.items_max = (int)L.items_max;
+  return hip_status(rlk::launch_topk_direct(a, static_cast<hipStream_t>(stream)));
+}
+
 int rlk_debug_logits(const void *hidden, int64_t ld_hidden, const void *weight,
                      int64_t ld_weight, float *logits, int64_t T, int64_t H, int64_t V,
                      void *stream) {

@@ -110,6 +110,40 @@ hipError_t launch_rmsnorm(const uint16_t *x, int64_t ldx, const uint16_t *gamma,
 hipError_t launch_topk(const float *logits, int64_t ld, const float *lse, const float *part_m,
                        int T, int V, int k, float inv_tau, int bf16, float *out_lp,
                        int32_t *out_id, hipStream_t s);
+// Top-k log-probabilities without stored logits: the candidate tiles of
+// every row (from the statistics pass's tile maxima) are recomputed by the
+// logit GEMM's MFMA chain into pair_z, 128 raw logits per (row, tile) pair,
+// and the selection reads them there.  Buffers are carved from the caller's
+// workspace (see rlk_topk_logp_direct); C = k pair slots per row, then
+// dcap * nST pairs for rows whose k-th largest tile maximum is -inf when
+// nST > C.
+struct TopkDirectArgs {
+  const uint16_t *hidden;
+  const uint16_t *weight;
+  int64_t ldh;
+  int64_t ldw;
+  const float *lse;
+  const float *part_m;   // [nST][T], the statistics pass's tile maxima
+  float *out_lp;
+  int32_t *out_id;
+  float *pair_z;         // [P][128]
+  int *bucket;           // [P] pair ids grouped by tile
+  int *cand_tile;        // [T][C]
+  int *cand_n;           // [T]
+  int *deg_rank;         // [T]
+  int *deg_row;          // [max(dcap, 1)]
+  int *tile_count;       // [nST]
+  int *tile_off;         // [nST]
+  int *tile_fill;        // [nST]
+  int *item_off;         // [nST + 1]
+  int *item_tile;        // [items_max]
+  int *totals;           // [2]: work items, pairs
+  float inv_tau;
+  int bf16;
+  int T, H, V, nST, k, C, dcap;
+  int items_max;
+};
+hipError_t launch_topk_direct(const TopkDirectArgs &a, hipStream_t s);
 // x[0 .. n) = 0.0f
 hipError_t launch_zero(float *x, int64_t n, hipStream_t s);
 hipError_t launch_compare(const float *a, const float *b, int64_t n,

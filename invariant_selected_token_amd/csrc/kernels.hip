@@ -1519,42 +1519,31 @@ struct TopK {
   }
 };
 
-template <int KC>
-__global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(
-    const float *__restrict__ logits, int64_t ld, const float *__restrict__ lse,
-    const float *__restrict__ part_m, int T, int V, int nST, int k, float inv_tau, int bf16,
-    float *__restrict__ out_lp, int32_t *__restrict__ out_id) {
-  __shared__ Cand red[TOPK_THREADS / 64];
-  __shared__ Cand win;
-  __shared__ int list[TOPK_LIST];
-  __shared__ int nlist;
-  __shared__ int csum[TOPK_THREADS / 64];
-  __shared__ float win_v[64];
-  __shared__ int win_i[64];
-  const int t = blockIdx.x;
-  const int tid = threadIdx.x;
-  // a count summed over the workgroup (every thread gets the total)
-  auto block_sum = [&](int c) {
+// A count summed over the workgroup of TOPK_THREADS threads (every thread
+// gets the total); csum holds one slot per wave.
+__device__ __forceinline__ int block_sum(int c, int *csum) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
-    if ((tid & 63) == 0) csum[tid >> 6] = c;
-    __syncthreads();
-    int total = 0;
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+  if ((threadIdx.x & 63) == 0) csum[threadIdx.x >> 6] = c;
+  __syncthreads();
+  int total = 0;
 #pragma unroll
-    for (int q = 0; q < TOPK_THREADS / 64; ++q) total += csum[q];
-    __syncthreads();
-    return total;
-  };
-  const float *row = logits + (size_t)t * ld;
-  TopK<KC> sel;
+  for (int q = 0; q < TOPK_THREADS / 64; ++q) total += csum[q];
+  __syncthreads();
+  return total;
+}
 
-  // Large k: the k-th largest value is found by bisection on its
-  // order-preserving key (32 block-wide counts) instead of k rounds of a
-  // block-wide maximum; small k keep the rounds, which cost less there (the
-  // instantiations for k <= 16 carry no bisection code, for their registers).
+// m* of row t: the k-th largest of its tile maxima part_m[j][t] (the entries
+// of this selection are the tiles), -inf when fewer than k tile maxima are
+// not NaN.  Large k: by bisection on the order-preserving key (32 block-wide
+// counts) instead of k rounds of a block-wide maximum; small k keep the
+// rounds, which cost less there (the instantiations for k <= 16 carry no
+// bisection code, for their registers).
+template <int KC>
+__device__ float kth_tile_max(const float *__restrict__ part_m, int t, int T, int nST, int k,
+                              TopK<KC> &sel, Cand *red, Cand *win, int *csum) {
+  const int tid = threadIdx.x;
   const bool bisect = KC >= 32 && k >= TOPK_BISECT_K;
-  // 1) m*: the k-th largest tile maximum (entries of a row are the tiles);
-  //    -inf when fewer than k tile maxima are not NaN
   float mstar;
   if (KC >= 32 && bisect && nST <= TOPK_THREADS * TOPK_MPT) {
     uint32_t key[TOPK_MPT];
@@ -1570,7 +1559,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(
       int c = 0;
 #pragma unroll
       for (int u = 0; u < TOPK_MPT; ++u) c += (ok[u] && key[u] >= kmin) ? 1 : 0;
-      return block_sum(c);
+      return block_sum(c, csum);
     };
     if (count_ge(0) < k) {
       mstar = -INFINITY;
@@ -1585,22 +1574,99 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(
     for (int j = tid; j < nST; j += TOPK_THREADS) sel.offer(part_m[(size_t)j * T + t], j, k);
     Cand kth{-INFINITY, TopK<KC>::NONE};
     const int kk = k < nST ? k : nST;
-    for (int r = 0; r < kk; ++r) kth = sel.next(k, red, &win);
+    for (int r = 0; r < kk; ++r) kth = sel.next(k, red, win);
     mstar = kth.v;
   }
+  return mstar;
+}
 
-  // 2) the tiles that can hold a top-k entry
-  if (tid == 0) nlist = 0;
-  __syncthreads();
-  for (int j = tid; j < nST; j += TOPK_THREADS) {
-    const float m = part_m[(size_t)j * T + t];
-    if (m >= mstar) {
-      const int at = atomicAdd(&nlist, 1);
-      if (at < TOPK_LIST) list[at] = j;
+// The candidate-pair source of the selection (rlk_topk_logp_direct): row
+// t's candidates are the tiles cand_tile[t C + u], u < cand_n[t], whose 128
+// raw logits sit at pair t C + u of pair_z (128 floats per pair).
+// cand_n[t] < 0 marks a row whose k-th largest tile maximum is -inf: all its
+// tiles are candidates, tile j at pair t C + j when nST <= C, else at pair
+// T C + d nST + j with d = deg_rank[t] (d < 0: the workspace had no room
+// for the row).
+struct PairSrc {
+  const int *cand_n;
+  const int *cand_tile;
+  const int *deg_rank;
+  const float *pair_z;
+  int C;
+};
+
+template <int KC, bool PAIRS>
+__global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(
+    const float *__restrict__ logits, int64_t ld, const float *__restrict__ lse,
+    const float *__restrict__ part_m, int T, int V, int nST, int k, float inv_tau, int bf16,
+    float *__restrict__ out_lp, int32_t *__restrict__ out_id, const PairSrc ps) {
+  __shared__ Cand red[TOPK_THREADS / 64];
+  __shared__ Cand win;
+  __shared__ int list[TOPK_LIST];
+  __shared__ int nlist;
+  __shared__ int csum[TOPK_THREADS / 64];
+  __shared__ float win_v[64];
+  __shared__ int win_i[64];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float *row = PAIRS ? nullptr : logits + (size_t)t * ld;
+  TopK<KC> sel;
+  const bool bisect = KC >= 32 && k >= TOPK_BISECT_K;
+
+  float mstar = 0.0f;
+  int n;
+  int64_t dbase = 0;   // pairs, whole row: tile j's logits are at pair dbase + j
+  if constexpr (PAIRS) {
+    const int cn = ps.cand_n[t];
+    if (cn >= 0) {
+      for (int u = tid; u < cn; u += TOPK_THREADS) list[u] = ps.cand_tile[(size_t)t * ps.C + u];
+      n = cn;
+    } else {
+      if (nST <= ps.C) {
+        dbase = (int64_t)t * ps.C;
+      } else {
+        const int d = ps.deg_rank[t];
+        if (d < 0) {   // no room for this row's tiles: marked, not guessed
+          if (tid < k) {
+            out_lp[(size_t)t * k + tid] = __builtin_nanf("");
+            out_id[(size_t)t * k + tid] = -2;
+          }
+          return;
+        }
+        dbase = (int64_t)T * ps.C + (int64_t)d * nST;
+      }
+      n = TOPK_LIST + 1;   // the whole row
     }
+    __syncthreads();
+  } else {
+    // 1) m*: the k-th largest tile maximum
+    mstar = kth_tile_max<KC>(part_m, t, T, nST, k, sel, red, &win, csum);
+    // 2) the tiles that can hold a top-k entry
+    if (tid == 0) nlist = 0;
+    __syncthreads();
+    for (int j = tid; j < nST; j += TOPK_THREADS) {
+      const float m = part_m[(size_t)j * T + t];
+      if (m >= mstar) {
+        const int at = atomicAdd(&nlist, 1);
+        if (at < TOPK_LIST) list[at] = j;
+      }
+    }
+    __syncthreads();
+    n = nlist;
   }
-  __syncthreads();
-  const int n = nlist;
+  // raw logit of list candidate i (entry v), and of entry v of the whole row
+  auto zl = [&](int i, int v) -> float {
+    if constexpr (PAIRS)
+      return ps.pair_z[((size_t)t * ps.C + i / STAT_V) * STAT_V + (i % STAT_V)];
+    else
+      return row[v];
+  };
+  auto zr = [&](int v) -> float {
+    if constexpr (PAIRS)
+      return ps.pair_z[(size_t)(dbase + v / STAT_V) * STAT_V + (v % STAT_V)];
+    else
+      return row[v];
+  };
 
   // 3) top-k of those tiles' entries (or of the whole row)
   const float l = lse[t];
@@ -1620,7 +1686,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(
     for (int u = 0; u < TOPK_CPT; ++u) {
       const int i = u * TOPK_THREADS + tid;
       const int v = i < ne ? list[i / STAT_V] * STAT_V + (i % STAT_V) : V;
-      float z = v < V ? row[v] : __builtin_nanf("");
+      float z = v < V ? zl(i, v) : __builtin_nanf("");
       z = z * inv_tau;
       if (bf16) z = (float)(__bf16)z;
       cz[u] = z;
@@ -1631,7 +1697,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(
       int c = 0;
 #pragma unroll
       for (int u = 0; u < TOPK_CPT; ++u) c += (cid[u] >= 0 && pred(u)) ? 1 : 0;
-      return block_sum(c);
+      return block_sum(c, csum);
     };
     const int nvalid = count([](int) { return true; });
     const int kk = k < nvalid ? k : nvalid;
@@ -1672,18 +1738,18 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(
     return;
   }
   sel.reset();
-  auto offer_v = [&](int v) {
-    float z = row[v] * inv_tau;
+  auto offer_z = [&](float z, int v) {
+    z = z * inv_tau;
     if (bf16) z = (float)(__bf16)z;
     sel.offer(z, v, k);
   };
   if (n <= TOPK_LIST && mstar == mstar) {
     for (int i = tid; i < n * STAT_V; i += TOPK_THREADS) {
       const int v = list[i / STAT_V] * STAT_V + (i % STAT_V);
-      if (v < V) offer_v(v);
+      if (v < V) offer_z(zl(i, v), v);
     }
   } else {
-    for (int v = tid; v < V; v += TOPK_THREADS) offer_v(v);
+    for (int v = tid; v < V; v += TOPK_THREADS) offer_z(zr(v), v);
   }
   for (int r = 0; r < k; ++r) {
     const Cand w = sel.next(k, red, &win);
@@ -1699,17 +1765,329 @@ hipError_t launch_topk(const float *logits, int64_t ld, const float *lse, const 
                        int32_t *out_id, hipStream_t s) {
   const int nST = ceil_div(V, STAT_V);
   if (k <= 8)
-    hipLaunchKernelGGL(topk_kernel<8>, dim3(T), dim3(TOPK_THREADS), 0, s, logits, ld, lse, part_m,
-                       T, V, nST, k, inv_tau, bf16, out_lp, out_id);
+    hipLaunchKernelGGL((topk_kernel<8, false>), dim3(T), dim3(TOPK_THREADS), 0, s, logits, ld, lse, part_m,
+                       T, V, nST, k, inv_tau, bf16, out_lp, out_id, PairSrc{});
   else if (k <= 16)
-    hipLaunchKernelGGL(topk_kernel<16>, dim3(T), dim3(TOPK_THREADS), 0, s, logits, ld, lse,
-                       part_m, T, V, nST, k, inv_tau, bf16, out_lp, out_id);
+    hipLaunchKernelGGL((topk_kernel<16, false>), dim3(T), dim3(TOPK_THREADS), 0, s, logits, ld, lse,
+                       part_m, T, V, nST, k, inv_tau, bf16, out_lp, out_id, PairSrc{});
   else if (k <= 32)
-    hipLaunchKernelGGL(topk_kernel<32>, dim3(T), dim3(TOPK_THREADS), 0, s, logits, ld, lse,
-                       part_m, T, V, nST, k, inv_tau, bf16, out_lp, out_id);
+    hipLaunchKernelGGL((topk_kernel<32, false>), dim3(T), dim3(TOPK_THREADS), 0, s, logits, ld, lse,
+                       part_m, T, V, nST, k, inv_tau, bf16, out_lp, out_id, PairSrc{});
   else
-    hipLaunchKernelGGL(topk_kernel<64>, dim3(T), dim3(TOPK_THREADS), 0, s, logits, ld, lse,
-                       part_m, T, V, nST, k, inv_tau, bf16, out_lp, out_id);
+    hipLaunchKernelGGL((topk_kernel<64, false>), dim3(T), dim3(TOPK_THREADS), 0, s, logits, ld, lse,
+                       part_m, T, V, nST, k, inv_tau, bf16, out_lp, out_id, PairSrc{});
+  return hipGetLastError();
+}
+
+// ------------------------------------------------ top-k from the operands
+// rlk_topk_logp_direct: the top-k selection above, but the logits of the
+// candidate tiles are recomputed instead of read from a stored [T][V]
+// array.  Candidate tiles of row t (m* its k-th largest tile maximum):
+//   A: the tiles whose maximum exceeds m* (fewer than k of them: the k-th
+//      largest maximum is m*);
+//   B: the first k - |A| tiles, by index, whose maximum equals m*.
+// Every top-k entry lies in A or B.  Entries above m* lie in A.  The entries
+// equal to m* that make the cut are the smallest ids among all entries equal
+// to m*; each tile of B holds at least one (its maximum, a value of the row),
+// so the first k - |A| of them hold at least k - |A| >= the number needed,
+// and any tile of B past them holds only larger ids.  So a row has exactly
+// k candidate tiles.  When m* is -inf (fewer than k tiles hold a value above
+// -inf: rows of NaN or infinities) every tile is a candidate.
+//
+// The logits of a (row, tile) pair come from the same MFMA instruction over
+// the same operands in the same K order as the logit GEMM (32 x 32 x 16 bf16,
+// fp32 accumulator from 0, K steps of 16 in increasing order, and the zero
+// block the GEMM appends when H / 64 is odd), so they are the GEMM's bits: the
+// selection sees exactly the values the stored-logits path reads.
+
+// 1) per row: m*, the candidate tiles into the row's k slots, and one count
+//    per candidate on its tile.
+template <int KC>
+__global__ __launch_bounds__(TOPK_THREADS) void topk_cand_kernel(const TopkDirectArgs a) {
+  __shared__ Cand red[TOPK_THREADS / 64];
+  __shared__ Cand win;
+  __shared__ int csum[TOPK_THREADS / 64];
+  __shared__ int nA;
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int T = a.T, nST = a.nST, k = a.k, C = a.C;
+  TopK<KC> sel;
+  const float mstar = kth_tile_max<KC>(a.part_m, t, T, nST, k, sel, red, &win, csum);
+  int *tiles = a.cand_tile + (size_t)t * C;
+  const float *pm = a.part_m + t;   // column t of [nST][T]
+  if (!(mstar > -INFINITY)) {
+    // every tile; with nST <= C they use the row's own slots, otherwise the
+    // plan assigns room (and counts them) in row order
+    if (tid == 0) a.cand_n[t] = -1;
+    if (nST <= C)
+      for (int j = tid; j < nST; j += TOPK_THREADS) atomicAdd(&a.tile_count[j], 1);
+    return;
+  }
+  if (tid == 0) nA = 0;
+  __syncthreads();
+  for (int j = tid; j < nST; j += TOPK_THREADS)
+    if (pm[(size_t)j * T] > mstar) {
+      const int at = atomicAdd(&nA, 1);
+      tiles[at] = j;
+      atomicAdd(&a.tile_count[j], 1);
+    }
+  __syncthreads();
+  const int na = nA;
+  const int need = k - na;
+  const int lane = tid & 63, w = tid >> 6;
+  int taken = 0;   // tied tiles met so far (uniform)
+  for (int base = 0; base < nST && taken < need; base += TOPK_THREADS) {
+    const int j = base + tid;
+    const bool f = j < nST && pm[(size_t)j * T] == mstar;
+    const uint64_t b = __ballot(f);
+    const int before = __popcll(b & ((1ull << lane) - 1ull));
+    if (lane == 0) csum[w] = __popcll(b);
+    __syncthreads();
+    int wbase = 0, total = 0;
+#pragma unroll
+    for (int q = 0; q < TOPK_THREADS / 64; ++q) {
+      wbase += q < w ? csum[q] : 0;
+      total += csum[q];
+    }
+    __syncthreads();
+    const int r = taken + wbase + before;
+    if (f && r < need) {
+      tiles[na + r] = j;
+      atomicAdd(&a.tile_count[j], 1);
+    }
+    taken += total;
+  }
+  if (tid == 0) a.cand_n[t] = na + (taken < need ? taken : need);
+}
+
+// Pairs per work item of the tile-logits kernel: 4 waves of 32.
+constexpr int TL_PAIRS = 128;
+
+// 2) one workgroup: room for the rows with m* = -inf (the first dcap in row
+//    order, when nST > C), then per tile its pair count, its first pair slot
+//    and its work items (TL_PAIRS pairs each, in tile order), and the tile of every
+//    work item.
+constexpr int PLAN_THREADS = 1024;
+__global__ __launch_bounds__(PLAN_THREADS) void topk_plan_kernel(const TopkDirectArgs a) {
+  __shared__ int wsum[PLAN_THREADS / 64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // exclusive prefix of x over the workgroup; `total` gets the sum
+  auto scan = [&](int x, int &total) {
+    int incl = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    int wb = 0;
+    total = 0;
+#pragma unroll
+    for (int q = 0; q < PLAN_THREADS / 64; ++q) {
+      wb += q < w ? wsum[q] : 0;
+      total += wsum[q];
+    }
+    __syncthreads();
+    return wb + incl - x;
+  };
+  int served = 0;
+  if (a.nST > a.C) {
+    int running = 0;
+    for (int base = 0; base < a.T; base += PLAN_THREADS) {
+      const int t = base + tid;
+      const int f = (t < a.T && a.cand_n[t] < 0) ? 1 : 0;
+      int tot;
+      const int r = running + scan(f, tot);
+      if (f) {
+        const int d = r < a.dcap ? r : -1;
+        a.deg_rank[t] = d;
+        if (d >= 0) a.deg_row[d] = t;
+      }
+      running += tot;
+    }
+    served = running < a.dcap ? running : a.dcap;
+  }
+  int carry_p = 0, carry_i = 0;
+  for (int base = 0; base < a.nST; base += PLAN_THREADS) {
+    const int j = base + tid;
+    const int c = j < a.nST ? a.tile_count[j] + served : 0;
+    int tp, ti;
+    const int op = scan(c, tp);
+    const int oi = scan((c + TL_PAIRS - 1) / TL_PAIRS, ti);
+    if (j < a.nST) {
+      a.tile_count[j] = c;
+      a.tile_off[j] = carry_p + op;
+      a.item_off[j] = carry_i + oi;
+      a.tile_fill[j] = 0;
+    }
+    carry_p += tp;
+    carry_i += ti;
+  }
+  if (tid == 0) {
+    a.item_off[a.nST] = carry_i;
+    a.totals[0] = carry_i;
+    a.totals[1] = carry_p;
+  }
+  __syncthreads();
+  for (int j = tid; j < a.nST; j += PLAN_THREADS)
+    for (int it = a.item_off[j]; it < a.item_off[j + 1]; ++it) a.item_tile[it] = j;
+}
+
+// 3) per row: its pairs into their tiles' buckets (a pair's place inside its
+//    bucket changes which work item computes it, never its bits).
+__global__ __launch_bounds__(64) void topk_scatter_kernel(const TopkDirectArgs a) {
+  const int t = blockIdx.x, l = threadIdx.x;
+  const int cn = a.cand_n[t];
+  auto put = [&](int j, int p) {
+    a.bucket[a.tile_off[j] + atomicAdd(&a.tile_fill[j], 1)] = p;
+  };
+  if (cn >= 0) {
+    for (int u = l; u < cn; u += 64) put(a.cand_tile[(size_t)t * a.C + u], t * a.C + u);
+  } else if (a.nST <= a.C) {
+    for (int j = l; j < a.nST; j += 64) put(j, t * a.C + j);
+  } else {
+    const int d = a.deg_rank[t];
+    if (d >= 0)
+      for (int j = l; j < a.nST; j += 64) put(j, a.T * a.C + d * a.nST + j);
+  }
+}
+
+// 4) one workgroup per work item: the 128 x (up to 128) logits of one tile
+//    for up to TL_PAIRS of its pairs, wave w taking pairs 32 w .. 32 w + 31.
+//    The tile's weight block (128 rows x 64 K, 16 KiB) goes to LDS by
+//    direct-to-LDS loads, double-buffered and shared by the 4 waves, in the
+//    logit GEMM's layout (16-byte chunk c of row r at c ^ swz(r); load q of
+//    wave w fills rows 8 (4 q + w) .. + 7); each lane loads its pair's hidden
+//    row straight into the MFMA operand layout (row l & 31, K slice 8 (l >> 5)
+//    .. + 7 of each 16-deep step), one block ahead.  Rows past V read zeros
+//    through the resource's range.
+__global__ __launch_bounds__(256) void tile_logits_kernel(const TopkDirectArgs a) {
+  __shared__ __attribute__((aligned(16))) char wlds[2][TILE_K * STAT_V * 2];
+  const int it = blockIdx.x;
+  if (it >= a.totals[0]) return;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, r = l & 31, fk = l >> 5;
+  const int j = a.item_tile[it];
+  const int first = a.tile_off[j] + TL_PAIRS * (it - a.item_off[j]) + 32 * wave;
+  const int cnt = min(32, a.tile_off[j] + a.tile_count[j] - first);   // <= 0: an idle wave
+  const int p = r < cnt ? a.bucket[first + r] : -1;
+  const int regular = a.T * a.C;
+  int t = -1;
+  if (p >= 0) t = p < regular ? p / a.C : a.deg_row[(p - regular) / a.nST];
+  const bool hv = t >= 0;
+  const uint16_t *hp = a.hidden + (size_t)(hv ? t : 0) * a.ldh + 8 * fk;
+  const int v0 = j * STAT_V;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(
+      a.weight + (size_t)v0 * a.ldw, (uint32_t)(min(STAT_V, a.V - v0) * a.ldw * 2));
+  typedef __attribute__((address_space(3))) void lds_void;
+  // load q of this wave: row 8 (4 q + wave) + (l >> 3), global chunk (l & 7) ^ swz(row)
+  uint32_t gofs[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = 8 * (4 * q + wave) + (l >> 3);
+    gofs[q] = (uint32_t)(row * a.ldw * 2 + (((l & 7) ^ swz(row)) << 4));
+  }
+  auto wload = [&](int kb, int st) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rw, (lds_void *)(&wlds[st][0] + (4 * q + wave) * 1024), 16, gofs[q],
+          (uint32_t)kb * (TILE_K * 2), 0, 0);
+  };
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  // (a lane without a pair loads row 0 and zeroes it where it is used, so
+  // that no wait for the load comes before the next block)
+  auto hload = [&](int kb, u32x4 (&hb)[4]) {
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) hb[s4] = *(const u32x4 *)(hp + kb * TILE_K + 16 * s4);
+  };
+  f32x16 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[i][q] = 0.0f;
+  const int nk = a.H / TILE_K;
+  const bool live = cnt > 0;   // uniform per wave
+  u32x4 hb0[4], hb1[4];
+  // K block kb from stage ST (== kb & 1); the next block's loads go to the
+  // other stage and hidden-fragment set
+  auto block = [&](int kb, auto stage) {
+    constexpr int ST = decltype(stage)::value;
+    u32x4(&cur)[4] = ST ? hb1 : hb0;
+    u32x4(&nxt)[4] = ST ? hb0 : hb1;
+    // this block's loads (every wave's) have landed; the other stage is free
+    __builtin_amdgcn_s_waitcnt(VMCNT0);
+    __syncthreads();
+    if (kb + 1 < nk) {
+      wload(kb + 1, ST ^ 1);
+      if (live) hload(kb + 1, nxt);
+    }
+    if (live) {
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const bf16x8 b = __builtin_bit_cast(bf16x8, hv ? cur[s4] : zero4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 32 * i + r;
+          const bf16x8 w8 = *(const bf16x8 *)(&wlds[ST][0] + row * 128 +
+                                              (((2 * s4 + fk) ^ swz(row)) << 4));
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w8, b, acc[i], 0, 0, 0);
+        }
+      }
+    }
+  };
+  wload(0, 0);
+  if (live) hload(0, hb0);
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  int kb = 0;
+  for (; kb + 1 < nk; kb += 2) {
+    block(kb, S0{});
+    block(kb + 1, S1{});
+  }
+  if (kb < nk) block(kb, S0{});
+  if (!live) return;
+  if (nk & 1) {   // the GEMM's appended zero block: 4 steps of zero operands
+    const bf16x8 z = __builtin_bit_cast(bf16x8, zero4);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(z, z, acc[i], 0, 0, 0);
+  }
+  // acc[i][4 q + e] is the logit of column 32 i + 8 q + 4 fk + e of the tile
+  if (p >= 0) {
+    float *o = a.pair_z + (size_t)p * STAT_V + 4 * fk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(u32x4 *)(o + 32 * i + 8 * q) =
+            u32x4{__float_as_uint(acc[i][4 * q]), __float_as_uint(acc[i][4 * q + 1]),
+                  __float_as_uint(acc[i][4 * q + 2]), __float_as_uint(acc[i][4 * q + 3])};
+  }
+}
+
+template <int KC>
+void launch_topk_direct_kc(const TopkDirectArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL((topk_cand_kernel<KC>), dim3(a.T), dim3(TOPK_THREADS), 0, s, a);
+  hipLaunchKernelGGL(topk_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, s, a);
+  hipLaunchKernelGGL(topk_scatter_kernel, dim3(a.T), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(tile_logits_kernel, dim3(a.items_max), dim3(256), 0, s, a);
+  const PairSrc ps{a.cand_n, a.cand_tile, a.deg_rank, a.pair_z, a.C};
+  hipLaunchKernelGGL((topk_kernel<KC, true>), dim3(a.T), dim3(TOPK_THREADS), 0, s, nullptr,
+                     (int64_t)0, a.lse, a.part_m, a.T, a.V, a.nST, a.k, a.inv_tau, a.bf16,
+                     a.out_lp, a.out_id, ps);
+}
+
+hipError_t launch_topk_direct(const TopkDirectArgs &a, hipStream_t s) {
+  hipError_t e = launch_zero(reinterpret_cast<float *>(a.tile_count), a.nST, s);
+  if (e != hipSuccess) return e;
+  if (a.k <= 8) launch_topk_direct_kc<8>(a, s);
+  else if (a.k <= 16) launch_topk_direct_kc<16>(a, s);
+  else if (a.k <= 32) launch_topk_direct_kc<32>(a, s);
+  else launch_topk_direct_kc<64>(a, s);
   return hipGetLastError();
 }
 

@@ -84,7 +84,7 @@ def test_boundary_calls_of_the_scope_table():
 
 
 def test_constants():
-    assert rlk.rlk_abi_version() == 3
+    assert rlk.rlk_abi_version() == 4
     assert rlk.rlk_vocab_tile() == 128
     msgs = {rlk.rlk_status_string(s) for s in range(9)}
     assert len(msgs) == 9 and all(msgs)
@@ -559,6 +559,64 @@ def test_topk_error_paths(kw, status):
     assert rlk.lib().rlk_topk_logp(a["logits"], a["ld"], a["lse"], a["ws"], a["ws_bytes"],
                                    a["T"], a["V"], a["k"], a["inv_tau"], a["flags"],
                                    a["out_lp"], a["out_id"], None) == status
+
+
+def test_topk_direct_workspace_size():
+    """k pair slots of 128 fp32 logits per row, then room for the rows whose
+    k-th largest tile maximum is -inf (all ceil(V / 128) tiles each) when
+    there are more tiles than k; 0 for invalid arguments."""
+    wb = rlk.rlk_topk_logp_direct_workspace_bytes
+    r = lambda x: (x + 255) // 256 * 256
+    for T, V, k, d in [(4096, 151936, 20, 16), (300, 1000, 20, 7), (1, 128, 1, 0)]:
+        nst = (V + 127) // 128
+        d = d if nst > k else 0
+        P = T * k + d * nst
+        items = (P + 127) // 128 + nst
+        want = (r(P * 512) + r(P * 4) + r(T * k * 4) + 2 * r(T * 4) + r(max(d, 1) * 4)
+                + 3 * r(nst * 4) + r((nst + 1) * 4) + r(items * 4) + r(16))
+        assert wb(T, V, k, d) == want, (T, V, k, d)
+    assert wb(4096, 151936, 20, 17) > wb(4096, 151936, 20, 16)
+    assert wb(300, 1000, 20, 1000) == wb(300, 1000, 20, 0)     # 8 tiles <= k: no extra room
+    assert wb(0, 10, 1, 0) == 0 and wb(4, 0, 1, 0) == 0
+    assert wb(4, 1000, 0, 0) == 0 and wb(4, 1000, 65, 0) == 0 and wb(4, 10, 20, 0) == 0
+    assert wb(4, 1000, 5, -1) == 0
+    assert wb(1 << 25, 151936, 64, 0) == 0                    # more than 2^30 pairs
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), rlk.RLK_ERR_INVALID_SHAPE),
+    (dict(V=0), rlk.RLK_ERR_INVALID_SHAPE),
+    (dict(H=100, ldh=104, ldw=104), rlk.RLK_ERR_UNSUPPORTED),
+    (dict(k=0), rlk.RLK_ERR_INVALID_VALUE),
+    (dict(k=65), rlk.RLK_ERR_INVALID_VALUE),
+    (dict(k=20, V=10), rlk.RLK_ERR_INVALID_VALUE),
+    (dict(dcap=-1), rlk.RLK_ERR_INVALID_VALUE),
+    (dict(inv_tau=float("inf")), rlk.RLK_ERR_INVALID_VALUE),
+    (dict(flags=4), rlk.RLK_ERR_INVALID_VALUE),
+    (dict(T=1 << 25, k=64), rlk.RLK_ERR_UNSUPPORTED),
+    (dict(hidden=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(lse=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(stats=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(ws=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(out_id=None), rlk.RLK_ERR_NULL_POINTER),
+    (dict(hidden=FAKE + 8), rlk.RLK_ERR_MISALIGNED),
+    (dict(stats=WS_FAKE + 4), rlk.RLK_ERR_MISALIGNED),
+    (dict(out_lp=FAKE + 2), rlk.RLK_ERR_MISALIGNED),
+    (dict(stats_bytes=64), rlk.RLK_ERR_WORKSPACE_TOO_SMALL),
+    (dict(ws_bytes=64), rlk.RLK_ERR_WORKSPACE_TOO_SMALL),
+    (dict(T=0, hidden=None, weight=None, lse=None, stats=None, ws=None, out_lp=None,
+          out_id=None), rlk.RLK_OK),
+])
+def test_topk_direct_error_paths(kw, status):
+    a = dict(hidden=FAKE, ldh=256, weight=FAKE, ldw=256, lse=FAKE, stats=WS_FAKE,
+             stats_bytes=1 << 20, T=4, H=256, V=1000, k=5, inv_tau=1.0, flags=0, dcap=2,
+             ws=WS_FAKE, ws_bytes=1 << 24, out_lp=FAKE, out_id=FAKE)
+    a.update(kw)
+    assert rlk.lib().rlk_topk_logp_direct(
+        a["hidden"], a["ldh"], a["weight"], a["ldw"], a["lse"], a["stats"], a["stats_bytes"],
+        a["T"], a["H"], a["V"], a["k"], a["inv_tau"], a["flags"], a["dcap"], a["ws"],
+        a["ws_bytes"], a["out_lp"], a["out_id"], None) == status
+    assert rlk.rlk_last_hip_error() == 0
 
 
 def test_binding_type_errors_before_any_device_work():
