@@ -1593,6 +1593,7 @@ struct PairSrc {
   const int *deg_rank;
   const float *pair_z;
   int C;
+  int all_tiles_only;   // skip the rows with k candidate tiles (a wave per row took them)
 };
 
 template <int KC, bool PAIRS>
@@ -1618,6 +1619,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(
   int64_t dbase = 0;   // pairs, whole row: tile j's logits are at pair dbase + j
   if constexpr (PAIRS) {
     const int cn = ps.cand_n[t];
+    if (cn >= 0 && ps.all_tiles_only) return;
     if (cn >= 0) {
       for (int u = tid; u < cn; u += TOPK_THREADS) list[u] = ps.cand_tile[(size_t)t * ps.C + u];
       n = cn;
@@ -2056,26 +2058,212 @@ __global__ __launch_bounds__(256) void tile_logits_kernel(const TopkDirectArgs a
       for (int i = 0; i < 4; ++i)
         acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(z, z, acc[i], 0, 0, 0);
   }
-  // acc[i][4 q + e] is the logit of column 32 i + 8 q + 4 fk + e of the tile
+  // acc[i][4 q + e] is the logit of column 32 i + 8 q + 4 fk + e of the tile;
+  // columns past V are stored as NaN, which no selection takes
   if (p >= 0) {
     float *o = a.pair_z + (size_t)p * STAT_V + 4 * fk;
+    const int lim = a.V - v0 - 4 * fk;   // columns at offset < lim are entries
+    const uint32_t qnan = 0x7FC00000u;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *(u32x4 *)(o + 32 * i + 8 * q) =
-            u32x4{__float_as_uint(acc[i][4 * q]), __float_as_uint(acc[i][4 * q + 1]),
-                  __float_as_uint(acc[i][4 * q + 2]), __float_as_uint(acc[i][4 * q + 3])};
+      for (int q = 0; q < 4; ++q) {
+        u32x4 d;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          d[e] = 32 * i + 8 * q + e < lim ? __float_as_uint(acc[i][4 * q + e]) : qnan;
+        *(u32x4 *)(o + 32 * i + 8 * q) = d;
+      }
+  }
+}
+
+// The candidate step and the selection with one wave per row (rows with k
+// candidate tiles; the tile maxima of a row or its k x 128 candidates held as
+// order keys in registers): every count is a wave reduction, no workgroup
+// barrier.  The same entries as the workgroup kernels, which remain for
+// vocabularies of more than 64 x CW_MPL tiles (candidate step) and for the
+// rows that need all their tiles (selection).
+__device__ __forceinline__ float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+constexpr int CW_MPL = 32;   // tile maxima per lane: up to 2048 tiles
+
+__global__ __launch_bounds__(256) void topk_cand_wave_kernel(const TopkDirectArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (t >= a.T) return;   // the whole wave
+  const int T = a.T, nST = a.nST, k = a.k, C = a.C;
+  const float *pm = a.part_m + t;
+  // tile j = 64 u + lane; key 0 marks no tile (past nST; a NaN maximum)
+  uint32_t key[CW_MPL];
+#pragma unroll
+  for (int u = 0; u < CW_MPL; ++u) {
+    const int j = 64 * u + lane;
+    const float m = j < nST ? pm[(size_t)j * T] : __builtin_nanf("");
+    key[u] = m == m ? order_key(m) : 0u;
+  }
+  // a count over the wave: per u the compare's lane mask, counted in the
+  // scalar unit (no cross-lane reduction)
+  auto count_ge = [&](uint32_t kmin) {   // kmin >= 1
+    int c = 0;
+#pragma unroll
+    for (int u = 0; u < CW_MPL; ++u) c += __popcll(__ballot(key[u] >= kmin));
+    return c;
+  };
+  uint32_t K = 0;   // the key of m*: the largest with at least k tile maxima at or above it
+  if (count_ge(1u) >= k)
+    for (int bit = 31; bit >= 0; --bit)
+      if (count_ge(K | (1u << bit)) >= k) K |= 1u << bit;
+  if (K == 0u || !(key_value(K) > -INFINITY)) {   // m* = -inf: every tile
+    if (lane == 0) a.cand_n[t] = -1;
+    if (nST <= C)
+      for (int j = lane; j < nST; j += 64) atomicAdd(&a.tile_count[j], 1);
+    return;
+  }
+  // A (maxima above m*) and the first k - |A| tiles whose maximum is m*, in
+  // tile index order (the selection relies on it: candidate order is then id
+  // order)
+  int gt = 0;
+#pragma unroll
+  for (int u = 0; u < CW_MPL; ++u) gt += __popcll(__ballot(key[u] > K));
+  const int need = k - gt;
+  int *tiles = a.cand_tile + (size_t)t * C;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  int n = 0, taken = 0;   // tiles written; tied tiles met (both uniform)
+#pragma unroll
+  for (int u = 0; u < CW_MPL; ++u) {
+    const bool tie = key[u] == K;
+    const uint64_t bt = __ballot(tie);
+    const bool f = key[u] > K || (tie && taken + __popcll(bt & lt) < need);
+    const uint64_t b = __ballot(f);
+    if (f) {
+      const int j = 64 * u + lane;
+      tiles[n + __popcll(b & lt)] = j;
+      atomicAdd(&a.tile_count[j], 1);
+    }
+    n += __popcll(b);
+    taken += __popcll(bt);
+  }
+  if (lane == 0) a.cand_n[t] = n;
+}
+
+// CPL >= 2 k, even: candidate i = 64 u + lane of the
+// row's k x 128, entry i & 127 of tile list[i >> 7].  The list is in tile
+// order, so candidate order is id order: the ties at the k-th value are cut
+// at the smallest candidate indices, and ids are looked up for the winners
+// only.  Entries past V hold NaN (stored so by the tile-logits kernel).
+template <int CPL>
+__global__ __launch_bounds__(256) void topk_select_wave_kernel(const TopkDirectArgs a) {
+  __shared__ float win_v[4][64];
+  __shared__ int win_i[4][64];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + w;   // uniform over the wave
+  if (t >= a.T) return;
+  const int cn = a.cand_n[t];
+  if (cn < 0) return;   // a row that needs all its tiles: the workgroup kernel
+  const int k = a.k;
+  const int ne = cn * STAT_V;
+  const float *zp = a.pair_z + (size_t)t * a.C * STAT_V;
+  const float itau = a.inv_tau;
+  const bool rb16 = a.bf16 != 0;
+  uint32_t key[CPL];   // 0: no candidate (past the row's k x 128, or NaN)
+#pragma unroll
+  for (int u = 0; u < CPL; ++u) {
+    const int i = 64 * u + lane;
+    float z = zp[i < ne ? i : 0] * itau;   // an unconditional load, then the select
+    if (rb16) z = (float)(__bf16)z;
+    key[u] = (i < ne && z == z) ? order_key(z) : 0u;
+  }
+  // (every predicate below is false for key 0: the thresholds are >= 1 and
+  // K >= 1 once kk > 0; no separate validity mask per candidate)
+  auto count = [&](auto pred) {   // over the wave, in the scalar unit
+    int c = 0;
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) c += __popcll(__ballot(pred(u)));
+    return c;
+  };
+  const int nvalid = count([&](int u) { return key[u] >= 1u; });
+  const int kk = k < nvalid ? k : nvalid;
+  uint32_t K = 0;   // the largest key with at least kk entries at or above it
+  int x = 0;        // ties at K are taken for candidate indices <= x
+  if (kk > 0) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t trial = K | (1u << bit);
+      if (count([&](int u) { return key[u] >= trial; }) >= kk) K = trial;
+    }
+    const int need = kk - count([&](int u) { return key[u] > K; });
+    const int top = ne > 1 ? 31 - __clz(ne - 1) : 0;
+    for (int bit = top; bit >= 0; --bit) {
+      const int trial = x | (1 << bit);
+      // candidate 64 u + lane < trial  <=>  lane < trial - 64 u (a scalar per u)
+      if (count([&](int u) { return key[u] == K && lane < trial - 64 * u; }) < need) x = trial;
+    }
+  }
+  // the kk winners into this wave's slots, in any order
+  const uint64_t lt = (1ull << lane) - 1ull;
+  const int *list = a.cand_tile + (size_t)t * a.C;
+  // the winners' values are read again (a fresh load: keeping the first
+  // loop's values live would cost CPL registers)
+  const float *zw = zp;
+  asm volatile("" : "+s"(zw));
+  int nw = 0;
+#pragma unroll
+  for (int u = 0; u < CPL; ++u) {
+    const bool f = kk > 0 && (key[u] > K || (key[u] == K && lane <= x - 64 * u));
+    const uint64_t b = __ballot(f);
+    if (f) {
+      const int i = 64 * u + lane;
+      const int at = nw + __popcll(b & lt);
+      float z = zw[i] * itau;
+      if (rb16) z = (float)(__bf16)z;
+      win_v[w][at] = z;
+      win_i[w][at] = list[i / STAT_V] * STAT_V + (i % STAT_V);
+    }
+    nw += __popcll(b);
+  }
+  __builtin_amdgcn_wave_barrier();
+  const float l = a.lse[t];
+  if (lane < kk) {
+    const float mv = win_v[w][lane];
+    const int mi = win_i[w][lane];
+    int rank = 0;
+    for (int q = 0; q < kk; ++q) rank += cand_gt(win_v[w][q], win_i[w][q], mv, mi) ? 1 : 0;
+    a.out_lp[(size_t)t * k + rank] = mv - l;
+    a.out_id[(size_t)t * k + rank] = mi;
+  } else if (lane < k) {
+    a.out_lp[(size_t)t * k + lane] = -INFINITY;
+    a.out_id[(size_t)t * k + lane] = -1;
   }
 }
 
 template <int KC>
 void launch_topk_direct_kc(const TopkDirectArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((topk_cand_kernel<KC>), dim3(a.T), dim3(TOPK_THREADS), 0, s, a);
+  const int wave_blocks = ceil_div(a.T, 4);
+  // up to 64 x CW_MPL tiles: a wave per row for the candidates (their lists
+  // in tile order) and for the selection of the rows with k candidate tiles
+  const bool waves = a.nST <= 64 * CW_MPL;
+  if (waves)
+    hipLaunchKernelGGL(topk_cand_wave_kernel, dim3(wave_blocks), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((topk_cand_kernel<KC>), dim3(a.T), dim3(TOPK_THREADS), 0, s, a);
   hipLaunchKernelGGL(topk_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, s, a);
   hipLaunchKernelGGL(topk_scatter_kernel, dim3(a.T), dim3(64), 0, s, a);
   hipLaunchKernelGGL(tile_logits_kernel, dim3(a.items_max), dim3(256), 0, s, a);
-  const PairSrc ps{a.cand_n, a.cand_tile, a.deg_rank, a.pair_z, a.C};
+  // the selection: a wave per row up to k = 32 (2 k candidates per lane in
+  // registers; for k = 64 the workgroup kernel measured faster)
+  const bool wave_sel = waves && a.k <= 32;
+  if (wave_sel) {
+    if (a.k <= 8)
+      hipLaunchKernelGGL(topk_select_wave_kernel<16>, dim3(wave_blocks), dim3(256), 0, s, a);
+    else if (a.k <= 16)
+      hipLaunchKernelGGL(topk_select_wave_kernel<32>, dim3(wave_blocks), dim3(256), 0, s, a);
+    else if (a.k <= 24)
+      hipLaunchKernelGGL(topk_select_wave_kernel<48>, dim3(wave_blocks), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(topk_select_wave_kernel<64>, dim3(wave_blocks), dim3(256), 0, s, a);
+  }
+  // the rows that need all their tiles (and, without the wave kernels, all rows)
+  const PairSrc ps{a.cand_n, a.cand_tile, a.deg_rank, a.pair_z, a.C, wave_sel ? 1 : 0};
   hipLaunchKernelGGL((topk_kernel<KC, true>), dim3(a.T), dim3(TOPK_THREADS), 0, s, nullptr,
                      (int64_t)0, a.lse, a.part_m, a.T, a.V, a.nST, a.k, a.inv_tau, a.bf16,
                      a.out_lp, a.out_id, ps);

@@ -53,7 +53,7 @@ def _rand(T, H, V, seed, dev, scale=1.0):
     return to_dev_bf16(h, dev), to_dev_bf16(w, dev), to_dev_i32(y, dev)
 
 
-@pytest.mark.parametrize("k", [1, 5, 8, 16, 17, 20, 33, 64])
+@pytest.mark.parametrize("k", [1, 5, 8, 9, 16, 17, 20, 24, 25, 32, 33, 64])
 def test_direct_equals_stored_tiny(tiny, k):
     _same(*_both(tiny.hidden, tiny.weight, tiny.targets, k), f"tiny k={k}")
 
@@ -76,7 +76,7 @@ def test_direct_equals_stored_options(tiny, inv_tau, bf16, k):
           f"1/tau={inv_tau} bf16={bf16} k={k}")
 
 
-@pytest.mark.parametrize("k", [1, 20, 64])
+@pytest.mark.parametrize("k", [1, 20, 32, 64])
 def test_direct_equals_stored_tied_tile_maxima(dev, k):
     """Coarse-grid operands: logits are multiples of 2^-8 over a small range,
     so many tiles share the same maximum and the first-k-by-index rule for
@@ -112,7 +112,7 @@ def _poisoned(dev, V=4096, H=128, T=8):
             to_dev_bf16(synth.f32_to_bf16_bits(w), dev), to_dev_i32(y, dev))
 
 
-@pytest.mark.parametrize("k", [4, 20])
+@pytest.mark.parametrize("k", [4, 20, 40])
 def test_direct_equals_stored_poisoned_rows(dev, k):
     h, w, y = _poisoned(dev)
     dl, di, sl, si = _both(h, w, y, k, dcap=8)
