@@ -15,6 +15,8 @@ of an existing file):
                    bound (2^-8 + (T + 16) 2^-24) (|dz|^T |h|) + 1e-6 computed
                    from the oracle's dz;
   prefill_options  logp, lse and entropy with inverse temperature 0.7;
+  prefill_topk     the 32 largest log-probabilities of every row and their ids
+                   (decreasing, ties to the smaller id);
   adversarial      T = 1024 coarse-grid rows: logp, lse;
   adversarial_sums per row, three exact integer checksums of the oracle's
                    logits q = 256 z (every coarse-grid logit is a multiple of
@@ -46,12 +48,13 @@ from oracle import oracle as orc  # noqa: E402
 
 OUT = os.path.join(HERE, "full_size_oracle.npz")
 DRY_OUT = "/tmp/full_size_oracle_dry.npz"
-PARTS = ("prefill", "prefill_gw", "prefill_options", "adversarial", "adversarial_sums",
-         "rollout")
+PARTS = ("prefill", "prefill_gw", "prefill_options", "prefill_topk", "adversarial",
+         "adversarial_sums", "rollout")
 ROLLOUT_CHUNK = 512
 GW_SEED = 15
 N_GW_ROWS = 24
 OPTIONS_INV_TAU = 0.7
+TOPK_STORED = 32
 
 
 def log(msg):
@@ -96,6 +99,15 @@ def part_prefill_options(c, out):
     lp, lse, ent = orc.selected_logp_ex(c.hidden, c.weight, c.targets, inv_tau=OPTIONS_INV_TAU)
     out["prefill_opt_inv_tau"] = np.array(OPTIONS_INV_TAU)
     out["prefill_opt_logp"], out["prefill_opt_lse"], out["prefill_opt_entropy"] = lp, lse, ent
+
+
+def part_prefill_topk(c, out, chunk=512):
+    lp = np.empty((c.T, TOPK_STORED))
+    ids = np.empty((c.T, TOPK_STORED), np.int32)
+    for r0 in range(0, c.T, chunk):
+        r1 = min(c.T, r0 + chunk)
+        lp[r0:r1], ids[r0:r1] = orc.topk_logp(c.hidden[r0:r1], c.weight, TOPK_STORED)
+    out["prefill_topk_logp"], out["prefill_topk_ids"] = lp, ids
 
 
 def part_adversarial(c, out):
@@ -154,7 +166,8 @@ def main(parts, dry=False):
         c = synth.prefill_case(**kw(128))
         out["prefill_fingerprint"] = np.array(synth.fingerprint(c))
         for p, fn in (("prefill", part_prefill), ("prefill_gw", part_prefill_gw),
-                      ("prefill_options", part_prefill_options)):
+                      ("prefill_options", part_prefill_options),
+                      ("prefill_topk", part_prefill_topk)):
             if p in parts:
                 t0 = time.time()
                 fn(c, out)

@@ -75,3 +75,39 @@ def test_backward_replays_bitwise(tiny):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(_bits(gh), _bits(ref_h)) and torch.equal(_bits(gw), _bits(ref_w))
+
+
+def test_direct_topk_replays_bitwise(prefill):
+    """The top-k path without stored logits (six launches, counters cleared
+    by a kernel and by its plan step) captured and replayed: each replay
+    gives the eager bits, with the workspace scribbled over in between."""
+    h, w, y = prefill.hidden[:512], prefill.weight, prefill.targets[:512]
+    T, V, k = 512, prefill.case.V, 20
+    ws = rlk.workspace_for(T, V, h.device)
+    _, lse = rlk.rlk_selected_logp(h, w, y, workspace=ws)
+    wsd = torch.empty(rlk.rlk_topk_logp_direct_workspace_bytes(T, V, k), dtype=torch.uint8,
+                      device=h.device)
+    tl = torch.empty((T, k), dtype=torch.float32, device=h.device)
+    ti = torch.empty((T, k), dtype=torch.int32, device=h.device)
+    ref_l, ref_i = rlk.rlk_topk_logp_direct(h, w, lse, ws, k)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        rlk.rlk_topk_logp_direct(h, w, lse, ws, k, workspace=wsd, topk_logp=tl, topk_ids=ti,
+                                 stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        rlk.rlk_topk_logp_direct(h, w, lse, ws, k, workspace=wsd, topk_logp=tl, topk_ids=ti,
+                                 stream=s)
+    for rep in range(4):
+        tl.fill_(np.nan)
+        ti.fill_(-7)
+        wsd.fill_(0xA5)                                   # stale counters and tables
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _ = (h[:16].float() @ w[:16].float().T).sum()     # unrelated eager work
+        assert torch.equal(ti, ref_i), f"replay {rep}"
+        assert torch.equal(_bits(tl), _bits(ref_l)), f"replay {rep}"
