@@ -36,6 +36,13 @@
 //                       order matters).
 //   topk_kernel         the k largest log-probabilities of a row from stored
 //                       logits (same options, same subtraction as the merge).
+//   topk_cand_*, topk_plan_kernel, topk_scatter_kernel, tile_logits_kernel,
+//   topk_select_wave_kernel
+//                       the same top-k without stored logits: each row's
+//                       candidate tiles, bucketed by tile, recomputed by the
+//                       logit GEMM's MFMA chain, then selected.
+//   transpose_kernel    h^T for the backward's product over the tokens
+//                       (64 x 64 tiles through LDS).
 //   compare_kernel      mismatch count / max |diff| / k3 of two fp32 arrays
 //                       (sections 六/七; the vLLM blog summary's diff = 0).
 //
