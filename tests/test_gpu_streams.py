@@ -45,3 +45,29 @@ def test_side_stream_without_workspace(prefill):
         assert torch.equal(lp.view(torch.int32), ref_lp.view(torch.int32))
         assert torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32))
         assert torch.equal(gh.view(torch.int32), ref_gh.view(torch.int32))
+
+
+def test_direct_topk_on_a_side_stream_without_workspace(prefill):
+    """The top-k path without stored logits allocates its pair buffers and
+    tables on the side stream (the plan's counters live there)."""
+    dev = prefill.hidden.device
+    h, w, y = prefill.hidden[:1024], prefill.weight, prefill.targets[:1024]
+    T, V, k = 1024, prefill.case.V, 20
+    ws = rlk.workspace_for(T, V, dev)
+    _, lse = rlk.rlk_selected_logp(h, w, y, workspace=ws)
+    ref_l, ref_i = rlk.rlk_topk_logp_direct(h, w, lse, ws, k)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        outs.append(rlk.rlk_topk_logp_direct(h, w, lse, ws, k, stream=side))
+        junk = torch.empty(rlk.rlk_topk_logp_direct_workspace_bytes(T, V, k), dtype=torch.uint8,
+                           device=dev)
+        junk.fill_(0x5A)
+        del junk
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for tl, ti in outs:
+        assert torch.equal(ti, ref_i)
+        assert torch.equal(tl.view(torch.int32), ref_l.view(torch.int32))

@@ -152,6 +152,12 @@ def test_direct_equals_stored_prefill(prefill, k):
     _same(*_both(prefill.hidden, prefill.weight, prefill.targets, k), f"prefill k={k}")
 
 
+def test_direct_equals_stored_rollout(rollout):
+    """The long rollout (T = 16384 packed rows), k = 20 and 64."""
+    for k in (20, 64):
+        _same(*_both(rollout.hidden, rollout.weight, rollout.targets, k), f"rollout k={k}")
+
+
 def test_direct_error_paths(tiny):
     h, w, y = tiny.hidden, tiny.weight, tiny.targets
     T, V = h.shape[0], w.shape[0]
