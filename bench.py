@@ -459,9 +459,27 @@ def time_variants(rlk, torch, np, hidden, weight, targets, T, H, V, steps, flops
 
         dr = timed(direct)
         del ws_d
+        # the two paths' entries, bit for bit
+        z = torch.empty((T, V), dtype=torch.float32, device=dev)
+        rlk.rlk_logits(hidden, weight, logits=z)
+        sl, si = rlk.rlk_topk_logp(z, lse_t, ws_t, 20)
+        del z
+        dl, di = rlk.rlk_topk_logp_direct(hidden, weight, lse_t, ws_t, 20)
+        torch.cuda.synchronize()
+        mism = int(((di != si) | (dl.view(torch.int32) != sl.view(torch.int32))).sum().item())
+
+        # context: the vendor route, torch's bf16 linear layer then torch.topk of
+        # the log-softmax (not batch-invariant; ties in its own order)
+        def vendor():
+            zz = torch.nn.functional.linear(hidden, weight).float()
+            torch.topk(torch.log_softmax(zz, dim=1), 20, dim=1)
+
+        vd = timed(vendor)
         out["topk20"] = {"logits_store_ms": lg, "select_ms": sel,
                          "select_GB/s": 4.0 * T * V / (sel * 1e-3) / 1e9,
-                         "direct_ms": dr, "direct_vs_stored": (lg + sel) / dr}
+                         "direct_ms": dr, "direct_vs_stored": (lg + sel) / dr,
+                         "direct_vs_stored_mismatches": mism,
+                         "vendor_linear_topk_ms": vd}
 
     if "long_rollout" in only:
         # 16384 rows (32 responses x 512 tokens) through the same path
