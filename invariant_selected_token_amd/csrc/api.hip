@@ -508,7 +508,10 @@ TopkLayout topk_layout(int64_t T, int64_t V, int64_t k, int64_t dcap) {
   const int64_t nST = ceil_div(V, rlk::STAT_V);
   if (nST <= k) dcap = 0;   // such rows use their own k slots
   L.P = T * k + dcap * nST;
-  L.items_max = (L.P + 127) / 128 + nST;   // work items of up to 128 pairs per tile
+  // work items of up to 128 pairs of a tile (256 when k > 32: about twice
+  // the pairs per tile, the weights then streamed once per tile)
+  const int64_t per_item = k > 32 ? 256 : 128;
+  L.items_max = (L.P + per_item - 1) / per_item + nST;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -606,6 +609,7 @@ int rlk_topk_logp_direct(const void *hidden, int64_t ld_hidden, const void *weig
   a.k = k;
   a.C = k;
   a.dcap = (int)max_degenerate_rows;
+  a.tl_pairs = k > 32 ? 256 : 128;
   a.items_max = (int)L.items_max;
   return hip_status(rlk::launch_topk_direct(a, static_cast<hipStream_t>(stream)));
 }

@@ -141,6 +141,7 @@ struct TopkDirectArgs {
   float inv_tau;
   int bf16;
   int T, H, V, nST, k, C, dcap;
+  int tl_pairs;   // pairs per work item of the tile logits: 128 (4 waves), 256 (8 waves)
   int items_max;
 };
 hipError_t launch_topk_direct(const TopkDirectArgs &a, hipStream_t s);

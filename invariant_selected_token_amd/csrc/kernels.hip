@@ -1868,12 +1868,9 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_cand_kernel(const TopkDirec
   if (tid == 0) a.cand_n[t] = na + (taken < need ? taken : need);
 }
 
-// Pairs per work item of the tile-logits kernel: 4 waves of 32.
-constexpr int TL_PAIRS = 128;
-
 // 2) one workgroup: room for the rows with m* = -inf (the first dcap in row
 //    order, when nST > C), then per tile its pair count, its first pair slot
-//    and its work items (TL_PAIRS pairs each, in tile order), and the tile of every
+//    and its work items (a.tl_pairs pairs each, in tile order), and the tile of every
 //    work item.
 constexpr int PLAN_THREADS = 1024;
 __global__ __launch_bounds__(PLAN_THREADS) void topk_plan_kernel(const TopkDirectArgs a) {
@@ -1922,7 +1919,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void topk_plan_kernel(const TopkDirec
     const int c = j < a.nST ? a.tile_count[j] + served : 0;
     int tp, ti;
     const int op = scan(c, tp);
-    const int oi = scan((c + TL_PAIRS - 1) / TL_PAIRS, ti);
+    const int oi = scan((c + a.tl_pairs - 1) / a.tl_pairs, ti);
     if (j < a.nST) {
       a.tile_count[j] = c;
       a.tile_off[j] = carry_p + op;
@@ -1961,24 +1958,28 @@ __global__ __launch_bounds__(64) void topk_scatter_kernel(const TopkDirectArgs a
   }
 }
 
-// 4) one workgroup per work item: the 128 x (up to 128) logits of one tile
-//    for up to TL_PAIRS of its pairs, wave w taking pairs 32 w .. 32 w + 31.
+// 4) one workgroup of NW waves per work item: the 128 x (up to 32 NW) logits
+//    of one tile for up to a.tl_pairs = 32 NW of its pairs, wave w taking
+//    pairs 32 w .. 32 w + 31 (NW = 8 when k > 32: a tile then holds about
+//    twice as many pairs, and one item streams its weights once).
 //    The tile's weight block (128 rows x 64 K, 16 KiB) goes to LDS by
-//    direct-to-LDS loads, double-buffered and shared by the 4 waves, in the
+//    direct-to-LDS loads, double-buffered and shared by the waves, in the
 //    logit GEMM's layout (16-byte chunk c of row r at c ^ swz(r); load q of
-//    wave w fills rows 8 (4 q + w) .. + 7); each lane loads its pair's hidden
+//    wave w fills rows 8 (NW q + w) .. + 7); each lane loads its pair's hidden
 //    row straight into the MFMA operand layout (row l & 31, K slice 8 (l >> 5)
 //    .. + 7 of each 16-deep step), one block ahead.  Rows past V read zeros
 //    through the resource's range.
-__global__ __launch_bounds__(256) void tile_logits_kernel(const TopkDirectArgs a) {
-  __shared__ __attribute__((aligned(16))) char wlds[2][TILE_K * STAT_V * 2];
+typedef char TileStage[TILE_K * STAT_V * 2];
+template <int NW>
+__device__ __forceinline__ void tile_logits_body(const TopkDirectArgs &a, TileStage *wlds) {
+  constexpr int LQ = 16 / NW;   // 1 KiB weight loads per wave and K block
   const int it = blockIdx.x;
   if (it >= a.totals[0]) return;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, r = l & 31, fk = l >> 5;
   const int j = a.item_tile[it];
-  const int first = a.tile_off[j] + TL_PAIRS * (it - a.item_off[j]) + 32 * wave;
+  const int first = a.tile_off[j] + 32 * NW * (it - a.item_off[j]) + 32 * wave;
   const int cnt = min(32, a.tile_off[j] + a.tile_count[j] - first);   // <= 0: an idle wave
   const int p = r < cnt ? a.bucket[first + r] : -1;
   const int regular = a.T * a.C;
@@ -1990,20 +1991,21 @@ __global__ __launch_bounds__(256) void tile_logits_kernel(const TopkDirectArgs a
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(
       a.weight + (size_t)v0 * a.ldw, (uint32_t)(min(STAT_V, a.V - v0) * a.ldw * 2));
   typedef __attribute__((address_space(3))) void lds_void;
-  // load q of this wave: row 8 (4 q + wave) + (l >> 3), global chunk (l & 7) ^ swz(row)
-  uint32_t gofs[4];
+  // load q of this wave: row 8 (NW q + wave) + (l >> 3), global chunk (l & 7) ^ swz(row)
+  uint32_t gofs[LQ];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int row = 8 * (4 * q + wave) + (l >> 3);
+  for (int q = 0; q < LQ; ++q) {
+    const int row = 8 * (NW * q + wave) + (l >> 3);
     gofs[q] = (uint32_t)(row * a.ldw * 2 + (((l & 7) ^ swz(row)) << 4));
   }
   auto wload = [&](int kb, int st) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < LQ; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rw, (lds_void *)(&wlds[st][0] + (4 * q + wave) * 1024), 16, gofs[q],
+          rw, (lds_void *)(&wlds[st][0] + (NW * q + wave) * 1024), 16, gofs[q],
           (uint32_t)kb * (TILE_K * 2), 0, 0);
   };
+
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
   // (a lane without a pair loads row 0 and zeroes it where it is used, so
   // that no wait for the load comes before the next block)
@@ -2243,6 +2245,21 @@ __global__ __launch_bounds__(256) void topk_select_wave_kernel(const TopkDirectA
   }
 }
 
+// (the kernels wrap the body: a template kernel with this body itself left
+// its host-side launch stubs unemitted)
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void tile_logits_kernel(const TopkDirectArgs a) {
+  __shared__ __attribute__((aligned(16))) TileStage wlds[2];
+  tile_logits_body<NW>(a, wlds);
+}
+
+void launch_tile_logits(const TopkDirectArgs &a, hipStream_t s) {
+  if (a.tl_pairs == 256)
+    hipLaunchKernelGGL((tile_logits_kernel<8>), dim3(a.items_max), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((tile_logits_kernel<4>), dim3(a.items_max), dim3(256), 0, s, a);
+}
+
 template <int KC>
 void launch_topk_direct_kc(const TopkDirectArgs &a, hipStream_t s) {
   const int wave_blocks = ceil_div(a.T, 4);
@@ -2255,7 +2272,7 @@ void launch_topk_direct_kc(const TopkDirectArgs &a, hipStream_t s) {
     hipLaunchKernelGGL((topk_cand_kernel<KC>), dim3(a.T), dim3(TOPK_THREADS), 0, s, a);
   hipLaunchKernelGGL(topk_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, s, a);
   hipLaunchKernelGGL(topk_scatter_kernel, dim3(a.T), dim3(64), 0, s, a);
-  hipLaunchKernelGGL(tile_logits_kernel, dim3(a.items_max), dim3(256), 0, s, a);
+  launch_tile_logits(a, s);
   // the selection: a wave per row up to k = 32 (2 k candidates per lane in
   // registers; for k = 64 the workgroup kernel measured faster)
   const bool wave_sel = waves && a.k <= 32;

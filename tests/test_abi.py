@@ -571,7 +571,8 @@ def test_topk_direct_workspace_size():
         nst = (V + 127) // 128
         d = d if nst > k else 0
         P = T * k + d * nst
-        items = (P + 127) // 128 + nst
+        per_item = 256 if k > 32 else 128
+        items = (P + per_item - 1) // per_item + nst
         want = (r(P * 512) + r(P * 4) + r(T * k * 4) + 2 * r(T * 4) + r(max(d, 1) * 4)
                 + 3 * r(nst * 4) + r((nst + 1) * 4) + r(items * 4) + r(16))
         assert wb(T, V, k, d) == want, (T, V, k, d)
