@@ -69,6 +69,7 @@ namespace rlk {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int STAGE_BYTES = TILE_V * TILE_K * 2;  // one operand, one stage
@@ -135,14 +136,21 @@ __device__ __forceinline__ void tile_of_logical(int L, int nMT, int nVT, int &m,
 }
 
 // LDS layout of one operand stage: 256 rows x 64 bf16 (128 bytes per row);
-// the 16-byte chunk c of row r sits at chunk position c ^ swz(r) with
-// swz(r) = (r & 7) ^ ((r >> 3) & 1).  A fragment read has 32 consecutive
-// lanes on 32 consecutive rows and one chunk; with this swizzle any 8
-// consecutive rows (aligned) use 8 distinct positions of a 128-byte bank
-// window, and any 16 (aligned) use 16 distinct 16-byte slots of a 256-byte
-// window, so ds_read_b128 is free of bank conflicts whether the LDS serves it
-// 8 or 16 lanes per cycle.
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// the 16-byte chunk c of row r sits at chunk position c ^ swz(r), where
+// swz(r) = 4 r2 + r1 + 2 (r0 ^ r3) in the bits r3 r2 r1 r0 of r & 15.  A
+// fragment read (ds_read_b128) has lanes 16 g + x on row x (16 consecutive
+// rows) and chunk c0 + g.  The counters show the LDS serving lanes l and
+// l + 32 in the same cycle: lanes x and x + 32 read one row's chunks c0 and
+// c0 ^ 2.  swz maps each aligned octet of rows to 8 distinct positions, the
+// even (and the odd) rows of an octet to four positions that differ in more
+// than bit 1 (so chunks c and c ^ 2 of them never meet), and the 8 even (odd)
+// rows of 16 to 8 distinct positions: the reads are free of bank conflicts
+// whether the LDS serves 8 consecutive lanes (128-byte window), 16
+// consecutive lanes, or lanes l .. l + 7 with l + 32 .. l + 39 (256-byte
+// window) per cycle.
+__device__ __forceinline__ int swz(int row) {
+  return 4 * ((row >> 2) & 1) + ((row >> 1) & 1) + 2 * ((row & 1) ^ ((row >> 3) & 1));
+}
 
 // ds_read_b64_tr_b16 through a restrict-qualified pointer: inlined, the
 // call then carries alias-scope information like the kernel's other LDS
@@ -173,18 +181,18 @@ __device__ __forceinline__ bf16x4 tr_read(const lds_bf16x4 *__restrict__ p) {
 template <bool STATS, bool PERSIST, int EX, bool KMW>
 __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   static_assert(!(STATS && KMW), "the statistics pass reads K-contiguous operands");
-  constexpr int NJ = 4;         // token blocks of 32 rows per wave
-  constexpr int TT = 64 * NJ;   // token rows of a tile (TILE_T)
-  constexpr int WT = 32 * NJ;   // token rows of a wave
-  constexpr int NQ = 4 * NJ;    // MFMAs per wave and K step
-  constexpr int NR = 4 + NJ;    // fragment reads per wave and K step
+  constexpr int NI = 8;         // vocabulary blocks of 16 rows per wave
+  constexpr int NJ = 8;         // token blocks of 16 rows per wave
+  constexpr int TT = 32 * NJ;   // token rows of a tile (TILE_T)
+  constexpr int WT = 16 * NJ;   // token rows of a wave
+  constexpr int NQ = NI * NJ;   // MFMAs per wave and 32-deep K step
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
   const int wv = wave & 1;   // vocabulary half of the tile
   const int wt = wave >> 1;  // token half of the tile
-  // Lane-dependent values (MFMA row fr = lane & 31, K slice fk = lane >> 5,
-  // load and read offsets) are formed where they are used, from a fresh
-  // lane id, so that none is live across both the K loop and the epilogue.
+  // Lane-dependent values (MFMA row lane & 15, K slice lane >> 4, load and
+  // read offsets) are formed where they are used, from a fresh lane id, so
+  // that none is live across both the K loop and the epilogue.
 
   const int total = a.nMT * a.nVT;
   // Dynamic tile claims (when the host passes a.queue):
@@ -231,7 +239,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   // LDS slot base + 16 * lane).  Load i of wave w fills the 1 KiB block
   // b = 4 i + w of a stage, i.e. rows 8 b .. 8 b + 7; lane l supplies row
   // 8 b + (l >> 3) and, because of the swizzle, global chunk
-  // (l & 7) ^ swz(row) = (l & 7) ^ (l >> 3) ^ (w & 1) of that row.  The K
+  // (l & 7) ^ swz(row) of that row.  The K
   // offset of the block rides in the scalar offset; rows past T or V fall
   // outside the tile's resource and read 0.
   //
@@ -366,26 +374,35 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     }
   };
 
-  // Fragment reads: A (weight) rows wv*128 + 32 i + fr, B (hidden) rows
-  // wt*128 + 32 j + fr, 16-byte chunk 2 ks + fk of the 64-wide K step.  Byte
-  // addresses per (stage, ks); the block index i or j adds i * 4096.
+  // MFMA v_mfma_f32_16x16x32_bf16: a 16 x 16 block of outputs from 16
+  // A rows and 16 B rows over 32 K.  Lane l supplies 8 consecutive K
+  // values, 8 (l >> 4) .. + 7, of A row l & 15 and of B row l & 15, and
+  // receives outputs (A row 4 (l >> 4) + r, B row l & 15), r = 0 .. 3.
+  // Each wave covers its 128 x 128 outputs as 8 x 8 such blocks.
+  //
+  // Fragment reads: A (weight) rows wv*128 + 16 i + (l & 15), B (hidden)
+  // rows wt*128 + 16 j + (l & 15), 16-byte chunk 4 s + (l >> 4) of K step s
+  // (0, 1) of the 64-wide block.  swz(16 i + x) == swz(x), so the byte
+  // address is a lane base per (stage, s) plus i * 2048.
   //
   // A K-major weight stage holds 64 depth rows k x 256 columns c (32 chunks
   // of 8 columns) as 128 lines of 256 bytes: chunk c of row k sits in line
   // 8 (k >> 2) + (c >> 2), 16-byte slot 2 (k & 3) + (c & 1) +
-  // 8 ((c >> 1) & 1).  The MFMA operand of a 32-column block and a 16-deep
-  // K step is two transposing reads (ds_read_b64_tr_b16: in each group of 16
-  // lanes, lane 4 r + s supplies columns 4 s .. 4 s + 3 of row r, and lane i
-  // receives column i of the 4 rows): lane l = 16 g + L reads row
-  // 16 ks + 8 (g >> 1) + 4 h + (L >> 2) (h = 0, 1), columns 16 (g & 1) +
-  // 4 (L & 3) of the block.  With this layout the 16 lanes of a group meet
-  // 32 distinct banks and any 32 lanes 64, and a read's address is a lane
-  // base plus 8192 ks + 2048 h + 256 block: immediate offsets only.  Load i
-  // of wave w fills lines 4 b .. 4 b + 3, b = 4 i + w (rows 4 (b >> 1) ..
-  // + 3, 256 contiguous bytes of each): lane l fetches row 4 (b >> 1) +
-  // ((l >> 1) & 3), chunk 16 (b & 1) + 4 (l >> 4) + 2 ((l >> 3) & 1) + (l & 1).
-  uint32_t ra[2][4], rb[2][4];
-  uint32_t kma[2];   // K-major weight: lane base per stage
+  // 8 (((c >> 1) & 1) ^ ((k >> 3) & 1)).  The MFMA operand of a 16-column
+  // block and a 32-deep K step is two transposing reads (ds_read_b64_tr_b16:
+  // in each group of 16 lanes, lane 4 r + s supplies columns 4 s .. 4 s + 3
+  // of row r, and lane i receives column i of the 4 rows): the lanes of
+  // group g = l >> 4 read rows 32 s + 8 g + 4 h + 0 .. 3 (h = 0, 1) as one
+  // contiguous 128-byte piece, at lane base + 16384 s + 2048 h + 256 (i >> 1)
+  // (immediate offsets; the base differs by the parity of i).  The XOR with
+  // (k >> 3) & 1 puts groups g and g + 1 in different halves of a 256-byte
+  // bank window, so each read is free of bank conflicts.  Load i of wave w
+  // fills lines 4 b .. 4 b + 3, b = 4 i + w (rows 8 i + 4 (w >> 1) .. + 3,
+  // 256 contiguous bytes of each): lane l fetches row 8 i + 4 (w >> 1) +
+  // ((l >> 1) & 3), chunk 16 (w & 1) + 4 (l >> 4) + 2 (((l >> 3) & 1) ^
+  // (i & 1)) + (l & 1).
+  uint32_t ra[2][2], rb[2][2];
+  uint32_t kma[2][2];   // K-major weight: lane base per stage and parity of i
   // The per-lane offsets of the loads, the prefetch and the fragment reads,
   // formed at the start of every tile from a lane id the compiler cannot
   // merge with an earlier one: they are then dead during the epilogue
@@ -394,12 +411,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     int l;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
     const int lrow = 8 * wave + (l >> 3);
-    const int lchunk = (l & 7) ^ (l >> 3) ^ (wave & 1);
-    // K-major: row 8 i + kmrow, chunk kmchunk of the block (b = 4 i + wave)
+    const int lchunk = (l & 7) ^ swz(lrow);   // swz(lrow + 32 i) == swz(lrow)
     const int kmrow = 4 * (wave >> 1) + ((l >> 1) & 3);
-    const int kmchunk = 16 * (wave & 1) + 4 * (l >> 4) + 2 * ((l >> 3) & 1) + (l & 1);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+      const int kmchunk =
+          16 * (wave & 1) + 4 * (l >> 4) + 2 * (((l >> 3) & 1) ^ (i & 1)) + (l & 1);
       gofs[0][i] = KMW ? (uint32_t)((8 * i + kmrow) * a.ldw * 2 + kmchunk * 16)
                        : (uint32_t)((lrow + 32 * i) * a.ldw * 2 + lchunk * 16);
       gofs[1][i] = (uint32_t)((lrow + 32 * i) * a.ldh * 2 + lchunk * 16);
@@ -409,116 +426,131 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     pofs_w = KMW ? (uint32_t)((16 * wave + (l >> 2)) * a.ldw * 2 + (l & 3) * 128)
                  : (uint32_t)(prow * a.ldw * 2);
     pofs_h = (uint32_t)(prow * a.ldh * 2);
+    const int lr = l & 15, lg = l >> 4;
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
-      kma[st] = st * (2 * STAGE_BYTES) + 4096 * (l >> 5) + 128 * ((l >> 4) & 1) + 8 * (l & 15) +
-                1024 * wv;
-    const int lr = l & 31, lk = l >> 5;
+    for (int st = 0; st < 2; ++st) {
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+      for (int ip = 0; ip < 2; ++ip)
+        kma[st][ip] = st * (2 * STAGE_BYTES) + 4096 * lg + 1024 * wv + 8 * lr +
+                      128 * (ip ^ (lg & 1));
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        // swz(32 i + fr) == swz(fr)
-        const uint32_t x = (uint32_t)(((2 * ks + lk) ^ swz(lr)) << 4);
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint32_t x = (uint32_t)(((4 * ks + lg) ^ swz(lr)) << 4);
         ra[st][ks] = st * (2 * STAGE_BYTES) + (wv * 128 + lr) * 128 + x;
         rb[st][ks] = st * (2 * STAGE_BYTES) + STAGE_BYTES + (wt * WT + lr) * 128 + x;
       }
-  };
-  bf16x8 fa[2][4], fb[2][NJ];
-  // A fragment, block i of K step ks (K-major: two transposing reads)
-  auto reada = [&](int st, int ks, int i) -> bf16x8 {
-    if constexpr (KMW) {
-      lds_char *p = (lds_char *)smem + kma[st] + 8192 * ks + 256 * i;
-      const bf16x4 lo = tr_read((const lds_bf16x4 *)p);
-      const bf16x4 hi = tr_read((const lds_bf16x4 *)(p + 2048));
-      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    } else {
-      return *(const bf16x8 *)(smem + ra[st][ks] + i * 4096);
     }
   };
-  // Read number w (0 .. NR-1) of the fragments of (stage, ks) into set `buf`,
-  // in the order the MFMAs consume them: A0, B0 .. B(NJ-1), A1, A2, A3.
-  auto fread = [&](int buf, int st, int ks, int w) {
-    if (w == 0) fa[buf][0] = reada(st, ks, 0);
-    else if (w <= NJ) fb[buf][w - 1] = *(const bf16x8 *)(smem + rb[st][ks] + (w - 1) * 4096);
-    else fa[buf][w - NJ] = reada(st, ks, w - NJ);
+  // A fragments: one set, each refilled for the next K step once its own
+  // MFMAs are issued; B fragments: two sets, one per K step.
+  bf16x8 fa[NI], fb[2][NJ];
+  // A fragment, block i of K step ks (K-major: two transposing reads)
+  auto reada = [&](int st, int ks, int i) {
+    if constexpr (KMW) {
+      lds_char *p = (lds_char *)smem + kma[st][i & 1] + 16384 * ks + 256 * (i >> 1);
+      const bf16x4 lo = tr_read((const lds_bf16x4 *)p);
+      const bf16x4 hi = tr_read((const lds_bf16x4 *)(p + 2048));
+      fa[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+      fa[i] = *(const bf16x8 *)(smem + ra[st][ks] + i * 2048);
+    }
   };
-  f32x16 acc[4][NJ];
-  // MFMA q of a K step: A block i = q / NJ, B (token) block j = q % NJ
+  auto readb = [&](int buf, int st, int ks, int j) {
+    fb[buf][j] = *(const bf16x8 *)(smem + rb[st][ks] + j * 2048);
+  };
+  f32x4 acc[NI][NJ];
+  // MFMA q of a K step: A block i = q / 8 with the eight B blocks in turn,
+  // so A_i is used by MFMAs 8 i .. 8 i + 7 (an operand held for eight
+  // MFMAs in a row toggles the matrix core's inputs less: measured, the
+  // clock the kernel holds at the power limit is ~1.5 % higher than with A
+  // held for four).  In inline assembly: the builtin of this instruction gets its
+  // accumulator copied between registers on every use by this compiler,
+  // while the assembly form keeps each accumulator in place.  The compiler
+  // does not see an MFMA here, so the tile supplies the wait states it
+  // would insert (after zeroing the accumulators and before reading them,
+  // below).
   auto mfma = [&](int buf, int q) {
-    const int i = q / NJ, j = q % NJ;
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j],
-                                                       0, 0, 0);
+    const int i = q >> 3, j = q & 7;
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                 : "+a"(acc[i][j])
+                 : "v"(fa[i]), "v"(fb[buf][j]));
   };
 
-  // One K block of the main loop.  Each accumulator advances in increasing k
-  // (16 per MFMA); the fixed instruction order below only decides what
-  // overlaps with what.  Each of the first eight of the 16 MFMAs of step ks
-  // is followed by one read of step ks + 1's fragments, and every second
-  // MFMA of steps 0 and 1 (the odd ones) by one direct-to-LDS load of the
-  // next K block, so the sixteen loads are issued early but never in bursts
-  // (a burst stalls the wave's in-order issue, and with it the next MFMA,
-  // until the texture path takes the load); step 2 issues the L2 prefetch.
-  // Half-way through step 3 the wave waits for its loads and the workgroup
-  // meets at the barrier (the next block has landed; this block is no longer
-  // read), then the next block's first fragments are read under the last
-  // eight MFMAs.  The tile's last block (MORE false) has no next block of its
-  // own: its load slots carry the next tile's first block into the other
-  // stage (r_w, r_h, p_w then name the next tile), which is free once the
-  // barrier of the block before has passed.  p_w and kp name the weight
+  // One K block of the main loop: two 32-deep K steps of 64 MFMAs.  Each
+  // accumulator advances in increasing k (32 per MFMA); the fixed
+  // instruction order below only decides what overlaps with what.  The
+  // fragment reads are spread one per two to four MFMAs (a burst of them
+  // queues in the LDS, and the MFMAs wait):
+  //   Step 0 (B set 0): behind MFMAs 1, 5, 9, 13 this step's A_4-7 (the
+  //   block before read only what its first MFMAs need); behind 17, 21, ..,
+  //   45 step 1's B_0-7 (set 1); behind 8 i + 10 (i < 6) and 58 step 1's
+  //   A_i, i < 7 (each after its last use here, MFMA 8 i + 7); behind every
+  //   third MFMA (1, 4, .., 46) one direct-to-LDS load of the next K block,
+  //   so the sixteen loads are issued early (the barrier that waits for them
+  //   comes 1.5 steps later) but never in bursts (a burst stalls the wave's
+  //   in-order issue, and with it the next MFMA, until the texture path
+  //   takes the load).
+  //   Step 1 (B set 1): behind MFMA 2 its A_7, behind 16 the L2 prefetch;
+  //   after MFMA 31 the wave waits for its loads and the workgroup meets at
+  //   the barrier (the next block has landed; this block is no longer read);
+  //   then behind 33, 35, .., 47 the next block's B_0-7 (set 0) and behind
+  //   34, 38, 42, 46 its A_0-3 (last used here at MFMA 31 or before).
+  // The loads fetch K block kl of (r_w, r_h) into the other stage: kb + 1
+  // of this tile, and in the tile's last block block 0 of the next tile
+  // (r_w, r_h then name the next tile; the other stage is free once the
+  // barrier of the block before has passed).  p_w and kp name the weight
   // block the L2 prefetch fetches: kb + 1 + PREFETCH_AHEAD of this tile, and
-  // in the last two blocks the next tile's blocks 0 and 1.
-  auto k_block = [&](int kb, auto stage, auto more, HW r_w, __amdgpu_buffer_rsrc_t r_h,
-                     HW p_w, __amdgpu_buffer_rsrc_t p_h, int kp) {
+  // in the last two blocks the next tile's blocks 0 and 1.  Every block,
+  // the last included, meets the barrier and reads the next block's first
+  // fragments (in the last block those of the next tile's first block, which
+  // the next tile reads again after its epilogue).
+  auto k_block = [&](int kb, auto stage, int kl, HW r_w, __amdgpu_buffer_rsrc_t r_h, HW p_w,
+                     __amdgpu_buffer_rsrc_t p_h, int kp, bool sync) {
     constexpr int st = decltype(stage)::value;    // == kb & 1
-    constexpr bool MORE = decltype(more)::value;  // not the last K block
-    const int kl = MORE ? kb + 1 : 0;             // K block the loads fetch
     uint32_t s_w;
     const __amdgpu_buffer_rsrc_t b_w = src_w(r_w, kl, s_w);
     asm volatile("" : "+s"(lds_wave));
 #pragma unroll
-    for (int ks = 0; ks < 3; ++ks) {
-      const int cur = ks & 1;
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        mfma(cur, q);
-        if (q < NR) fread(cur ^ 1, st, ks + 1, q);
-        if (ks < 2) {
-          // eight loads per step, one behind every odd MFMA
-          if (q & 1) gload(b_w, s_w, r_h, st ^ 1, kl, 8 * ks + (q >> 1));
-        } else if (ks == 2 && q == NQ / 2) {
-          prefetch(p_w, kp);
-          if constexpr (!STATS) prefetch_h(p_h, kp);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int q = 0; q < NQ; ++q) {
+      mfma(0, q);
+      if (q < 16 && (q & 3) == 1) reada(st, 0, 4 + (q >> 2));
+      if (q >= 17 && q <= 45 && (q & 3) == 1) readb(1, st, 1, (q - 17) >> 2);
+      if (q >= 10 && q <= 50 && (q & 7) == 2) reada(st, 1, (q - 10) >> 3);
+      if (q == 58) reada(st, 1, 6);
+      if (q < 48 && q % 3 == 1) gload(b_w, s_w, r_h, st ^ 1, kl, q / 3);
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int q = 0; q < NQ / 2; ++q) {
       mfma(1, q);
+      if (q == 2) reada(st, 1, 7);
+      if (q == 16) {
+        prefetch(p_w, kp);
+        if constexpr (!STATS) prefetch_h(p_h, kp);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (MORE) {
-      // This wave's loads of the next block have landed (only the
-      // prefetch issued after them may still be in flight) and its reads of
-      // this block are complete; then the workgroup barrier.  A plain
-      // s_barrier, not a fenced __syncthreads(), so that the prefetch is not
-      // waited for; the empty asm statements keep the compiler from moving
-      // memory accesses across it.
-      asm volatile("" ::: "memory");
+    // This wave's loads of the next block have landed (only the prefetch
+    // issued after them may still be in flight) and its reads of this block
+    // are complete; then the workgroup barrier.  A plain s_barrier, not a
+    // fenced __syncthreads(), so that the prefetch is not waited for; the
+    // empty asm statements keep the compiler from moving memory accesses
+    // across it.  The tile's last block (sync false) skips both: its loads
+    // (the next tile's first block) are waited for after the epilogue, at
+    // the next tile's start, so that their latency hides under the
+    // epilogue, and what it reads below is read again there.
+    asm volatile("" ::: "memory");
+    if (sync) {
       __builtin_amdgcn_s_waitcnt(STATS ? VMCNT1_LGKMCNT0 : VMCNT2_LGKMCNT0);
       __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
     }
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int q = NQ / 2; q < NQ; ++q) {
       mfma(1, q);
-      if (MORE && q - NQ / 2 < NR) fread(0, st ^ 1, 0, q - NQ / 2);
+      if (q < 48 && (q & 1) == 1) readb(0, st ^ 1, 0, (q - 33) >> 1);
+      if (q < 48 && (q & 3) == 2) reada(st ^ 1, 0, (q - 34) >> 2);
       __builtin_amdgcn_sched_barrier(0);
-    }
-    if (MORE) {
-#pragma unroll
-      for (int w = NQ / 2; w < NR; ++w) fread(0, st ^ 1, 0, w);
     }
   };
 
@@ -556,14 +588,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   issue_first(rw, rh, pw, ph);
 
   for (;;) {
-    const HW rw_last = (nk & 1) ? zero_w() : rw;
-    const __amdgpu_buffer_rsrc_t rh_last = (nk & 1) ? zero : rh;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     set_offsets();
     if (dyn && threadIdx.x == 0) claimed[parity ^ 1] = claim();   // the next tile
     // The tile's first block (issued by the previous tile's last K block, or
@@ -571,43 +599,80 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     __builtin_amdgcn_s_waitcnt(VMCNT0);
     __syncthreads();
 #pragma unroll
-    for (int w = 0; w < NR; ++w) fread(0, 0, 0, w);
+    for (int x = 0; x < 8; ++x) {
+      if (x < 4) reada(0, 0, x);
+      readb(0, 0, 0, x);
+    }
     // The logit gradient's per-row inputs (lse, upstream gradient), loaded
     // now so that their latency hides under the first K block: issued in the
     // epilogue they would wait behind the next tile's operand loads (vector
     // memory completes in order).
-    float lse_r[4] = {0.0f, 0.0f, 0.0f, 0.0f}, grad_r[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float lse_r[NJ], grad_r[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) lse_r[j] = grad_r[j] = 0.0f;
     if constexpr (EX == 3) {
       int l;
       asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = m * TT + wt * WT + 32 * j + (l & 31);
+      for (int j = 0; j < NJ; ++j) {
+        const int t = m * TT + wt * WT + 16 * j + (l & 15);
         if (t < a.T) {
           lse_r[j] = a.lse[t];
           grad_r[j] = a.grad[t];
         }
       }
     }
-    for (int kb = 0; kb + 2 < nk2; kb += 2) {
-      k_block(kb, S0{}, std::true_type{}, rw, rh, pw, ph, kb + 1 + PREFETCH_AHEAD);
-      k_block(kb + 1, S1{}, std::true_type{}, rw, rh, pw, ph, kb + 2 + PREFETCH_AHEAD);
-    }
-    // The next tile (its first two weight blocks are prefetched by the last
-    // two blocks of this one) and its targets; the last block loads its
-    // first block into stage 0.  After the last tile those loads and
-    // prefetches go through the zero-size resource and read nothing.
+    // Wait states between the accumulators' zeroing (VALU writes) and the
+    // first MFMA that reads them.
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 4");
+    __builtin_amdgcn_sched_barrier(0);
+    // The next tile (scalars; its resources are formed in the last K pair).
     const int Ln = dyn ? claimed[parity ^ 1] : PERSIST ? L + (int)gridDim.x : total;
     const bool more_tiles = dyn ? Ln >= 0 : Ln < total;
     int mn = m, nn = n;
     if (more_tiles) coords(Ln, mn, nn);
-    const HW rwn = more_tiles ? rsrc_w(nn) : zero_w();
-    const __amdgpu_buffer_rsrc_t rhn = more_tiles ? rsrc_h(mn) : zero;
-    const HW pwn = pf_rsrc(mn, rwn);
-    const __amdgpu_buffer_rsrc_t phn = pfh_rsrc(rhn);
-    k_block(nk2 - 2, S0{}, std::true_type{}, rw_last, rh_last, pwn, phn, 0);
-    stage_targets(mn, parity ^ 1);   // after the last tile: its own, unused
-    k_block(nk2 - 1, S1{}, std::false_type{}, rwn, rhn, pwn, phn, 1);
+    // Every K block in one loop (no copy of the K-block code after it: the
+    // register copies a compiler may place between such copies would sit
+    // next to MFMAs whose wait states it does not know about).  K blocks run
+    // in pairs (stage 0, stage 1).  In the last pair the loads of the second
+    // block (a zero block when H / 64 is odd) and of the next tile's first
+    // block, and the L2 prefetches of the next tile's first two weight
+    // blocks, take their resources from the next tile (after the last tile,
+    // the zero-size resource: they read nothing).
+    for (int kb = 0; kb < nk2; kb += 2) {
+      const bool last = kb + 2 == nk2;
+      HW w0 = rw, w1 = rw, p = pw;
+      __amdgpu_buffer_rsrc_t h0 = rh, h1 = rh, ph_ = ph;
+      int kp0 = kb + 1 + PREFETCH_AHEAD, kp1 = kb + 2 + PREFETCH_AHEAD, kl1 = kb + 2;
+      if (last) {
+        w1 = more_tiles ? rsrc_w(nn) : zero_w();
+        h1 = more_tiles ? rsrc_h(mn) : zero;
+        p = pf_rsrc(mn, w1);
+        ph_ = pfh_rsrc(h1);
+        if (nk & 1) {
+          w0 = zero_w();
+          h0 = zero;
+        }
+        kp0 = 0;
+        kp1 = 1;
+        kl1 = 0;
+      }
+      k_block(kb, S0{}, kb + 1, w0, h0, p, ph_, kp0, true);
+      if (last) stage_targets(mn, parity ^ 1);   // after the last tile: its own, unused
+      k_block(kb + 1, S1{}, kl1, w1, h1, p, ph_, kp1, !last);
+      // wait states after the iteration's last MFMA, for register copies
+      // the compiler may place where the loop ends (issued while the MFMA
+      // pipeline is still busy)
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_nop 7\n\ts_nop 3");
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Wait states between the last MFMA and the first read of its result
+    // (more than the instruction's latency requires).
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+    __builtin_amdgcn_sched_barrier(0);
 
     const int v0 = n * TILE_V;
     const int t0 = m * TT;
@@ -620,20 +685,58 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
 
     // acc[i][j][r] holds z[t][v] for
-    //   v = v0 + wv*128 + 32 i + 8 (r >> 2) + 4 fk + (r & 3)
-    //   t = t0 + wt*WT + 32 j + fr
+    //   v = v0 + wv*128 + 16 i + 4 fg + r
+    //   t = t0 + wt*WT + 16 j + fc
     const int vbase = v0 + wv * 128;
     {
-    const int fr = lane_e & 31;
-    const int fk = lane_e >> 5;
-    auto xor32 = [&](float x) {
-      return __int_as_float(__builtin_amdgcn_ds_bpermute((lane_e ^ 32) << 2, __float_as_int(x)));
+    const int fc = lane_e & 15;
+    const int fg = lane_e >> 4;
+    // Combining the four row groups' values of a column (lanes fc, fc + 16,
+    // fc + 32, fc + 48) in the VALU: v_permlane16_swap exchanges the odd
+    // 16-lane rows of one copy with the even rows of the other, so the pair
+    // (lo, hi) below holds, in every lane, the values of rows 2 k and 2 k + 1
+    // of its pair of rows; v_permlane32_swap does the same for the halves.
+    // Every lane then applies the operation in the same operand order.
+    auto rows16 = [](float x, float &lo, float &hi) {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                      false, false);
+      lo = __uint_as_float(r[0]);
+      hi = __uint_as_float(r[1]);
+    };
+    auto rows32 = [](float x, float &lo, float &hi) {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                      false, false);
+      lo = __uint_as_float(r[0]);
+      hi = __uint_as_float(r[1]);
+    };
+    // the register of a 16-row block that holds row rel (0 .. 127) for the
+    // lane of row group (rel >> 2) & 3: block rel >> 4, register rel & 3,
+    // picked by a fixed select tree over the 32 values of token block j
+    auto pick = [&](int j, int rel) {
+      const int bi = (rel >> 4) & 7, ri = rel & 3;
+      float sel[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v8[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v8[i] = acc[i][j][r];
+#pragma unroll
+        for (int lvl = 0; lvl < 3; ++lvl) {
+          const bool bit = (bi >> lvl) & 1;
+#pragma unroll
+          for (int q = 0; q < (4 >> lvl); ++q) v8[q] = bit ? v8[2 * q + 1] : v8[2 * q];
+        }
+        sel[r] = v8[0];
+      }
+      const float lo = (ri & 1) ? sel[1] : sel[0];
+      const float hi = (ri & 1) ? sel[3] : sel[2];
+      return (ri & 2) ? hi : lo;
     };
     // this tile's targets, staged in LDS before its K loop (read with
     // ds_read: no wait on the vector memory counter)
     const int *tgt = reinterpret_cast<const int *>(smem + TGT_OFS + parity * (TILE_T * 4));
     auto target_of = [&](int j, int t) {
-      return (t < a.T) ? tgt[wt * WT + 32 * j + fr] : -1;
+      return (t < a.T) ? tgt[wt * WT + 16 * j + fc] : -1;
     };
     // neighbouring-lane exchange (lane l gets lane l ^ 1's value): a DPP quad
     // permutation [1, 0, 3, 2] in the VALU, no LDS round trip
@@ -652,29 +755,30 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
       constexpr uint32_t DROP = 0x80000000u;
       constexpr bool vec = EX == 0;
       if constexpr (vec) {
-        // Through LDS: each wave stages its 32-row blocks (32 rows x 128
-        // columns fp32, 16 KiB) in its quarter of the operand buffer's stage 1
-        // (free once every wave is past the tile's last K block), then stores
-        // whole rows, two per instruction: 8 full lines per store instead of
-        // 32 rows x 32 bytes.  16-byte chunk c of staging row r sits at slot
-        // c ^ (r & 15), which keeps the writes (8 rows, one chunk) and the row
-        // reads free of bank conflicts.
+        // Through LDS: each wave stages 32 token rows at a time (two token
+        // blocks; 32 rows x 128 columns fp32, 16 KiB) in its quarter of the
+        // operand buffer's stage 1 (free once every wave is past the tile's
+        // last K block), then stores whole rows, two per instruction: 8 full
+        // lines per store instead of 32 rows x 32 bytes.  16-byte chunk c of
+        // staging row r sits at slot c ^ (r & 15), which keeps the writes (16
+        // rows, one chunk) and the row reads free of bank conflicts.
         typedef __attribute__((address_space(3))) char lds_c;
         lds_c *stg = (lds_c *)smem + 2 * STAGE_BYTES + wave * (STAGE_BYTES / 2);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
+        for (int jp = 0; jp < NJ / 2; ++jp) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-              *(u32x4 *)(stg + fr * 512 + (((8 * i + 2 * q + fk) ^ (fr & 15)) << 4)) =
-                  u32x4{__float_as_uint(acc[i][j][4 * q]), __float_as_uint(acc[i][j][4 * q + 1]),
-                        __float_as_uint(acc[i][j][4 * q + 2]),
-                        __float_as_uint(acc[i][j][4 * q + 3])};
-          const int trow = t0 + wt * WT + 32 * j;
+            for (int i = 0; i < NI; ++i) {
+              const f32x4 v = acc[i][2 * jp + jj];
+              *(u32x4 *)(stg + (16 * jj + fc) * 512 + (((4 * i + fg) ^ fc) << 4)) =
+                  u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                        __float_as_uint(v[3])};
+            }
+          const int trow = t0 + wt * WT + 32 * jp;
           const int rows = min(32, a.T - trow);
           const __amdgpu_buffer_rsrc_t r_out = make_rsrc(
               a.logits + (size_t)trow * a.V, rows > 0 ? (uint32_t)rows * (uint32_t)a.V * 4u : 0u);
@@ -693,24 +797,22 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
       } else {
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const int trow = t0 + wt * WT + 32 * j;
-        const int rows = min(32, a.T - trow);
+        const int trow = t0 + wt * WT + 16 * j;
+        const int rows = min(16, a.T - trow);
         const __amdgpu_buffer_rsrc_t r_out = make_rsrc(
             a.logits + (size_t)trow * a.V, rows > 0 ? (uint32_t)rows * (uint32_t)a.V * 4u : 0u);
-        const uint32_t rofs = (uint32_t)fr * (uint32_t)a.V * 4u;
+        const uint32_t rofs = (uint32_t)fc * (uint32_t)a.V * 4u;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < NI; ++i) {
+          const int v4 = vbase + 16 * i + 4 * fg;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int v4 = vbase + 32 * i + 8 * q + 4 * fk;
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-              const int v = v4 + rr;
-              const uint32_t off = v < a.V ? rofs + 4u * (uint32_t)v : DROP;
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][4 * q + rr]),
-                                                    r_out, (int)off, 0, 0);
-            }
+          for (int rr = 0; rr < 4; ++rr) {
+            const int v = v4 + rr;
+            const uint32_t off = v < a.V ? rofs + 4u * (uint32_t)v : DROP;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][rr]), r_out,
+                                                  (int)off, 0, 0);
           }
+        }
       }
       }  // vec
     } else {
@@ -739,7 +841,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
         // c ^ sw(r), sw(r) = 4 (r & 3) + ((r >> 2) & 3), which keeps the
         // writes (16 rows, one chunk), the row reads (one row, 16 x 16
         // bytes) and the transposing reads (4 rows x 4 chunks) free of bank
-        // conflicts.
+        // conflicts.  Pass p stages token blocks 4 p .. 4 p + 3: block jj of
+        // the pass in staging rows 16 jj .. 16 jj + 15.
         typedef __attribute__((address_space(3))) char lds_c;
         typedef short v4s __attribute__((ext_vector_type(4)));
         typedef __attribute__((address_space(3))) v4s lds_v4s;
@@ -760,58 +863,42 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
         auto stage_pass = [&](int p, auto masked) {
           constexpr bool MASK = decltype(masked)::value;
 #pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            const int j = 2 * p + jj;
-            const int t = t0 + wt * 128 + 32 * j + fr;
+          for (int jj = 0; jj < 4; ++jj) {
+            const int j = 4 * p + jj;
+            const int t = t0 + wt * 128 + 16 * j + fc;
             const bool trow = t < a.T;
             const int y = trow ? target_of(j, t) : -1;
             const bool live = trow && y >= 0 && y < a.V;
             const float lse_t = live ? lse_r[j] : 0.0f;
             const float gs = live ? grad_r[j] * a.inv_tau : 0.0f;
             const uint64_t keep = live ? ~0ull : 0ull;
-            const int lim = a.V - vbase - 4 * fk;   // MASK: offsets below lim are valid
+            const int lim = a.V - vbase - 4 * fg;   // MASK: offsets below lim are valid
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < NI; ++i) {
+              uint16_t b[4];
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                uint16_t b[4];
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                  const float zs = acc[i][j][4 * q + rr] * a.inv_tau;
-                  const float pr = __builtin_amdgcn_exp2f((zs - lse_t) * LOG2E);
-                  float d = gs * (0.0f - pr);
-                  if (MASK && 32 * i + 8 * q + rr >= lim) d = 0.0f;
-                  b[rr] = __builtin_bit_cast(uint16_t, (__bf16)d);
-                }
-                const uint64_t packed = (uint64_t)b[0] | ((uint64_t)b[1] << 16) |
-                                        ((uint64_t)b[2] << 32) | ((uint64_t)b[3] << 48);
-                *(uint64_t *)slot(32 * jj + fr, 8 * i + 2 * q + fk) = packed & keep;
+              for (int rr = 0; rr < 4; ++rr) {
+                const float zs = acc[i][j][rr] * a.inv_tau;
+                const float pr = __builtin_amdgcn_exp2f((zs - lse_t) * LOG2E);
+                float d = gs * (0.0f - pr);
+                if (MASK && 16 * i + rr >= lim) d = 0.0f;
+                b[rr] = __builtin_bit_cast(uint16_t, (__bf16)d);
               }
-            // the target column: block i = rel >> 5, register 4 q + rr with
-            // q = (rel >> 3) & 3, rr = rel & 3, picked by a fixed select tree
+              const uint64_t packed = (uint64_t)b[0] | ((uint64_t)b[1] << 16) |
+                                      ((uint64_t)b[2] << 32) | ((uint64_t)b[3] << 48);
+              *(uint64_t *)slot(16 * jj + fc, 4 * i + fg) = packed & keep;
+            }
+            // the target column: block rel >> 4, register rel & 3, in the
+            // lane of row group (rel >> 2) & 3
             const int rel = y - vbase;
-            const bool hit = live && rel >= 0 && rel < STAT_V && ((rel >> 2) & 1) == fk;
+            const bool hit = live && rel >= 0 && rel < STAT_V && ((rel >> 2) & 3) == fg;
             if (__any(hit)) {
-              const int bi = (rel >> 5) & 3;
-              const int ri = (((rel & 31) >> 3) << 2) | (rel & 3);
-              float sel[16];
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const float lo = (bi & 1) ? acc[1][j][r] : acc[0][j][r];
-                const float hi = (bi & 1) ? acc[3][j][r] : acc[2][j][r];
-                sel[r] = (bi & 2) ? hi : lo;
-              }
-#pragma unroll
-              for (int lvl = 0; lvl < 4; ++lvl) {
-                const bool bit = (ri >> lvl) & 1;
-#pragma unroll
-                for (int q = 0; q < (8 >> lvl); ++q) sel[q] = bit ? sel[2 * q + 1] : sel[2 * q];
-              }
+              const float zy = pick(j, rel);
               if (hit) {
-                const float zs = sel[0] * a.inv_tau;
+                const float zs = zy * a.inv_tau;
                 const float pr = __builtin_amdgcn_exp2f((zs - lse_t) * LOG2E);
                 const float d = gs * (1.0f - pr);
-                *(uint16_t *)(slot(32 * jj + fr, (rel & (STAT_V - 1)) >> 2) + 2 * (rel & 3)) =
+                *(uint16_t *)(slot(16 * jj + fc, (rel & (STAT_V - 1)) >> 2) + 2 * (rel & 3)) =
                     __builtin_bit_cast(uint16_t, (__bf16)d);
               }
             }
@@ -885,96 +972,104 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
         // Columns past the vocabulary end count as -inf: they add nothing to
         // the max and exactly 0 to the sum.  On valid columns the masked and
         // unmasked instantiations compute the same thing.
-        const int lim = a.V - vbase - 4 * fk;  // columns at offset < lim are valid
+        const int lim = a.V - vbase - 4 * fg;  // columns at offset < lim are valid
+        auto zv = [&](int i, int j, int r) {
+          const bool out = MASK && (16 * i + r >= lim);
+          return out ? -INFINITY : xf(acc[i][j][r]);
+        };
+        // Token blocks two at a time, with no branch until the stores (so
+        // the two blocks' dependency chains overlap).
+        // 1) tile max: this lane's 32 values in (i, r) order, then across
+        //    the four lanes (row groups fg) holding the tile's 128 rows:
+        //    row groups 0 with 1 and 2 with 3, then the two pairs.
+        // 2) sum of exp(z - m): the lane's 32 exponentials added as a fixed
+        //    pairwise tree ((e0 + e1) + (e2 + e3)) + ..., in (i, r) order
+        //    (subtrees of 8 per pair of blocks i, then those four pairwise),
+        //    then across the row groups as for the max; m is taken as 0 when
+        //    the whole tile is -inf so that such a tile adds exactly 0.  z == m
+        //    gives exp(0) = 1 exactly, so the sum is >= 1 when the max is
+        //    finite.  The entropy partial e (z - m) the same way (a -inf
+        //    logit has e == 0 and adds -0: d clamped to the finite range).
+        float m2[NJ], s2[NJ], u2[NJ];
+#pragma unroll
+        for (int jg = 0; jg < NJ; jg += 2) {
+#pragma unroll
+          for (int j = jg; j < jg + 2; ++j) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) mx = fmaxf(mx, zv(i, j, r));
+            m2[j] = mx;
+          }
+#pragma unroll
+          for (int j = jg; j < jg + 2; ++j) {
+            float lo, hi;
+            rows16(m2[j], lo, hi);
+            const float m1 = fmaxf(lo, hi);
+            rows32(m1, lo, hi);
+            m2[j] = fmaxf(lo, hi);
+          }
+#pragma unroll
+          for (int j = jg; j < jg + 2; ++j) {
+            const float ms = (m2[j] == -INFINITY) ? 0.0f : m2[j];
+            float ps[4], pu[4];
+#pragma unroll
+            for (int i2 = 0; i2 < 4; ++i2) {
+              float e[8], u[8];
+#pragma unroll
+              for (int x = 0; x < 8; ++x) {
+                const int i = 2 * i2 + (x >> 2), r = x & 3;
+                const float d = zv(i, j, r) - ms;
+                e[x] = __builtin_amdgcn_exp2f(d * LOG2E);
+                if constexpr (EX == 2) u[x] = e[x] * fmaxf(d, -FLT_MAX);
+              }
+              ps[i2] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+              if constexpr (EX == 2)
+                pu[i2] = ((u[0] + u[1]) + (u[2] + u[3])) + ((u[4] + u[5]) + (u[6] + u[7]));
+            }
+            s2[j] = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+            u2[j] = EX == 2 ? (pu[0] + pu[1]) + (pu[2] + pu[3]) : 0.0f;
+          }
+#pragma unroll
+          for (int j = jg; j < jg + 2; ++j) {
+            float lo, hi;
+            rows16(s2[j], lo, hi);
+            const float s1 = lo + hi;
+            rows32(s1, lo, hi);
+            s2[j] = lo + hi;
+            if constexpr (EX == 2) {
+              rows16(u2[j], lo, hi);
+              const float u1 = lo + hi;
+              rows32(u1, lo, hi);
+              u2[j] = lo + hi;
+            }
+          }
+        }
+        // 3) tile-major [nST][T] statistics (coalesced over rows): row
+        //    group 0 stores the max, 1 the sum, 2 the entropy partial, one
+        //    store per token block.
+        float *const dst = fg == 0 ? a.part_m : fg == 1 ? a.part_s : a.part_u;
+        const bool writer = fg < 2 || (EX == 2 && fg == 2);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-          const int t = t0 + wt * WT + 32 * j + fr;
-          // 1) tile max: this lane's 64 values in (i, r) order, then the
-          //    partner lane (fk flipped) holding the other 64 of the tile.
-          float mx = -INFINITY;
+          const int t = t0 + wt * WT + 16 * j + fc;
+          const float v = fg == 0 ? m2[j] : fg == 1 ? s2[j] : u2[j];
+          if (writer && t < a.T) dst[(size_t)(a.js_base + js) * a.T + t] = v;
+        }
+        // 4) target capture: the one lane holding z[t][y[t]] writes xt[t],
+        //    the value picked by a fixed select tree over its 32 values.
+        // (targets are global ids; a weight slice starts at y_base)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const bool out = MASK && (32 * i + 8 * (r >> 2) + (r & 3) >= lim);
-              mx = fmaxf(mx, out ? -INFINITY : xf(acc[i][j][r]));
-            }
-          const float mo = xor32(mx);
-          const float m2 = fk == 0 ? fmaxf(mx, mo) : fmaxf(mo, mx);
-          // 2) sum of exp(z - m), same tree; m is taken as 0 when the whole
-          //    tile is -inf so that such a tile adds exactly 0.  z == m gives
-          //    exp(0) = 1 exactly, so the sum is >= 1 when the max is finite.
-          const float ms = (m2 == -INFINITY) ? 0.0f : m2;
-          // Per block i, the 16 differences first, then the exponentials,
-          // then the sums in r order: the same operations and summation
-          // order as one value at a time, but no exponential waits on the
-          // one before it or feeds the next add directly (that latency, not
-          // the arithmetic, was what the one-at-a-time chain paid).
-          float sx = 0.0f, ux = 0.0f;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float dd[16], ee[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const bool out = MASK && (32 * i + 8 * (r >> 2) + (r & 3) >= lim);
-              const float z = out ? -INFINITY : xf(acc[i][j][r]);
-              dd[r] = z - ms;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) ee[r] = __builtin_amdgcn_exp2f(dd[r] * LOG2E);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              sx = sx + ee[r];
-              // entropy partial: e (z - m); a -inf logit has e == 0 and
-              // adds -0 (d clamped to the finite range first)
-              if constexpr (EX == 2) ux = ux + ee[r] * fmaxf(dd[r], -FLT_MAX);
-            }
-          }
-          const float so = xor32(sx);
-          const float s2 = fk == 0 ? sx + so : so + sx;
-          float u2 = 0.0f;
-          if constexpr (EX == 2) {
-            const float uo = xor32(ux);
-            u2 = fk == 0 ? ux + uo : uo + ux;
-          }
-          // 3) tile-major [nST][T] statistics (coalesced over rows).
-          if (t < a.T) {
-            const size_t o = (size_t)(a.js_base + js) * a.T + t;
-            if (fk == 0) {
-              a.part_m[o] = m2;
-              if constexpr (EX == 2) a.part_u[o] = u2;
-            } else {
-              a.part_s[o] = s2;
-            }
-          }
-          // 4) target capture: the one lane holding z[t][y[t]] writes xt[t],
-          //    the value picked by a fixed select tree over its 64 values.
-          // (targets are global ids; a weight slice starts at y_base)
+        for (int j = 0; j < NJ; ++j) {
+          const int t = t0 + wt * WT + 16 * j + fc;
           const int yt = target_of(j, t);
           const int y = yt < 0 ? -1 : yt - a.y_base;
           const int rel = y - vbase;
-          const bool hit = rel >= 0 && rel < STAT_V && ((rel >> 2) & 1) == fk;
+          const bool hit = rel >= 0 && rel < STAT_V && ((rel >> 2) & 3) == fg;
           if (__any(hit)) {
-            // block i = rel >> 5, register r = ((w >> 3) << 2) | (w & 3),
-            // w = rel & 31
-            const int bi = (rel >> 5) & 3;
-            const int w = rel & 31;
-            const int ri = ((w >> 3) << 2) | (w & 3);
-            float sel[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float lo = (bi & 1) ? acc[1][j][r] : acc[0][j][r];
-              const float hi = (bi & 1) ? acc[3][j][r] : acc[2][j][r];
-              sel[r] = (bi & 2) ? hi : lo;
-            }
-#pragma unroll
-            for (int lvl = 0; lvl < 4; ++lvl) {
-              const bool bit = (ri >> lvl) & 1;
-#pragma unroll
-              for (int q = 0; q < (8 >> lvl); ++q)
-                sel[q] = bit ? sel[2 * q + 1] : sel[2 * q];
-            }
-            if (hit) a.xt[t] = xf(sel[0]);
+            const float zy = pick(j, rel);
+            if (hit) a.xt[t] = xf(zy);
           }
         }
       };
@@ -997,8 +1092,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     L = Ln;
     m = mn;
     n = nn;
-    rw = rwn;
-    rh = rhn;
+    rw = rsrc_w(n);
+    rh = rsrc_h(m);
     pw = pf_rsrc(m, rw);
     ph = pfh_rsrc(rh);
   }
@@ -1965,10 +2060,13 @@ __global__ __launch_bounds__(64) void topk_scatter_kernel(const TopkDirectArgs a
 //    The tile's weight block (128 rows x 64 K, 16 KiB) goes to LDS by
 //    direct-to-LDS loads, double-buffered and shared by the waves, in the
 //    logit GEMM's layout (16-byte chunk c of row r at c ^ swz(r); load q of
-//    wave w fills rows 8 (NW q + w) .. + 7); each lane loads its pair's hidden
-//    row straight into the MFMA operand layout (row l & 31, K slice 8 (l >> 5)
-//    .. + 7 of each 16-deep step), one block ahead.  Rows past V read zeros
-//    through the resource's range.
+//    wave w fills rows 8 (NW q + w) .. + 7).  The wave's pairs are two
+//    16-column MFMA blocks: lane l loads the hidden rows of its pairs
+//    l & 15 and 16 + (l & 15) straight into the MFMA operand layout (K slice
+//    8 (l >> 4) .. + 7 of each 32-deep step), one block ahead.  Every logit
+//    is the logit GEMM's: the same MFMA instruction over the same 32-deep K
+//    slices in the same order, with the same K slice in each lane.  Rows
+//    past V read zeros through the resource's range.
 typedef char TileStage[TILE_K * STAT_V * 2];
 template <int NW>
 __device__ __forceinline__ void tile_logits_body(const TopkDirectArgs &a, TileStage *wlds) {
@@ -1977,16 +2075,25 @@ __device__ __forceinline__ void tile_logits_body(const TopkDirectArgs &a, TileSt
   if (it >= a.totals[0]) return;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l = tid & 63, r = l & 31, fk = l >> 5;
+  const int l = tid & 63, c = l & 15, g = l >> 4;
   const int j = a.item_tile[it];
   const int first = a.tile_off[j] + 32 * NW * (it - a.item_off[j]) + 32 * wave;
   const int cnt = min(32, a.tile_off[j] + a.tile_count[j] - first);   // <= 0: an idle wave
-  const int p = r < cnt ? a.bucket[first + r] : -1;
   const int regular = a.T * a.C;
-  int t = -1;
-  if (p >= 0) t = p < regular ? p / a.C : a.deg_row[(p - regular) / a.nST];
-  const bool hv = t >= 0;
-  const uint16_t *hp = a.hidden + (size_t)(hv ? t : 0) * a.ldh + 8 * fk;
+  // the lane's pairs in blocks 0 and 1 (p < 0: none; its column is not stored)
+  int pj[2];
+  const uint16_t *hp[2];
+#pragma unroll
+  for (int jb = 0; jb < 2; ++jb) {
+    const int pc = 16 * jb + c;
+    const int pp = pc < cnt ? a.bucket[first + pc] : -1;
+    int t = -1;
+    if (pp >= 0) t = pp < regular ? pp / a.C : a.deg_row[(pp - regular) / a.nST];
+    pj[jb] = t >= 0 ? pp : -1;
+    // (a lane without a pair loads row 0: the MFMA keeps each output column
+    // to its own B column, and that column is not stored)
+    hp[jb] = a.hidden + (size_t)(t >= 0 ? t : 0) * a.ldh + 8 * g;
+  }
   const int v0 = j * STAT_V;
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(
       a.weight + (size_t)v0 * a.ldw, (uint32_t)(min(STAT_V, a.V - v0) * a.ldw * 2));
@@ -2006,27 +2113,32 @@ __device__ __forceinline__ void tile_logits_body(const TopkDirectArgs &a, TileSt
           (uint32_t)kb * (TILE_K * 2), 0, 0);
   };
 
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  // (a lane without a pair loads row 0 and zeroes it where it is used, so
-  // that no wait for the load comes before the next block)
-  auto hload = [&](int kb, u32x4 (&hb)[4]) {
+  // hidden fragments of a block: [K step][pair block]
+  auto hload = [&](int kb, u32x4 (&hb)[2][2]) {
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) hb[s4] = *(const u32x4 *)(hp + kb * TILE_K + 16 * s4);
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+        hb[ks][jb] = *(const u32x4 *)(hp[jb] + kb * TILE_K + 32 * ks);
   };
-  f32x16 acc[4];
+  f32x4 acc[8][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int q = 0; q < 16; ++q) acc[i][q] = 0.0f;
+    for (int jb = 0; jb < 2; ++jb) acc[i][jb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   const int nk = a.H / TILE_K;
   const bool live = cnt > 0;   // uniform per wave
-  u32x4 hb0[4], hb1[4];
+  u32x4 hb0[2][2], hb1[2][2];
+  auto mma = [&](int i, int jb, bf16x8 w8, bf16x8 h8) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[i][jb]) : "v"(w8), "v"(h8));
+  };
   // K block kb from stage ST (== kb & 1); the next block's loads go to the
-  // other stage and hidden-fragment set
+  // other stage and hidden-fragment set.  (MFMAs in inline assembly, as in
+  // the logit GEMM; wait states after the zeroing and before the reads.)
   auto block = [&](int kb, auto stage) {
     constexpr int ST = decltype(stage)::value;
-    u32x4(&cur)[4] = ST ? hb1 : hb0;
-    u32x4(&nxt)[4] = ST ? hb0 : hb1;
+    u32x4(&cur)[2][2] = ST ? hb1 : hb0;
+    u32x4(&nxt)[2][2] = ST ? hb0 : hb1;
     // this block's loads (every wave's) have landed; the other stage is free
     __builtin_amdgcn_s_waitcnt(VMCNT0);
     __syncthreads();
@@ -2035,19 +2147,30 @@ __device__ __forceinline__ void tile_logits_body(const TopkDirectArgs &a, TileSt
       if (live) hload(kb + 1, nxt);
     }
     if (live) {
+      // the weight fragments of step 0, then those of step 1 under step 0's
+      // MFMAs
+      bf16x8 w8[2][8];
+      auto wread = [&](int ks, int i) {
+        const int row = 16 * i + c;
+        w8[ks][i] = *(const bf16x8 *)(&wlds[ST][0] + row * 128 + (((4 * ks + g) ^ swz(row)) << 4));
+      };
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        const bf16x8 b = __builtin_bit_cast(bf16x8, hv ? cur[s4] : zero4);
+      for (int i = 0; i < 8; ++i) wread(0, i);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 32 * i + r;
-          const bf16x8 w8 = *(const bf16x8 *)(&wlds[ST][0] + row * 128 +
-                                              (((2 * s4 + fk) ^ swz(row)) << 4));
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w8, b, acc[i], 0, 0, 0);
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (ks == 0) wread(1, i);
+#pragma unroll
+          for (int jb = 0; jb < 2; ++jb)
+            mma(i, jb, w8[ks][i], __builtin_bit_cast(bf16x8, cur[ks][jb]));
         }
       }
     }
   };
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 4");
+  __builtin_amdgcn_sched_barrier(0);
   wload(0, 0);
   if (live) hload(0, hb0);
   using S0 = std::integral_constant<int, 0>;
@@ -2059,30 +2182,41 @@ __device__ __forceinline__ void tile_logits_body(const TopkDirectArgs &a, TileSt
   }
   if (kb < nk) block(kb, S0{});
   if (!live) return;
-  if (nk & 1) {   // the GEMM's appended zero block: 4 steps of zero operands
-    const bf16x8 z = __builtin_bit_cast(bf16x8, zero4);
+  if (nk & 1) {
+    // the GEMM's appended zero block: 2 steps of zero operands (the wait
+    // states cover the zero operand's VALU write)
+    const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4)
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(z, z, acc[i], 0, 0, 0);
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+          asm volatile("s_nop 4\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %1, %0"
+                       : "+a"(acc[i][jb])
+                       : "v"(z));
   }
-  // acc[i][4 q + e] is the logit of column 32 i + 8 q + 4 fk + e of the tile;
-  // columns past V are stored as NaN, which no selection takes
-  if (p >= 0) {
-    float *o = a.pair_z + (size_t)p * STAT_V + 4 * fk;
-    const int lim = a.V - v0 - 4 * fk;   // columns at offset < lim are entries
-    const uint32_t qnan = 0x7FC00000u;
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+  __builtin_amdgcn_sched_barrier(0);
+  // acc[i][jb][e] is the logit of column 16 i + 4 g + e of the tile for the
+  // lane's pair of block jb; columns past V are stored as NaN, which no
+  // selection takes
+  const int lim = a.V - v0 - 4 * g;   // columns at offset < lim are entries
+  const uint32_t qnan = 0x7FC00000u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+  for (int jb = 0; jb < 2; ++jb) {
+    if (pj[jb] >= 0) {
+      float *o = a.pair_z + (size_t)pj[jb] * STAT_V + 4 * g;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int i = 0; i < 8; ++i) {
         u32x4 d;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          d[e] = 32 * i + 8 * q + e < lim ? __float_as_uint(acc[i][4 * q + e]) : qnan;
-        *(u32x4 *)(o + 32 * i + 8 * q) = d;
+          d[e] = 16 * i + e < lim ? __float_as_uint(acc[i][jb][e]) : qnan;
+        *(u32x4 *)(o + 16 * i) = d;
       }
+    }
   }
 }
 
