@@ -186,6 +186,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   constexpr int TT = 32 * NJ;   // token rows of a tile (TILE_T)
   constexpr int WT = 16 * NJ;   // token rows of a wave
   constexpr int NQ = NI * NJ;   // MFMAs per wave and 32-deep K step
+  constexpr int BAR_Q = 40;     // the K block's barrier: behind this many MFMAs of step 1
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
   const int wv = wave & 1;   // vocabulary half of the tile
@@ -491,10 +492,13 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   //   in-order issue, and with it the next MFMA, until the texture path
   //   takes the load).
   //   Step 1 (B set 1): behind MFMA 2 its A_7, behind 16 the L2 prefetch;
-  //   after MFMA 31 the wave waits for its loads and the workgroup meets at
-  //   the barrier (the next block has landed; this block is no longer read);
-  //   then behind 33, 35, .., 47 the next block's B_0-7 (set 0) and behind
-  //   34, 38, 42, 46 its A_0-3 (last used here at MFMA 31 or before).
+  //   after MFMA BAR_Q - 1 (39) the wave waits for its loads and the
+  //   workgroup meets at the barrier (the next block has landed; this block
+  //   is no longer read); then behind the 15 MFMAs after it the next
+  //   block's B_0-7 (set 0, every second one) and A_0-3 (every fourth; last
+  //   used here at MFMA 31 or before).  (Barrier positions 32, 40 and 48
+  //   measured the same at 4096 rows; 40 and 48 hide more of the weight
+  //   stream's latency at 256 rows.)
   // The loads fetch K block kl of (r_w, r_h) into the other stage: kb + 1
   // of this tile, and in the tile's last block block 0 of the next tile
   // (r_w, r_h then name the next tile; the other stage is free once the
@@ -521,7 +525,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int q = 0; q < NQ / 2; ++q) {
+    for (int q = 0; q < BAR_Q; ++q) {
       mfma(1, q);
       if (q == 2) reada(st, 1, 7);
       if (q == 16) {
@@ -546,10 +550,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     }
     asm volatile("" ::: "memory");
 #pragma unroll
-    for (int q = NQ / 2; q < NQ; ++q) {
+    for (int q = BAR_Q; q < NQ; ++q) {
       mfma(1, q);
-      if (q < 48 && (q & 1) == 1) readb(0, st ^ 1, 0, (q - 33) >> 1);
-      if (q < 48 && (q & 3) == 2) reada(st ^ 1, 0, (q - 34) >> 2);
+      if (q > BAR_Q && q < BAR_Q + 16 && ((q - BAR_Q) & 1) == 1)
+        readb(0, st ^ 1, 0, (q - BAR_Q - 1) >> 1);
+      if (q > BAR_Q && q < BAR_Q + 16 && ((q - BAR_Q) & 3) == 2)
+        reada(st ^ 1, 0, (q - BAR_Q - 2) >> 2);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -2147,24 +2153,22 @@ __device__ __forceinline__ void tile_logits_body(const TopkDirectArgs &a, TileSt
       if (live) hload(kb + 1, nxt);
     }
     if (live) {
-      // the weight fragments of step 0, then those of step 1 under step 0's
-      // MFMAs
-      bf16x8 w8[2][8];
-      auto wread = [&](int ks, int i) {
-        const int row = 16 * i + c;
-        w8[ks][i] = *(const bf16x8 *)(&wlds[ST][0] + row * 128 + (((4 * ks + g) ^ swz(row)) << 4));
+      // the 16 weight fragments of the block (step ks, block i: x = 8 ks +
+      // i) through a ring of four, each read three fragments ahead (more
+      // registers would cost this LDS-bound kernel resident waves)
+      bf16x8 w8[4];
+      auto wread = [&](int x) {
+        const int ks = x >> 3, row = 16 * (x & 7) + c;
+        w8[x & 3] = *(const bf16x8 *)(&wlds[ST][0] + row * 128 + (((4 * ks + g) ^ swz(row)) << 4));
       };
 #pragma unroll
-      for (int i = 0; i < 8; ++i) wread(0, i);
+      for (int x = 0; x < 3; ++x) wread(x);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int x = 0; x < 16; ++x) {
+        if (x + 3 < 16) wread(x + 3);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          if (ks == 0) wread(1, i);
-#pragma unroll
-          for (int jb = 0; jb < 2; ++jb)
-            mma(i, jb, w8[ks][i], __builtin_bit_cast(bf16x8, cur[ks][jb]));
-        }
+        for (int jb = 0; jb < 2; ++jb)
+          mma(x & 7, jb, w8[x & 3], __builtin_bit_cast(bf16x8, cur[x >> 3][jb]));
       }
     }
   };
@@ -2382,7 +2386,7 @@ __global__ __launch_bounds__(256) void topk_select_wave_kernel(const TopkDirectA
 // (the kernels wrap the body: a template kernel with this body itself left
 // its host-side launch stubs unemitted)
 template <int NW>
-__global__ __launch_bounds__(64 * NW) void tile_logits_kernel(const TopkDirectArgs a) {
+__global__ __launch_bounds__(64 * NW, 4) void tile_logits_kernel(const TopkDirectArgs a) {
   __shared__ __attribute__((aligned(16))) TileStage wlds[2];
   tile_logits_body<NW>(a, wlds);
 }
