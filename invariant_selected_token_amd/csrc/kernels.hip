@@ -666,7 +666,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
       }
       k_block(kb, S0{}, kb + 1, w0, h0, p, ph_, kp0, true);
       if (last) stage_targets(mn, parity ^ 1);   // after the last tile: its own, unused
-      k_block(kb + 1, S1{}, kl1, w1, h1, p, ph_, kp1, !last);
+      // (the logit-gradient pass keeps the wait: its epilogue reloads
+      // spilled per-row values and waits on vector memory, which would then
+      // wait for the next tile's loads)
+      k_block(kb + 1, S1{}, kl1, w1, h1, p, ph_, kp1, !last || EX == 3);
       // wait states after the iteration's last MFMA, for register copies
       // the compiler may place where the loop ends (issued while the MFMA
       // pipeline is still busy)
@@ -983,14 +986,16 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
           const bool out = MASK && (16 * i + r >= lim);
           return out ? -INFINITY : xf(acc[i][j][r]);
         };
-        // Token blocks two at a time, with no branch until the stores (so
-        // the two blocks' dependency chains overlap).
+        // Token blocks two at a time (one with 1/tau and bf16 rounding alone:
+        // two spilled 38 registers there, one spills 6), with no branch until
+        // the stores (so the blocks' dependency chains overlap).
+        constexpr int JG = EX == 0 ? 2 : 1;
         // 1) tile max: this lane's 32 values in (i, r) order, then across
         //    the four lanes (row groups fg) holding the tile's 128 rows:
         //    row groups 0 with 1 and 2 with 3, then the two pairs.
         // 2) sum of exp(z - m): the lane's 32 exponentials added as a fixed
         //    pairwise tree ((e0 + e1) + (e2 + e3)) + ..., in (i, r) order
-        //    (subtrees of 8 per pair of blocks i, then those four pairwise),
+        //    (subtrees of 4 per block i, then those eight pairwise),
         //    then across the row groups as for the max; m is taken as 0 when
         //    the whole tile is -inf so that such a tile adds exactly 0.  z == m
         //    gives exp(0) = 1 exactly, so the sum is >= 1 when the max is
@@ -998,9 +1003,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
         //    logit has e == 0 and adds -0: d clamped to the finite range).
         float m2[NJ], s2[NJ], u2[NJ];
 #pragma unroll
-        for (int jg = 0; jg < NJ; jg += 2) {
+        for (int jg = 0; jg < NJ; jg += JG) {
 #pragma unroll
-          for (int j = jg; j < jg + 2; ++j) {
+          for (int j = jg; j < jg + JG; ++j) {
             float mx = -INFINITY;
 #pragma unroll
             for (int i = 0; i < NI; ++i)
@@ -1009,7 +1014,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
             m2[j] = mx;
           }
 #pragma unroll
-          for (int j = jg; j < jg + 2; ++j) {
+          for (int j = jg; j < jg + JG; ++j) {
             float lo, hi;
             rows16(m2[j], lo, hi);
             const float m1 = fmaxf(lo, hi);
@@ -1017,28 +1022,28 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
             m2[j] = fmaxf(lo, hi);
           }
 #pragma unroll
-          for (int j = jg; j < jg + 2; ++j) {
+          for (int j = jg; j < jg + JG; ++j) {
             const float ms = (m2[j] == -INFINITY) ? 0.0f : m2[j];
-            float ps[4], pu[4];
+            float ps[8], pu[8];
 #pragma unroll
-            for (int i2 = 0; i2 < 4; ++i2) {
-              float e[8], u[8];
+            for (int i = 0; i < NI; ++i) {
+              float e[4], u[4];
 #pragma unroll
-              for (int x = 0; x < 8; ++x) {
-                const int i = 2 * i2 + (x >> 2), r = x & 3;
+              for (int r = 0; r < 4; ++r) {
                 const float d = zv(i, j, r) - ms;
-                e[x] = __builtin_amdgcn_exp2f(d * LOG2E);
-                if constexpr (EX == 2) u[x] = e[x] * fmaxf(d, -FLT_MAX);
+                e[r] = __builtin_amdgcn_exp2f(d * LOG2E);
+                if constexpr (EX == 2) u[r] = e[r] * fmaxf(d, -FLT_MAX);
               }
-              ps[i2] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-              if constexpr (EX == 2)
-                pu[i2] = ((u[0] + u[1]) + (u[2] + u[3])) + ((u[4] + u[5]) + (u[6] + u[7]));
+              ps[i] = (e[0] + e[1]) + (e[2] + e[3]);
+              if constexpr (EX == 2) pu[i] = (u[0] + u[1]) + (u[2] + u[3]);
             }
-            s2[j] = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-            u2[j] = EX == 2 ? (pu[0] + pu[1]) + (pu[2] + pu[3]) : 0.0f;
+            s2[j] = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
+            u2[j] = EX == 2
+                        ? ((pu[0] + pu[1]) + (pu[2] + pu[3])) + ((pu[4] + pu[5]) + (pu[6] + pu[7]))
+                        : 0.0f;
           }
 #pragma unroll
-          for (int j = jg; j < jg + 2; ++j) {
+          for (int j = jg; j < jg + JG; ++j) {
             float lo, hi;
             rows16(s2[j], lo, hi);
             const float s1 = lo + hi;
@@ -1053,15 +1058,33 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
           }
         }
         // 3) tile-major [nST][T] statistics (coalesced over rows): row
-        //    group 0 stores the max, 1 the sum, 2 the entropy partial, one
-        //    store per token block.
-        float *const dst = fg == 0 ? a.part_m : fg == 1 ? a.part_s : a.part_u;
-        const bool writer = fg < 2 || (EX == 2 && fg == 2);
+        //    group 0 stores the max, 1 the sum, 2 the entropy partial, through
+        //    buffer resources over this wave's 128 rows of the tile's row
+        //    (rows past T lie past their size; the other row groups' lanes
+        //    get an offset past it): no branch and no per-lane pointer.
+        {
+          constexpr uint32_t DROP = 0x80000000u;
+          const int r0 = t0 + wt * WT;
+          const size_t base = (size_t)(a.js_base + js) * a.T + r0;
+          const uint32_t bytes = r0 < a.T ? (uint32_t)min(WT, a.T - r0) * 4u : 0u;
+          const __amdgpu_buffer_rsrc_t r_m = make_rsrc(a.part_m + base, bytes);
+          const __amdgpu_buffer_rsrc_t r_s = make_rsrc(a.part_s + base, bytes);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int t = t0 + wt * WT + 16 * j + fc;
-          const float v = fg == 0 ? m2[j] : fg == 1 ? s2[j] : u2[j];
-          if (writer && t < a.T) dst[(size_t)(a.js_base + js) * a.T + t] = v;
+          for (int j = 0; j < NJ; ++j) {
+            const uint32_t off = (uint32_t)(16 * j + fc) * 4u;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m2[j]), r_m,
+                                                  (int)(fg == 0 ? off : DROP), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s2[j]), r_s,
+                                                  (int)(fg == 1 ? off : DROP), 0, 0);
+          }
+          if constexpr (EX == 2) {
+            const __amdgpu_buffer_rsrc_t r_u = make_rsrc(a.part_u + base, bytes);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+              __builtin_amdgcn_raw_buffer_store_b32(
+                  __float_as_uint(u2[j]), r_u,
+                  (int)(fg == 2 ? (uint32_t)(16 * j + fc) * 4u : DROP), 0, 0);
+          }
         }
         // 4) target capture: the one lane holding z[t][y[t]] writes xt[t],
         //    the value picked by a fixed select tree over its 32 values.
