@@ -165,7 +165,7 @@ __device__ __forceinline__ bf16x4 tr_read(const lds_bf16x4 *__restrict__ p) {
 // The logit GEMM with its epilogue, for a sequence of workgroup tiles of 256
 // vocabulary x 256 token rows -- one tile shape for every batch size.  4
 // waves; wave w covers vocabulary half wv = w & 1 and token half wt = w >> 1
-// as 4 x 4 MFMA blocks of 32 x 32.  Every tile runs the same instructions:
+// as 8 x 8 MFMA blocks of 16 x 16.  Every tile runs the same instructions:
 // rows past T (in the last token tile of a batch whose size is not a
 // multiple of 256, e.g. every decode batch) read as zeros through the buffer
 // unit's range check, and no epilogue writes their results.  (Skipping their
@@ -1928,9 +1928,10 @@ hipError_t launch_topk(const float *logits, int64_t ld, const float *lse, const 
 // -inf: rows of NaN or infinities) every tile is a candidate.
 //
 // The logits of a (row, tile) pair come from the same MFMA instruction over
-// the same operands in the same K order as the logit GEMM (32 x 32 x 16 bf16,
-// fp32 accumulator from 0, K steps of 16 in increasing order, and the zero
-// block the GEMM appends when H / 64 is odd), so they are the GEMM's bits: the
+// the same operands in the same K order as the logit GEMM (16 x 16 x 32 bf16,
+// fp32 accumulator from 0, K steps of 32 in increasing order with the same K
+// slice in each lane, and the zero block the GEMM appends when H / 64 is
+// odd), so they are the GEMM's bits: the
 // selection sees exactly the values the stored-logits path reads.
 
 // 1) per row: m*, the candidate tiles into the row's k slots, and one count
