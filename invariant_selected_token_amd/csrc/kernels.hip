@@ -464,14 +464,18 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   // so A_i is used by MFMAs 8 i .. 8 i + 7 (an operand held for eight
   // MFMAs in a row toggles the matrix core's inputs less: measured, the
   // clock the kernel holds at the power limit is ~1.5 % higher than with A
-  // held for four).  In inline assembly: the builtin of this instruction gets its
+  // held for four).  The B blocks go up for even i and down for odd i, so
+  // the MFMA that moves on to the next A block keeps the B operand of the
+  // one before it (~0.5 % faster, same reason).  Each accumulator still
+  // takes its K steps in K order, so the sums are the same bits either way.
+  // In inline assembly: the builtin of this instruction gets its
   // accumulator copied between registers on every use by this compiler,
   // while the assembly form keeps each accumulator in place.  The compiler
   // does not see an MFMA here, so the tile supplies the wait states it
   // would insert (after zeroing the accumulators and before reading them,
   // below).
   auto mfma = [&](int buf, int q) {
-    const int i = q >> 3, j = q & 7;
+    const int i = q >> 3, j = (i & 1) ? 7 - (q & 7) : (q & 7);
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
                  : "+a"(acc[i][j])
                  : "v"(fa[i]), "v"(fb[buf][j]));
