@@ -78,8 +78,10 @@ extern "C" {
  * stays as an alias), documented the workspace layout (rlk_workspace_layout)
  * and lowered the T and V limits to 2^31 - 4096; 4 added the top-k entry point
  * without stored logits (rlk_topk_logp_direct) and shrank the backward's
- * workspace (the weight is read as stored, with no transposed copy). */
-#define RLK_ABI_VERSION 4
+ * workspace (the weight is read as stored, with no transposed copy); 5
+ * requires grad_weight to be 16-byte aligned and drops dz^T from the
+ * backward's workspace (grad_weight reads dz as stored). */
+#define RLK_ABI_VERSION 5
 
 /* Status codes returned by every entry point that can fail. */
 #define RLK_OK                      0
@@ -287,15 +289,16 @@ int rlk_vocab_merge_ex(const int32_t *targets, float *logp, float *lse, float *e
  *   hidden, weight, targets, T, H, V  as for the forward.
  *   lse, grad_logp  fp32 [T], 4-byte aligned.
  *   grad_hidden     fp32 [T][H] (row stride H) or NULL: not computed.
- *   grad_weight     fp32 [V][H] (row stride H) or NULL: not computed.
- *                   Both NULL: returns RLK_OK, launches nothing.  T == 0:
- *                   grad_weight is set to zero.
+ *   grad_weight     fp32 [V][H] (row stride H), 16-byte aligned, or NULL:
+ *                   not computed.  Both NULL: returns RLK_OK, launches
+ *                   nothing.  T == 0: grad_weight is set to zero.
  *   inv_temperature finite, > 0 (RLK_ERR_INVALID_VALUE otherwise).
  *   workspace       rlk_selected_logp_backward_workspace_bytes(T, H, V)
- *                   bytes, 16-byte aligned: bf16 dz [T][Vp], dz^T [V][Tp] and
- *                   h^T [H][Tp] with Vp, Tp = V, T rounded up to 64 (zero
- *                   padded); about 2 * 2 V T + 2 H T bytes.  (grad_hidden
- *                   reads the weight as stored, with no copy.)
+ *                   bytes, 16-byte aligned: bf16 dz [T][Vp] and h^T [H][Tp]
+ *                   with Vp, Tp = V, T rounded up to 64 (zero padded); about
+ *                   2 V T + 2 H T bytes.  (grad_hidden reads the weight as
+ *                   stored and grad_weight reads dz as stored, with no
+ *                   transposed copy of either.)
  * Extra limit: V and T rounded up to 64 must not exceed 2^21
  * (RLK_ERR_UNSUPPORTED). */
 size_t rlk_selected_logp_backward_workspace_bytes(int64_t T, int64_t H, int64_t V);

@@ -118,16 +118,15 @@ int64_t pad64(int64_t x) { return (x + 63) / 64 * 64; }
 // counters (reset before each launch).  The weight needs no copy: grad_hidden
 // reads it as stored (K-major).
 struct BwdLayout {
-  size_t dz, dzt, ht, queue, total;  // byte offsets and size
+  size_t dz, ht, queue, total;  // byte offsets and size
 };
 
-BwdLayout bwd_layout(int64_t T, int64_t H, int64_t V, bool want_h, bool want_w) {
+// dz serves both products; h^T only the product over the tokens.
+BwdLayout bwd_layout(int64_t T, int64_t H, int64_t V, bool want_w) {
   BwdLayout L{};
   size_t o = 0;
   L.dz = o;
-  if (want_h) o += round_up((size_t)T * pad64(V) * 2);
-  L.dzt = o;
-  if (want_w) o += round_up((size_t)V * pad64(T) * 2);
+  o += round_up((size_t)T * pad64(V) * 2);
   L.ht = o;
   if (want_w) o += round_up((size_t)H * pad64(T) * 2);
   L.queue = o;
@@ -156,24 +155,27 @@ rlk::GemmArgs dz_args(const void *hidden, int64_t ldh, const void *weight, int64
   g.inv_tau = inv_tau;
   g.ex = 3;
   g.Vp = (int)pad64(V);
-  g.Tp = (int)pad64(T);
   return g;
 }
 
 // out [B rows][A rows] fp32 = A . B^T over depth K: B is [Brows][K]; A is
-// [Arows][K], or with a_kr > 0 K-major, [a_kr][Arows] (rows a_kr .. K-1 of
-// the depth read as zeros; Arows a multiple of 8).
+// [Arows][K], or with a_kr > 0 K-major, [a_kr][a_cols] with a_cols >= Arows
+// (default Arows) a multiple of 8 (rows a_kr .. K-1 of the depth read as
+// zeros).  out_t (K-major A only): out is stored transposed, [A rows][B rows]
+// (16-byte aligned, Brows a multiple of 4).
 int plain_gemm(const uint16_t *A, int64_t lda, int64_t Arows, const uint16_t *B,
                int64_t ldb, int64_t Brows, int64_t K, float *out, int *queue,
-               hipStream_t s, int64_t a_kr = 0) {
+               hipStream_t s, int64_t a_kr = 0, int64_t a_cols = 0, bool out_t = false) {
   rlk::GemmArgs g = gemm_args(B, ldb, A, lda, Brows, K, Arows);
   g.kmw = a_kr > 0;
   g.kr = (int)a_kr;
+  g.kcols = (int)(a_cols > 0 ? a_cols : Arows);
+  g.out_t = out_t ? 1 : 0;
   g.logits = out;
   g.queue = queue;
-  // Both backward products stream an operand from HBM in the hidden role
-  // (dz, dz^T); prefetching it as well as the weight role measured 3.7 %
-  // faster over the whole backward, bitwise identical.
+  // Prefetching the hidden-role operand into L2 as well as the weight role
+  // measured 3.7 % faster over the whole backward (when its hidden roles were
+  // dz and dz^T), bitwise identical.
   g.pf_hidden = 1;
   return hip_status(rlk::launch_gemm_logits(g, compute_units(), s));
 }
@@ -367,7 +369,7 @@ int rlk_selected_logp(const void *hidden, int64_t ld_hidden,
 
 size_t rlk_selected_logp_backward_workspace_bytes(int64_t T, int64_t H, int64_t V) {
   if (T <= 0 || H <= 0 || V <= 0 || T > MAX_ROWS || V > MAX_ROWS || H > MAX_H) return 0;
-  return bwd_layout(T, H, V, true, true).total;
+  return bwd_layout(T, H, V, true).total;
 }
 
 int rlk_logp_grad_logits(const void *hidden, int64_t ld_hidden, const void *weight,
@@ -401,7 +403,7 @@ int rlk_selected_logp_backward(const void *hidden, int64_t ld_hidden, const void
   if (st != RLK_OK) return st;
   const bool want_h = grad_hidden != nullptr, want_w = grad_weight != nullptr;
   if (!want_h && !want_w) return RLK_OK;
-  if ((want_h && !aligned(grad_hidden, 4)) || (want_w && !aligned(grad_weight, 4)))
+  if ((want_h && !aligned(grad_hidden, 4)) || (want_w && !aligned(grad_weight, 16)))
     return RLK_ERR_MISALIGNED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (T == 0) {  // no rows: grad_weight is a sum over nothing
@@ -413,30 +415,29 @@ int rlk_selected_logp_backward(const void *hidden, int64_t ld_hidden, const void
   if (!aligned(targets, 4) || !aligned(lse, 4) || !aligned(grad_logp, 4) ||
       !aligned(workspace, 16))
     return RLK_ERR_MISALIGNED;
-  const BwdLayout L = bwd_layout(T, H, V, want_h, want_w);
+  const BwdLayout L = bwd_layout(T, H, V, want_w);
   if (workspace_bytes < L.total) return RLK_ERR_WORKSPACE_TOO_SMALL;
   char *ws = static_cast<char *>(workspace);
   const int64_t Vp = pad64(V), Tp = pad64(T);
   uint16_t *dz = reinterpret_cast<uint16_t *>(ws + L.dz);
-  uint16_t *dzt = reinterpret_cast<uint16_t *>(ws + L.dzt);
   uint16_t *ht = reinterpret_cast<uint16_t *>(ws + L.ht);
   const uint16_t *h16 = static_cast<const uint16_t *>(hidden);
   const uint16_t *w16 = static_cast<const uint16_t *>(weight);
-  // grad_weight contracts over T: its operands are dz^T (written by the dz
-  // pass) and hidden^T, a copy with the tokens contiguous.  (Reading the
-  // token-major dz and hidden K-major instead measured slower: the
-  // transposing LDS reads deliver about 3/4 of ds_read_b128's bandwidth, and
-  // both operands would need them, 0.56 ms over this copy and dz^T's store.)
+  // grad_weight contracts over T.  It is formed as its transpose, [H][V] =
+  // h^T [H][Tp] . dz [Tp][Vp], stored transposed: dz is read K-major as the
+  // dz pass wrote it (token rows are the depth), and hidden^T is a copy
+  // with the tokens contiguous (T H bf16, small next to dz), so only one
+  // operand takes the transposing LDS reads and no dz^T is written.  (Both
+  // operands read K-major measured 0.56 ms slower than a dz^T store plus
+  // this copy; a dz^T store measured slower than this product.)
   if (want_w) {
     st = hip_status(rlk::launch_transpose(h16, ld_hidden, (int)T, (int)H, ht, Tp, s));
     if (st != RLK_OK) return st;
   }
   rlk::GemmArgs g = dz_args(hidden, ld_hidden, weight, ld_weight, targets, lse, grad_logp, T,
                             H, V, inv_temperature);
-  g.dz = want_h ? dz : nullptr;
+  g.dz = dz;
   g.ld_dz = Vp;
-  g.dzt = want_w ? dzt : nullptr;
-  g.ld_dzt = Tp;
   int *queue = reinterpret_cast<int *>(ws + L.queue);
   g.queue = queue;
   st = hip_status(rlk::launch_gemm_stats(g, compute_units(), s));
@@ -448,8 +449,10 @@ int rlk_selected_logp_backward(const void *hidden, int64_t ld_hidden, const void
     st = plain_gemm(w16, ld_weight, H, dz, Vp, T, Vp, grad_hidden, queue, s, V);
     if (st != RLK_OK) return st;
   }
-  // grad_weight [V][H] = dzt [V][Tp] . ht [H][Tp]^T
-  if (want_w) st = plain_gemm(ht, Tp, H, dzt, Tp, V, Tp, grad_weight, queue, s);
+  // grad_weight [V][H] = (ht [H][Tp] . dz [Tp][Vp])^T: dz in the weight role,
+  // K-major with T depth rows (rows T .. Tp-1 read as zeros) and Vp columns
+  // (columns V .. Vp-1 hold zeros), the output stored transposed
+  if (want_w) st = plain_gemm(dz, Vp, V, ht, Tp, H, Tp, grad_weight, queue, s, T, Vp, true);
   return st;
 }
 

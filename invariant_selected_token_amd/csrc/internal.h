@@ -48,22 +48,24 @@ struct GemmArgs {
   // or null for the fixed walk
   int *queue;
   // Logit gradient (ex == 3): dz = g inv_tau (onehot(y) - exp(z inv_tau - lse))
-  // rounded to bf16, written to dz [T][ld_dz] (columns V .. Vp-1 zero) and / or
-  // dzt [V][ld_dzt] (columns T .. Tp-1 zero); either pointer may be null.
+  // rounded to bf16, written to dz [T][ld_dz] (columns V .. Vp-1 zero).
   const float *lse;
   const float *grad;
   uint16_t *dz;
-  uint16_t *dzt;
   int64_t ld_dz;
-  int64_t ld_dzt;
   int Vp;
-  int Tp;
-  // Plain GEMM: the weight-role operand stored K-major, [depth][V columns]
-  // with the depth along its rows (the product over the vocabulary reads
-  // the weight as it is stored); kr is its number of rows along the depth
-  // (rows kr .. H-1 of the depth read as zeros).  V must be a multiple of 8.
+  // Plain GEMM: the weight-role operand stored K-major, [depth][kcols
+  // columns] with the depth along its rows (the product over the vocabulary
+  // reads the weight as it is stored); kr is its number of rows along the
+  // depth (rows kr .. H-1 of the depth read as zeros); kcols >= V columns
+  // are read (a multiple of 8; columns V .. kcols-1 reach only outputs that
+  // are not stored).
   int kmw;
   int kr;
+  int kcols;
+  // Plain GEMM: store the output transposed, out[v][t] with row stride T
+  // (logits then points at a [V][T] fp32 array).  K-major weight role only.
+  int out_t;
   int64_t ldh;
   int64_t ldw;
   int T;

@@ -90,10 +90,14 @@ constexpr int VMCNT0_LGKMCNT0 = 0x0070;
 constexpr int PREFETCH_AHEAD = 1;
 // LDS bytes past the two stages that absorb the prefetch loads' data.
 constexpr int PREFETCH_SINK = 256;
-// Then a double buffer of the tiles' targets (2 x 256 int32).
+// Then a double buffer of the tiles' targets (2 x 256 int32), and for the
+// logit-gradient pass double buffers of their lse and upstream gradients
+// (2 x 256 fp32 each).
 constexpr int TGT_OFS = 4 * TILE_V * TILE_K * 2 + PREFETCH_SINK;
+constexpr int LSE_OFS = TGT_OFS + 2 * TILE_T * 4;
+constexpr int GRAD_OFS = LSE_OFS + 2 * TILE_T * 4;
 // Then the two tile-claim slots of the dynamic walk.
-constexpr int CLAIM_OFS = TGT_OFS + 2 * TILE_T * 4;
+constexpr int CLAIM_OFS = GRAD_OFS + 2 * TILE_T * 4;
 
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base,
@@ -250,11 +254,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   // operand's last row.  Each K block reads through a resource of its own,
   // based at the block's first row (so no offset reaches 2^32 whatever the
   // operand's size) and ending at the operand's last element: depth rows
-  // past kr read zeros, and so do the last row's columns past its end (V
+  // past kr read zeros, and so do the last row's columns past its end (kcols
   // columns, a multiple of 8, so that no 16-byte chunk is cut by the range
   // check, which drops each 4-byte piece on its own).  Columns past the end
   // in other rows read the next row's values; they only reach outputs of
-  // columns past the end, which are never stored.
+  // columns past V, which are never stored.
   struct KMajor {
     const uint16_t *p;
     int krows;
@@ -264,7 +268,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   auto rsrc_w = [&](int n) -> HW {
     const int v0 = n * TILE_V;
     if constexpr (KMW) {
-      return KMajor{a.weight + v0, a.kr, (uint32_t)(a.V - v0) * 2u};
+      return KMajor{a.weight + v0, a.kr, (uint32_t)(a.kcols - v0) * 2u};
     } else {
       return make_rsrc(a.weight + (size_t)v0 * a.ldw,
                        (uint32_t)(min(TILE_V, a.V - v0) * a.ldw * 2));
@@ -347,7 +351,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
   // Targets of a tile: one 4-byte direct-to-LDS load per wave (64 rows
   // each) into the tile's half of a double buffer, through a resource based
   // at the tile's first row and sized to its rows below T (rows past T read
-  // 0; every offset stays below 1 KiB whatever T).
+  // 0; every offset stays below 1 KiB whatever T).  The logit-gradient pass
+  // stages the rows' lse and upstream gradient the same way: read from LDS
+  // in the epilogue, they hold no register across the K loop.
   // The lane offset is formed afresh (an asm the compiler cannot merge with
   // the set-up's): kept across the K loop it would be spilled, and its
   // reload would wait for every load in flight.
@@ -355,11 +361,22 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     if (STATS) {
       int l;
       asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
-      const __amdgpu_buffer_rsrc_t r_tgt =
-          make_rsrc(a.targets + (size_t)tile_m * TT, (uint32_t)(rows_of(tile_m) * 4));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r_tgt, (lds_void *)(smem + TGT_OFS + par * (TILE_T * 4) + wave * 256), 4,
-          (uint32_t)(l * 4), (uint32_t)(64 * wave * 4), 0, 0);
+      const uint32_t bytes = (uint32_t)(rows_of(tile_m) * 4);
+      const int slot = par * (TILE_T * 4) + wave * 256;
+      const __amdgpu_buffer_rsrc_t r_tgt = make_rsrc(a.targets + (size_t)tile_m * TT, bytes);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r_tgt, (lds_void *)(smem + TGT_OFS + slot), 4,
+                                               (uint32_t)(l * 4), (uint32_t)(64 * wave * 4), 0,
+                                               0);
+      if constexpr (EX == 3) {
+        const __amdgpu_buffer_rsrc_t r_lse = make_rsrc(a.lse + (size_t)tile_m * TT, bytes);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_lse, (lds_void *)(smem + LSE_OFS + slot), 4,
+                                                 (uint32_t)(l * 4), (uint32_t)(64 * wave * 4),
+                                                 0, 0);
+        const __amdgpu_buffer_rsrc_t r_g = make_rsrc(a.grad + (size_t)tile_m * TT, bytes);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_g, (lds_void *)(smem + GRAD_OFS + slot), 4,
+                                                 (uint32_t)(l * 4), (uint32_t)(64 * wave * 4),
+                                                 0, 0);
+      }
     }
   };
   auto issue_first = [&](HW r_w, __amdgpu_buffer_rsrc_t r_h, HW p_w,
@@ -613,25 +630,6 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
       if (x < 4) reada(0, 0, x);
       readb(0, 0, 0, x);
     }
-    // The logit gradient's per-row inputs (lse, upstream gradient), loaded
-    // now so that their latency hides under the first K block: issued in the
-    // epilogue they would wait behind the next tile's operand loads (vector
-    // memory completes in order).
-    float lse_r[NJ], grad_r[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) lse_r[j] = grad_r[j] = 0.0f;
-    if constexpr (EX == 3) {
-      int l;
-      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int t = m * TT + wt * WT + 16 * j + (l & 15);
-        if (t < a.T) {
-          lse_r[j] = a.lse[t];
-          grad_r[j] = a.grad[t];
-        }
-      }
-    }
     // Wait states between the accumulators' zeroing (VALU writes) and the
     // first MFMA that reads them.
     __builtin_amdgcn_sched_barrier(0);
@@ -670,9 +668,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
       }
       k_block(kb, S0{}, kb + 1, w0, h0, p, ph_, kp0, true);
       if (last) stage_targets(mn, parity ^ 1);   // after the last tile: its own, unused
-      // (the logit-gradient pass keeps the wait: its epilogue reloads
-      // spilled per-row values and waits on vector memory, which would then
-      // wait for the next tile's loads)
+      // (the logit-gradient pass keeps the wait: without it the pass
+      // measured no faster, with its heavier epilogue of stores)
       k_block(kb + 1, S1{}, kl1, w1, h1, p, ph_, kp1, !last || EX == 3);
       // wait states after the iteration's last MFMA, for register copies
       // the compiler may place where the loop ends (issued while the MFMA
@@ -748,6 +745,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
     // this tile's targets, staged in LDS before its K loop (read with
     // ds_read: no wait on the vector memory counter)
     const int *tgt = reinterpret_cast<const int *>(smem + TGT_OFS + parity * (TILE_T * 4));
+    const float *lse_s = reinterpret_cast<const float *>(smem + LSE_OFS + parity * (TILE_T * 4));
+    const float *grad_s = reinterpret_cast<const float *>(smem + GRAD_OFS + parity * (TILE_T * 4));
     auto target_of = [&](int j, int t) {
       return (t < a.T) ? tgt[wt * WT + 16 * j + fc] : -1;
     };
@@ -767,7 +766,53 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
       // instantiations; the arithmetic, and so every stored bit, is the same.
       constexpr uint32_t DROP = 0x80000000u;
       constexpr bool vec = EX == 0;
-      if constexpr (vec) {
+      if constexpr (EX == 2) {
+        // Transposed: out[v][t], row stride T.  Each wave stages 32 of its
+        // 128 weight-role rows v at a time (blocks i = 2 ip, 2 ip + 1; 32 x
+        // 128 fp32, 16 KiB) in its quarter of the operand buffer's stage 1,
+        // staging row R = 16 ii + 4 fg + r holding the wave's 128 columns t,
+        // then stores whole 512-byte row pieces, two rows per instruction.
+        // A lane's four registers of a block are four rows of one column, so
+        // the writes are single dwords.  16-byte chunk c of staging row R
+        // sits at slot c ^ 4 ((R >> 2) & 3) ^ (R & 1): the four row groups
+        // of a write fall in different banks, and so do the two rows of a
+        // read (lanes l and l + 32).
+        typedef __attribute__((address_space(3))) char lds_c;
+        lds_c *stg = (lds_c *)smem + 2 * STAGE_BYTES + wave * (STAGE_BYTES / 2);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        const int u = lane_e & 31, rh = lane_e >> 5;
+        const int tcol = t0 + wt * WT + 4 * u;   // this lane's first column
+        const uint32_t coff = tcol < a.T ? 4u * (uint32_t)tcol : DROP;
+#pragma unroll
+        for (int ip = 0; ip < NI / 2; ++ip) {
+#pragma unroll
+          for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                // R = 16 ii + 4 fg + r: (R >> 2) & 3 == fg, R & 1 == r & 1
+                const int slot = (4 * j + (fc >> 2)) ^ (4 * fg) ^ (r & 1);
+                *(uint32_t *)(stg + (16 * ii + 4 * fg + r) * 512 + (slot << 4) + 4 * (fc & 3)) =
+                    __float_as_uint(acc[2 * ip + ii][j][r]);
+              }
+          const int vrow = vbase + 32 * ip;
+          const int rows = min(32, a.V - vrow);
+          const __amdgpu_buffer_rsrc_t r_out =
+              make_rsrc(a.logits + (size_t)vrow * a.T,
+                        rows > 0 ? (uint32_t)rows * (uint32_t)a.T * 4u : 0u);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int R = 2 * e + rh;
+            const int slot = u ^ (4 * ((R >> 2) & 3)) ^ (R & 1);
+            const u32x4 d = *(const u32x4 *)(stg + R * 512 + (slot << 4));
+            const uint32_t off = coff == DROP ? DROP : (uint32_t)R * (uint32_t)a.T * 4u + coff;
+            __builtin_amdgcn_raw_buffer_store_b128(d, r_out, (int)off, 0, 0);
+          }
+        }
+      } else if constexpr (vec) {
         // Through LDS: each wave stages 32 token rows at a time (two token
         // blocks; 32 rows x 128 columns fp32, 16 KiB) in its quarter of the
         // operand buffer's stage 1 (free once every wave is past the tile's
@@ -846,19 +891,16 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
         // Each wave stages its 128 x 128 block of dz, 64 token rows at a
         // time, in 16 KiB of the operand buffer's stage 1 (free once every
         // wave is past the tile's last K block; the next tile's first block
-        // lands in stage 0), then writes dz [T][ld_dz] as 16-byte row pieces
-        // and dz^T [V][ld_dzt] as 16-byte pieces of 8 token rows, read back
-        // with the transposing LDS read: 64 full stores per wave and tile
-        // instead of 192 narrow scattered ones.  Staging row r holds the
-        // 128 columns as 32 chunks of 4 (8 bytes); chunk c sits at slot
+        // lands in stage 0), then writes dz [T][ld_dz] as 16-byte row
+        // pieces: 32 full stores per wave and tile instead of 128 narrow
+        // scattered ones.  (The product over the tokens reads dz K-major as
+        // stored, so no transposed copy is written.)  Staging row r holds
+        // the 128 columns as 32 chunks of 4 (8 bytes); chunk c sits at slot
         // c ^ sw(r), sw(r) = 4 (r & 3) + ((r >> 2) & 3), which keeps the
-        // writes (16 rows, one chunk), the row reads (one row, 16 x 16
-        // bytes) and the transposing reads (4 rows x 4 chunks) free of bank
-        // conflicts.  Pass p stages token blocks 4 p .. 4 p + 3: block jj of
-        // the pass in staging rows 16 jj .. 16 jj + 15.
+        // writes (16 rows, one chunk) and the row reads (one row, 16 x 16
+        // bytes) free of bank conflicts.  Pass p stages token blocks 4 p ..
+        // 4 p + 3: block jj of the pass in staging rows 16 jj .. 16 jj + 15.
         typedef __attribute__((address_space(3))) char lds_c;
-        typedef short v4s __attribute__((ext_vector_type(4)));
-        typedef __attribute__((address_space(3))) v4s lds_v4s;
         lds_c *stg = (lds_c *)smem + 2 * STAGE_BYTES + wave * (STAGE_BYTES / 2);
         auto sw = [](int r) { return ((r & 3) << 2) | ((r >> 2) & 3); };
         auto slot = [&](int r, int c) { return stg + r * 256 + ((c ^ sw(r)) << 3); };
@@ -882,8 +924,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
             const bool trow = t < a.T;
             const int y = trow ? target_of(j, t) : -1;
             const bool live = trow && y >= 0 && y < a.V;
-            const float lse_t = live ? lse_r[j] : 0.0f;
-            const float gs = live ? grad_r[j] * a.inv_tau : 0.0f;
+            const float lse_t = live ? lse_s[wt * WT + 16 * j + fc] : 0.0f;
+            const float gs = live ? grad_s[wt * WT + 16 * j + fc] * a.inv_tau : 0.0f;
             const uint64_t keep = live ? ~0ull : 0ull;
             const int lim = a.V - vbase - 4 * fg;   // MASK: offsets below lim are valid
 #pragma unroll
@@ -938,31 +980,6 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, char *smem) {
               const u32x4 o = swp ? u32x4{d[2], d[3], d[0], d[1]} : d;
               const int t = trow0 + r, v = vbase + 8 * u;
               if (t < a.T && v < a.Vp) *(u32x4 *)(a.dz + (size_t)t * a.ld_dz + v) = o;
-            }
-          }
-          if (a.dzt) {
-            // lane 16 G + i: column 16 cb + i, token rows 8 tb .. 8 tb + 7 with
-            // tb = 4 h + G; in each 16-lane group lane 4 k + s points the
-            // transposing read at row 8 tb + k (then + 4), chunk 4 cb + s, so
-            // lane i receives rows 8 tb + 0..3 of column 16 cb + i
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int cb = e >> 1, h = e & 1;
-              const int G = lane_e >> 4, i = lane_e & 15;
-              const int tb = 4 * h + G;
-              const int k = i >> 2, sl = i & 3;
-              const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (lds_v4s *)slot(8 * tb + k, 4 * cb + sl));
-              const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (lds_v4s *)slot(8 * tb + 4 + k, 4 * cb + sl));
-              const int v = vbase + 16 * cb + i, t = trow0 + 8 * tb;
-              if (v < a.V && t < a.Tp) {
-                const u32x4 o = {(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
-                                 (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
-                                 (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
-                                 (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
-                *(u32x4 *)(a.dzt + (size_t)v * a.ld_dzt + t) = o;
-              }
             }
           }
         }
@@ -1345,12 +1362,17 @@ void launch_stats_kernel(const GemmArgs &a, int grid, hipStream_t s) {
 
 template <int EX>
 void launch_store_kernel(const GemmArgs &a, int grid, hipStream_t s) {
-  if (a.kmw)   // the weight-role operand K-major (the product over the vocabulary)
-    hipLaunchKernelGGL((gemm_kernel<false, true, EX, true>), dim3(grid), dim3(GEMM_THREADS), 0,
+  if constexpr (EX == 2) {   // transposed output: K-major weight role only
+    hipLaunchKernelGGL((gemm_kernel<false, true, 2, true>), dim3(grid), dim3(GEMM_THREADS), 0,
                        s, a);
-  else
-    hipLaunchKernelGGL((gemm_kernel<false, true, EX, false>), dim3(grid), dim3(GEMM_THREADS), 0,
-                       s, a);
+  } else {
+    if (a.kmw)   // the weight-role operand K-major (the product over the vocabulary)
+      hipLaunchKernelGGL((gemm_kernel<false, true, EX, true>), dim3(grid), dim3(GEMM_THREADS),
+                         0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_kernel<false, true, EX, false>), dim3(grid), dim3(GEMM_THREADS),
+                         0, s, a);
+  }
 }
 
 }  // namespace
@@ -1374,7 +1396,12 @@ hipError_t launch_gemm_logits(const GemmArgs &a, int workers, hipStream_t s) {
   // whole rows through LDS when V is a multiple of 4 and the output 16-byte
   // aligned; otherwise one column per store (the same values)
   const bool vec = (a.V & 3) == 0 && ((uintptr_t)a.logits & 15) == 0;
-  if (vec) launch_store_kernel<0>(a, grid, s);
+  if (a.out_t) {
+    // transposed: whole 16-byte pieces of rows of T columns (T % 4 == 0)
+    if (!a.kmw || (a.T & 3) != 0 || ((uintptr_t)a.logits & 15) != 0)
+      return hipErrorInvalidValue;
+    launch_store_kernel<2>(a, grid, s);
+  } else if (vec) launch_store_kernel<0>(a, grid, s);
   else launch_store_kernel<1>(a, grid, s);
   return hipGetLastError();
 }

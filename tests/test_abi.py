@@ -84,7 +84,7 @@ def test_boundary_calls_of_the_scope_table():
 
 
 def test_constants():
-    assert rlk.rlk_abi_version() == 4
+    assert rlk.rlk_abi_version() == 5
     assert rlk.rlk_vocab_tile() == 128
     msgs = {rlk.rlk_status_string(s) for s in range(9)}
     assert len(msgs) == 9 and all(msgs)
@@ -433,9 +433,9 @@ def test_backward_workspace_size():
     r = lambda x: (x + 255) // 256 * 256
     p = lambda x: (x + 63) // 64 * 64
     for T, H, V in [(1, 64, 1), (64, 256, 4096), (4096, 4096, 151936), (300, 192, 1000)]:
-        # dz, dz^T, hidden^T (the weight is read as stored), then the
+        # dz, hidden^T (the weight and dz are read as stored), then the
         # tile-claim counters
-        want = r(T * p(V) * 2) + r(V * p(T) * 2) + r(H * p(T) * 2) + 256
+        want = r(T * p(V) * 2) + r(H * p(T) * 2) + 256
         assert wb(T, H, V) == want
     assert wb(0, 64, 10) == 0 and wb(4, 0, 10) == 0 and wb(4, 64, 0) == 0
 
@@ -457,6 +457,7 @@ def _bwd(hidden=FAKE, ldh=256, weight=FAKE, ldw=256, targets=FAKE, lse=FAKE, gra
     (dict(gh=None, gw=None), rlk.RLK_OK),                         # nothing asked for
     (dict(gh=FAKE + 2), rlk.RLK_ERR_MISALIGNED),
     (dict(gw=FAKE + 1), rlk.RLK_ERR_MISALIGNED),
+    (dict(gw=FAKE + 4), rlk.RLK_ERR_MISALIGNED),                  # 16-byte pieces of its rows
     (dict(hidden=None), rlk.RLK_ERR_NULL_POINTER),
     (dict(lse=None), rlk.RLK_ERR_NULL_POINTER),
     (dict(grad=None), rlk.RLK_ERR_NULL_POINTER),
@@ -474,7 +475,7 @@ def test_backward_error_paths(kw, status):
 
 
 def test_backward_workspace_shrinks_with_one_output():
-    """Only grad_hidden: the dz^T and h^T regions are not needed."""
+    """Only grad_hidden: the h^T region is not needed."""
     T, H, V = 300, 192, 1000
     full = rlk.rlk_selected_logp_backward_workspace_bytes(T, H, V)
     r = lambda x: (x + 255) // 256 * 256
