@@ -114,6 +114,41 @@ def test_backward_ragged(dev, T, H, V):
     _check(gw.cpu().numpy(), rw, bw, f"grad_weight {T}x{H}x{V}")
 
 
+@pytest.mark.parametrize("T,H,V", [(70, 192, 1000), (1, 64, 5), (300, 64, 257)])
+def test_grad_weight_stays_in_bounds(dev, T, H, V):
+    """grad_weight's tiles are stored transposed, as 16-byte pieces of its rows,
+    through a range-checked resource per 32 rows (rows past V and columns past
+    H dropped): written into the middle of a sentinel-filled buffer, the floats
+    around it keep the sentinel and the values equal a plain output's bits."""
+    c = synth.normal_case(f"bwd_bounds_{T}x{H}x{V}", 900 + T, T, H, V, weight_std=0.1)
+    g = _grads_dev(_upstream(T, 31 + T), dev)
+    h, w, y = to_dev_bf16(c.hidden, dev), to_dev_bf16(c.weight, dev), to_dev_i32(c.targets, dev)
+    lse, _, gw_ref = _run(h, w, y, g, 0.9, want_hidden=False)
+    pad = 1024   # floats on each side (4 KiB: keeps the output 16-byte aligned)
+    sentinel = -7.25
+    buf = torch.full((V * H + 2 * pad,), sentinel, dtype=torch.float32, device=dev)
+    gw = buf[pad:pad + V * H].view(V, H)
+    _, got = rlk.rlk_selected_logp_backward(h, w, y, lse, g, inv_temperature=0.9,
+                                            want_hidden=False, grad_weight=gw)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:pad] == sentinel) and torch.all(buf[pad + V * H:] == sentinel)
+    assert torch.equal(got.view(torch.int32), gw_ref.view(torch.int32))
+
+
+def test_grad_weight_must_be_16_byte_aligned(tiny, dev):
+    """Its rows leave as 16-byte pieces: a 4-byte-aligned grad_weight is refused
+    before any launch (RLK_ERR_MISALIGNED, raised by the binding)."""
+    h, w, y = tiny.hidden, tiny.weight, tiny.targets
+    T, H, V = h.shape[0], h.shape[1], w.shape[0]
+    _, lse, _ = rlk.rlk_selected_logp_ex(h, w, y)
+    g = torch.ones(T, dtype=torch.float32, device=dev)
+    buf = torch.zeros(V * H + 1, dtype=torch.float32, device=dev)
+    with pytest.raises(RuntimeError, match="misaligned"):
+        rlk.rlk_selected_logp_backward(h, w, y, lse, g, want_hidden=False,
+                                       grad_weight=buf[1:].view(V, H))
+    torch.cuda.synchronize()
+
+
 def test_backward_medium_full_grad_weight(dev):
     """A bigger vocabulary and depth: T=512, H=1024, V=8192."""
     c = synth.normal_case("bwd_medium", 4321, 512, 1024, 8192)
