@@ -113,10 +113,10 @@ int hip_status(hipError_t e) {
 // Backward: workspace layout, limits and launch helpers.
 int64_t pad64(int64_t x) { return (x + 63) / 64 * 64; }
 
-// dz [T][pad64(V)] (grad_hidden's operand), dz^T [V][pad64(T)] and
-// hidden^T [H][pad64(T)] (grad_weight's), then the GEMMs' tile-claim
-// counters (reset before each launch).  The weight needs no copy: grad_hidden
-// reads it as stored (K-major).
+// dz [T][pad64(V)] (the operand of both products) and hidden^T [H][pad64(T)]
+// (grad_weight's), then the GEMMs' tile-claim counters (reset before each
+// launch).  Neither the weight nor dz needs a transposed copy: grad_hidden
+// reads the weight and grad_weight reads dz as stored (K-major).
 struct BwdLayout {
   size_t dz, ht, queue, total;  // byte offsets and size
 };
