@@ -149,6 +149,25 @@ def test_grad_weight_must_be_16_byte_aligned(tiny, dev):
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("T,H,V", [(70, 192, 1000), (300, 128, 4133)])
+def test_backward_strided_operands_same_bits(dev, T, H, V):
+    """hidden and weight as views into wider rows whose extra columns hold NaN:
+    the row strides reach the hidden-row transpose, the dz pass and both
+    products' K-major reads, and the gradients keep the contiguous call's bits
+    (any read of a padding column would bring a NaN in)."""
+    c = synth.normal_case(f"bwd_strided_{T}x{H}x{V}", 950 + T, T, H, V, weight_std=0.1)
+    g = _grads_dev(_upstream(T, 41 + T), dev)
+    h, w, y = to_dev_bf16(c.hidden, dev), to_dev_bf16(c.weight, dev), to_dev_i32(c.targets, dev)
+    _, gh, gw = _run(h, w, y, g, 0.8)
+    hb = torch.full((T, H + 64), float("nan"), dtype=h.dtype, device=dev)
+    wb = torch.full((V, H + 128), float("nan"), dtype=w.dtype, device=dev)
+    hb[:, :H] = h
+    wb[:, :H] = w
+    _, gh2, gw2 = _run(hb[:, :H], wb[:, :H], y, g, 0.8)
+    assert torch.equal(gh.view(torch.int32), gh2.view(torch.int32)), "grad_hidden"
+    assert torch.equal(gw.view(torch.int32), gw2.view(torch.int32)), "grad_weight"
+
+
 def test_backward_medium_full_grad_weight(dev):
     """A bigger vocabulary and depth: T=512, H=1024, V=8192."""
     c = synth.normal_case("bwd_medium", 4321, 512, 1024, 8192)
