@@ -9,8 +9,9 @@ whole hot path on one batch, with inputs already resident in HBM:
                       per-(row, 128-wide vocabulary tile) max / sum of
                       exponentials and the target-logit capture;
   2. rlk_vocab_merge  fixed-order fold of the tile statistics -> lse, logp;
-  3. rlk_compare x2   bitwise consistency of this step's logp and lse against
-                      the first call's (mismatch count, max |diff|).
+  3. rlk_compare      bitwise consistency of this step's logp and lse (one
+                      buffer, one launch) against the first call's (mismatch
+                      count, max |diff|).
 Prints one JSON line.  Only one GPU is used; --gpus N > 1 exits.
 
 After the timed region (never inside it) the line also gets: per-step median
@@ -588,17 +589,17 @@ def main() -> int:
     hidden, weight = to_dev(case.hidden), to_dev(case.weight)
     targets = torch.from_numpy(case.targets).to(dev)
     ws = rlk.workspace_for(T, V, dev)
-    logp = torch.empty(T, dtype=torch.float32, device=dev)
-    lse = torch.empty(T, dtype=torch.float32, device=dev)
+    # logp and lse in one buffer, so that one compare covers both
+    out = torch.empty(2 * T, dtype=torch.float32, device=dev)
+    logp, lse = out[:T], out[T:]
     ref_lp, ref_lse = rlk.rlk_selected_logp(hidden, weight, targets)
-    stats_lp = torch.zeros((max(args.steps, 1), 8), dtype=torch.float64, device=dev)
-    stats_lse = torch.zeros_like(stats_lp)
+    ref = torch.cat([ref_lp, ref_lse])
+    stats = torch.zeros((max(args.steps, 1), 8), dtype=torch.float64, device=dev)
 
     def step(i):
         rlk.rlk_vocab_stats(hidden, weight, targets, ws)
         rlk.rlk_vocab_merge(targets, ws, V, logp=logp, lse=lse)
-        rlk.rlk_compare(logp, ref_lp, stats=stats_lp[i])
-        rlk.rlk_compare(lse, ref_lse, stats=stats_lse[i])
+        rlk.rlk_compare(out, ref, stats=stats[i])
 
     if args.calib_copy_mb > 0:
         n = args.calib_copy_mb * (1 << 20) // 4
@@ -611,8 +612,7 @@ def main() -> int:
     for i in range(args.warmup):
         step(0)
     torch.cuda.synchronize()
-    stats_lp.zero_()
-    stats_lse.zero_()
+    stats.zero_()
 
     K = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
@@ -625,8 +625,7 @@ def main() -> int:
         e[1].record()
         rlk.rlk_vocab_merge(targets, ws, V, logp=logp, lse=lse)
         e[2].record()
-        rlk.rlk_compare(logp, ref_lp, stats=stats_lp[i])
-        rlk.rlk_compare(lse, ref_lse, stats=stats_lse[i])
+        rlk.rlk_compare(out, ref, stats=stats[i])
         e[3].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -638,10 +637,9 @@ def main() -> int:
     gemm_ms = sum(g_ms) / K
     merge_ms = sum(m_ms) / K
     check_ms = sum(c_ms) / K
-    s_lp = stats_lp.cpu().numpy()
-    s_lse = stats_lse.cpu().numpy()
-    mismatch = int(s_lp[:, 1].sum() + s_lse[:, 1].sum())
-    max_diff = float(max(s_lp[:, 2].max(), s_lse[:, 2].max()))
+    s_all = stats.cpu().numpy()
+    mismatch = int(s_all[:, 1].sum())
+    max_diff = float(s_all[:, 2].max())
 
     flops = 2.0 * T * H * V                      # algorithmic work per launch
     achieved = flops / (gemm_ms * 1e-3) / 1e12   # TFLOP/s
