@@ -14,11 +14,13 @@
 //                       stage-by-stage comparison of section 五; also the two
 //                       gradient products of the backward).  EX 0 stores 16
 //                       bytes per lane, EX 1 one column per store, for rows
-//                       whose length or base is not 16-byte aligned.  KMW
-//                       reads the weight-role operand K-major (stored with
-//                       the depth along its rows) through the transposing
-//                       LDS read: the product over the vocabulary takes the
-//                       weight as it is stored.
+//                       whose length or base is not 16-byte aligned, EX 2
+//                       each tile transposed (out[v][t]).  KMW reads the
+//                       weight-role operand K-major (stored with the depth
+//                       along its rows) through the transposing LDS read:
+//                       the product over the vocabulary takes the weight,
+//                       and the product over the tokens takes dz, as they
+//                       are stored.
 //   merge_kernel        per row, folds the tile statistics in a fixed order
 //                       that depends only on the number of vocabulary tiles,
 //                       then lse = M + log(s) and logp = z_y - lse (and, with
@@ -174,9 +176,10 @@ __device__ __forceinline__ bf16x4 tr_read(const lds_bf16x4 *__restrict__ p) {
 // multiple of 256, e.g. every decode batch) read as zeros through the buffer
 // unit's range check, and no epilogue writes their results.  (Skipping their
 // loads and MFMAs needs either a branch per load or MFMA, which measured 2.5 %
-// slower on full tiles, or copies of the K loop specialised on the number of
-// live rows, which push the option and backward epilogues into scratch
-// spills and amount to a batch-size-dependent code path.)
+// slower on full tiles for the loads and 28 % for a branch inside each MFMA's
+// assembly, or copies of the K loop specialised on the number of live rows,
+// which push the option and backward epilogues into scratch spills and amount
+// to a batch-size-dependent code path.)
 //
 // PERSIST: the workgroup walks tiles L = blockIdx.x, + gridDim.x, ... and
 // issues the next tile's first K-block loads before the current tile's
