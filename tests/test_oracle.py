@@ -163,6 +163,29 @@ def test_vocab_permutation_equivariance():
     np.testing.assert_allclose(b_lse, a_lse, rtol=0, atol=1e-13)
 
 
+@pytest.mark.parametrize("c", [-512.0, -3.0, 0.75, 64.0, 4096.0])
+def test_shift_equivariance(c):
+    """Adding c to every logit of a row adds c to its lse and leaves its logp
+    unchanged (the softmax is invariant under a common shift).  The shift is
+    built from the inputs: 64 more hidden columns (1, 0, ..., 0) and weight
+    columns (c, 0, ..., 0), so every logit gains c exactly (c is bf16-exact
+    and the fp64 sums stay exact).  A max shift applied twice or not at all,
+    or an lse that drops the max, fails this."""
+    k = synth.tiny_case()
+    T, V = k.hidden.shape[0], k.weight.shape[0]
+    hx = np.zeros((T, 64), np.float32)
+    hx[:, 0] = 1.0
+    wx = np.zeros((V, 64), np.float32)
+    wx[:, 0] = c
+    hidden2 = np.concatenate([k.hidden, _bf16(hx)], axis=1)
+    weight2 = np.concatenate([k.weight, _bf16(wx)], axis=1)
+    lp, lse = orc.selected_logp(k.hidden, k.weight, k.targets)
+    lp2, lse2 = orc.selected_logp(hidden2, weight2, k.targets)
+    ulp = np.spacing(np.maximum(np.abs(lse2), abs(c)))
+    assert np.all(np.abs(lse2 - (lse + c)) <= 4 * ulp)
+    assert np.all(np.abs(lp2 - lp) <= 4 * ulp)
+
+
 def test_row_independence():
     """A row's result does not depend on the other rows passed with it."""
     c = synth.tiny_case()
